@@ -1,0 +1,153 @@
+/*
+ * gptq_mi355x.h -- C ABI of the GPTQ weight-only quantized linear layer for AMD MI355X (gfx950).
+ *
+ *     y[M, N] = x[M, K] . dequant(qweight, qzeros, scales, g_idx)^T
+ *     W[n, k] = (code[k, n] - zero[g, n]) * scale[g, n],   g = g_idx[k]
+ *
+ * The operation is defined on "39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes",
+ * section "GPTQ" / "The format" (tensor shapes, stored-minus-one zeros, the dequant equation, and
+ * sorting the inputs by g_idx once at load time), and on "GPTQ packed checkpoint (safetensors /
+ * torch)", sections "GptqLayer", "QuantizeConfig", "Reader" and "Reject the file when".
+ * The split into a load-time repack that builds a kernel-private runtime layout and a per-call
+ * GEMM follows "Kernel Backends Reference", section "Packed storage and execution concepts"
+ * (runtime ABI, post_init).
+ *
+ * Conventions that hold for every entry point:
+ *  - Every tensor pointer is a DEVICE pointer on the HIP device that is current when the call
+ *    is made, unless its name ends in _host.  The caller owns every buffer it passes.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *  - Errors are returned as gptq_status, never by abort().  All argument and shape checks run
+ *    before any device work, so a failed call has launched nothing and changed no output.
+ *    There is no silent fallback to another kernel, dtype or layout.
+ *  - A HIP runtime failure returns GPTQ_E_HIP; gptq_last_hip_error() returns its hipError_t for
+ *    the calling thread.
+ *  - The library is thread-safe for calls on distinct handles.  A handle is immutable after
+ *    gptq_repack, so gptq_gemm may run on one handle from several streams at once as long as
+ *    each call has its own workspace.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gptq_layer* gptq_handle_t;
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_E_INVALID_ARG = 1, /* NULL / misaligned pointer, M < 0, bad dtype or path, y aliasing x */
+  GPTQ_E_SHAPE = 2,       /* rule GPTQ-002 / GPTQ-003: qweight, qzeros or scales shape wrong,
+                             in_features or out_features not a multiple of 32 */
+  GPTQ_E_GIDX = 3,        /* rule GPTQ-004: g_idx length wrong or an index outside [0, G) */
+  GPTQ_E_UNSUPPORTED = 4, /* rule GPTQ-001 (bits not 2/3/4/8), GPTQ-005 (a private layout such as
+                             marlin), group_size not -1 and not a positive multiple of 32, or a
+                             g_idx whose groups are not whole (its stable sort is not j // gs) */
+  GPTQ_E_HIP = 5,         /* a HIP runtime call failed (see gptq_last_hip_error) */
+  GPTQ_E_OOM = 6,         /* device allocation for the runtime layout failed */
+  GPTQ_E_WORKSPACE = 7,   /* workspace smaller than gptq_workspace_size() or not 256-B aligned */
+  GPTQ_E_DEVICE = 8       /* no gfx950 device, or the handle lives on another device */
+} gptq_status;
+
+typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype;
+
+/* Checkpoint formats.  Only GPTQ_FORMAT_GPTQ (AutoGPTQ "cuda" pack, v1 stored-minus-one zeros)
+ * is accepted; the others are named so that callers can pass what the checkpoint declares and be
+ * refused with GPTQ_E_UNSUPPORTED (rule GPTQ-005). */
+typedef enum { GPTQ_FORMAT_GPTQ = 0, GPTQ_FORMAT_MARLIN = 1, GPTQ_FORMAT_GPTQ_V2 = 2 } gptq_format;
+
+/* Kernel family for gptq_gemm.  AUTO picks SKINNY for M <= 64 and TILED otherwise.  Forcing a
+ * family is for tests; a forced family that cannot run the given M returns GPTQ_E_INVALID_ARG. */
+typedef enum { GPTQ_PATH_AUTO = 0, GPTQ_PATH_SKINNY = 1, GPTQ_PATH_TILED = 2 } gptq_path;
+
+/* Description of one checkpoint layer.  The *_shape fields are the shapes of the tensors the
+ * caller holds; they are checked against K, N, bits and group_size (rules GPTQ-002..004). */
+typedef struct {
+  int32_t in_features;       /* K                                                              */
+  int32_t out_features;      /* N                                                              */
+  int32_t bits;              /* 2, 3, 4 or 8 (GPTQ-001)                                        */
+  int32_t group_size;        /* -1 = one group over all K, else a positive multiple of 32      */
+  int32_t desc_act;          /* informational; act-order is taken from g_idx itself            */
+  int32_t checkpoint_format; /* gptq_format                                                    */
+  int32_t scales_dtype;      /* gptq_dtype of `scales`: F16, BF16 or F32                        */
+  int32_t reserved;          /* must be 0                                                      */
+  int64_t qweight_shape[2];  /* must be [K / 32 * bits, N]                                     */
+  int64_t qzeros_shape[2];   /* must be [G, N / 32 * bits], G = ceil(K / group_size)           */
+  int64_t scales_shape[2];   /* must be [G, N]                                                 */
+  int64_t g_idx_len;         /* K, or 0 when no g_idx is passed (then g = k / group_size)      */
+} gptq_layer_desc;
+
+typedef struct {
+  int32_t in_features, out_features, bits, group_size, groups;
+  int32_t padded_in_features; /* K rounded up to a multiple of 128 (the kernels' K chunk)      */
+  int32_t has_perm;           /* 1 when the load-time sort of g_idx is not the identity        */
+  int32_t scales_dtype;
+  int64_t runtime_bytes;      /* device bytes owned by the handle                              */
+  int32_t device;             /* HIP ordinal the handle lives on                               */
+} gptq_handle_info;
+
+/* Host-only check of a layer description and (optionally) a host copy of g_idx, with the same
+ * rules gptq_repack applies ("GPTQ packed checkpoint", "Reject the file when").  Needs no GPU.
+ * g_idx_host may be NULL (sequential groups).  Returns GPTQ_OK or the first failing status. */
+gptq_status gptq_validate(const gptq_layer_desc* desc, const int32_t* g_idx_host);
+
+/* Load-time repack (the runtime initialisation after loading).  Reads the checkpoint tensors
+ *   qweight int32 [K*bits/32, N], qzeros int32 [G, N*bits/32], scales [G, N] (desc->scales_dtype),
+ *   g_idx int32 [K] or NULL,
+ * all device pointers, row-major, 4-byte aligned; validates them (this copies g_idx to the host
+ * once); computes the stable sort of the inputs by g_idx; and builds the kernel-private runtime
+ * layout in device memory owned by the new handle.  Work is queued on `stream`, which is
+ * synchronised before return, so the caller may free or change the checkpoint tensors afterwards
+ * (the handle does not alias them; changed tensors need a new repack).  On failure *out is NULL. */
+gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, const int32_t* qzeros,
+                        const void* scales, const int32_t* g_idx, void* stream, gptq_handle_t* out);
+
+/* Device bytes of workspace gptq_gemm needs for this handle, M, activation dtype and path
+ * (0 when none).  The size depends only on (handle, M, path): act-order layers need a sorted copy
+ * of x, and the TILED family needs per-row segment sums of x. */
+gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int32_t path,
+                                size_t* bytes);
+
+/* y = x . W^T for the handle's layer.
+ *   x  [M, K] row-major, dtype x_dtype (F16 or BF16), 16-byte aligned;
+ *   y  [M, N] row-major, same dtype as x, 16-byte aligned, must not overlap x or the workspace;
+ *   workspace: device memory of at least gptq_workspace_size() bytes, 256-byte aligned
+ *              (may be NULL when that size is 0); its contents are scratch, and two calls in
+ *              flight at once must not share one workspace.
+ * Accumulates in fp32 and rounds y to x_dtype with round-to-nearest-even.  M == 0 returns
+ * GPTQ_OK with nothing launched ("Formats and kernels ...", the zero-token forward of an idle
+ * data-parallel rank).  Queues work on `stream` only: no allocation, no synchronisation, so the
+ * call can be captured in a HIP graph. */
+gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, void* y,
+                      void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
+/* Frees the handle's device memory (after synchronising the device).  NULL is accepted. */
+gptq_status gptq_destroy(gptq_handle_t h);
+
+/* Handle properties (sizes, groups, whether a permutation is in effect). */
+gptq_status gptq_info(gptq_handle_t h, gptq_handle_info* info);
+
+/* Test hook: reads the runtime layout back and decodes it on the host into the checkpoint's
+ * logical values, in ORIGINAL input order:
+ *   codes_kn_host  uint8 [K * N]  code[k, n] at k * N + n
+ *   zeros_gn_host  int32 [G * N]  zero[g, n] = stored + 1
+ *   scales_gn_host uint32 [G * N] raw scale bits (16-bit patterns zero-extended, or f32 bits)
+ *   perm_host      int32 [K]      input index at each sorted position
+ * Any output pointer may be NULL to skip it.  Synchronises the device.  The runtime layout is
+ * not a checkpoint and must not be saved as one. */
+gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t* zeros_gn_host,
+                                uint32_t* scales_gn_host, int32_t* perm_host);
+
+/* Static message for a status code. */
+const char* gptq_status_str(gptq_status s);
+
+/* hipError_t behind the calling thread's last GPTQ_E_HIP (0 if none). */
+int32_t gptq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,55 @@
+"""Shared helpers of the GPU tests: move seeded numpy inputs to the device and call the library.
+Nothing here computes the method: expected values come from oracle/ only."""
+import numpy as np
+
+import oracle as o
+import gptq_inputs as gi
+
+TOL = {"f16": dict(rel_l2=1e-3, max_abs_over_rms=2e-2), "bf16": dict(rel_l2=4e-3, max_abs_over_rms=2e-2)}
+
+
+def torch_dtype(tag):
+    import torch
+    return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[tag]
+
+
+def bits_to_device(a, tag):
+    """uint16 bit patterns (or float32) -> torch tensor of that float dtype on cuda:0."""
+    import torch
+    if tag == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).cuda()
+    return t.view(torch_dtype(tag))
+
+
+def device_to_bits(t):
+    import torch
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def repack_layer(L: gi.Layer, use_gidx=True):
+    import torch
+    import weight_only_quantized_amd as wq
+    qw = torch.from_numpy(np.ascontiguousarray(L.qweight)).cuda()
+    qz = torch.from_numpy(np.ascontiguousarray(L.qzeros)).cuda()
+    sc = bits_to_device(L.scales, L.scales_dtype)
+    g = torch.from_numpy(np.ascontiguousarray(L.g_idx, dtype=np.int32)).cuda() if use_gidx else None
+    h = wq.repack(qw, qz, sc, g, bits=L.bits, group_size=L.group_size, desc_act=L.desc_act)
+    return h
+
+
+def run_gemm(h, x_bits, x_tag, path=0):
+    x = bits_to_device(x_bits, x_tag)
+    y = h.gemm(x, path=path)
+    import torch
+    torch.cuda.synchronize()
+    return device_to_bits(y)
+
+
+def check(y_bits, x_tag, y_ref, label=""):
+    m = o.compare(y_bits, x_tag, y_ref)
+    tol = TOL[x_tag]
+    assert m["nonfinite"] == 0, (label, m)
+    assert m["rel_l2"] <= tol["rel_l2"], (label, m)
+    assert m["max_abs_over_rms"] <= tol["max_abs_over_rms"], (label, m)
+    return m

@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path against the float64 CPU oracle, element by element, through the C ABI.
+
+Repack must be bit-exact (decoded runtime layout == oracle unpack).  GEMM output must be within
+rel-L2 <= 1e-3 (fp16 out) / 4e-3 (bf16 out) and max-abs <= 2e-2 * rms(y_ref).  Cases with a
+single nonzero product per output must be bit-exact."""
+import itertools
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as o
+import gptq_inputs as gi
+from gpu_util import TOL, bits_to_device, check, device_to_bits, repack_layer, run_gemm
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_only_quantized_amd as wq
+    wq.load_library()
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ---- repack: bit-exact ---------------------------------------------------------------------------
+
+REPACK_CASES = [
+    (256, 256, 4, 128, False, "f16"), (256, 96, 2, 64, True, "bf16"), (288, 64, 3, 32, True, "f16"),
+    (512, 64, 8, -1, True, "f32"), (96, 32, 4, 32, False, "bf16"), (1024, 160, 3, 128, True, "f16"),
+    (384, 64, 8, 96, True, "f16"), (4096, 128, 4, 128, True, "f16"),
+]
+
+
+@pytest.mark.parametrize("K,N,bits,gs,desc,sdt", REPACK_CASES)
+def test_repack_decodes_to_oracle_unpack(K, N, bits, gs, desc, sdt):
+    say("repack", K, N, bits, gs, desc, sdt)
+    L = gi.make_layer(K, N, bits, gs, desc_act=desc, scales_dtype=sdt, seed=K + N + bits)
+    h = repack_layer(L)
+    d = h.decode()
+    assert np.array_equal(d["codes"], o.unpack_codes(L.qweight, bits))
+    assert np.array_equal(d["zeros"], o.unpack_zeros(L.qzeros, bits))
+    want_sc = L.scales.view(np.uint32) if sdt == "f32" else L.scales.astype(np.uint32)
+    assert np.array_equal(d["scales"], want_sc)
+    assert np.array_equal(d["perm"], o.runtime_perm(L.g_idx))
+    assert h.info()["has_perm"] == int(not np.array_equal(o.runtime_perm(L.g_idx), np.arange(K)))
+    h.close()
+
+
+# ---- GEMM parity on small shapes that span several tiles and a ragged tail -----------------------
+
+def _small_cases():
+    rng = np.random.default_rng(1234)
+    cases = []
+    for bits, xdt in itertools.product([2, 3, 4, 8], ["f16", "bf16"]):
+        for trial in range(3):
+            K = int(rng.choice([32, 96, 160, 256, 384, 544]))
+            N = int(rng.choice([32, 64, 96, 160, 288]))
+            gs = int(rng.choice([32, 64, 128, -1]))
+            if gs > K:
+                gs = -1
+            desc = bool(rng.integers(0, 2))
+            sdt = str(rng.choice(["f16", "bf16", "f32"]))
+            cases.append((K, N, bits, gs, desc, sdt, xdt))
+    return cases
+
+
+MS = [1, 2, 3, 5, 8, 16, 17, 33, 64, 65, 130]
+
+
+@pytest.mark.parametrize("K,N,bits,gs,desc,sdt,xdt", _small_cases())
+def test_gemm_small_shapes_both_paths(K, N, bits, gs, desc, sdt, xdt):
+    import weight_only_quantized_amd as wq
+    say("gemm-small", K, N, bits, gs, desc, sdt, xdt)
+    L = gi.make_layer(K, N, bits, gs, desc_act=desc, scales_dtype=sdt, seed=7 * K + N)
+    h = repack_layer(L)
+    x = gi.make_x(max(MS), K, xdt, seed=K * N)
+    y_ref_all = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, sdt, L.g_idx, bits)
+    for M in MS:
+        paths = [wq.PATH_TILED] + ([wq.PATH_SKINNY] if M <= 64 else [])
+        for p in paths:
+            y = run_gemm(h, x[:M], xdt, path=p)
+            check(y, xdt, y_ref_all[:M], label=(M, p))
+    h.close()
+
+
+# ---- closed-form special cases: bit-exact ------------------------------------------------------
+
+@pytest.mark.parametrize("bits,xdt", [(4, "f16"), (4, "bf16"), (2, "f16"), (3, "bf16"), (8, "f16"), (8, "bf16")])
+def test_identity_weight(bits, xdt):
+    """W = 0.5 * I.  fp16 operands (code - zero) and 8-bit bf16 operands are exact, so each output
+    is one exact product and must be bit-exact; the 2/3/4-bit bf16 operand carries a constant bias
+    of 144 removed in fp32 (see dequant.h), so there the bar is the bf16 tolerance."""
+    import torch
+    import weight_only_quantized_amd as wq
+    K = N = 256
+    z = 1
+    codes = np.full((K, N), z) + np.eye(K, dtype=np.int64)
+    zeros = np.full((1, N), z)
+    scales = gi.to_f16_bits(np.full((1, N), 0.5))
+    L = gi.Layer(K, N, bits, -1, False, o.pack_codes(codes, bits), o.pack_zeros(zeros, bits), scales, "f16",
+                 np.zeros(K, dtype=np.int32))
+    h = repack_layer(L)
+    x = gi.make_x(130, K, xdt, seed=3)
+    want = o.round_to_dtype_bits(o.decode_float_bits(x, xdt) * 0.5, xdt)
+    for M, p in [(1, wq.PATH_SKINNY), (16, wq.PATH_SKINNY), (64, wq.PATH_SKINNY), (1, wq.PATH_TILED), (130, wq.PATH_TILED)]:
+        y = run_gemm(h, x[:M], xdt, path=p)
+        if xdt == "f16" or bits == 8:
+            assert np.array_equal(y, want[:M]), (M, p)
+        else:
+            check(y, xdt, o.decode_float_bits(x[:M], xdt) * 0.5, label=(M, p))
+    h.close()
+
+
+def test_zero_weight_gives_exact_zero():
+    import weight_only_quantized_amd as wq
+    K, N, bits, gs = 256, 64, 4, 64
+    rng = np.random.default_rng(2)
+    zeros = rng.integers(1, 16, size=(K // gs, N))
+    codes = zeros[np.arange(K) // gs]
+    L0 = gi.make_layer(K, N, bits, gs, seed=4)
+    L = gi.Layer(K, N, bits, gs, False, o.pack_codes(codes, bits), o.pack_zeros(zeros, bits), L0.scales, "f16",
+                 L0.g_idx)
+    h = repack_layer(L)
+    x = gi.make_x(80, K, "f16", seed=5)
+    for M, p in [(1, wq.PATH_SKINNY), (80, wq.PATH_TILED)]:
+        y = run_gemm(h, x[:M], "f16", path=p)
+        assert np.all((y & 0x7FFF) == 0), (M, p)     # fp16 operands are exact zeros
+    h.close()
+
+
+# ---- lifetime and API behaviour -----------------------------------------------------------------
+
+def test_repeated_calls_are_bitwise_identical_and_inputs_can_be_freed():
+    import torch
+    import weight_only_quantized_amd as wq
+    L = gi.make_layer(512, 256, 4, 128, desc_act=True, seed=9)
+    h = repack_layer(L)        # the device copies of the checkpoint tensors are dropped right here
+    torch.cuda.empty_cache()
+    x = bits_to_device(gi.make_x(70, 512, "f16", seed=10), "f16")
+    for M, p in [(3, wq.PATH_SKINNY), (70, wq.PATH_TILED)]:
+        ys = [device_to_bits(h.gemm(x[:M], path=p)) for _ in range(4)]
+        for y in ys[1:]:
+            assert np.array_equal(ys[0], y)
+    h2 = repack_layer(L)
+    assert np.array_equal(device_to_bits(h2.gemm(x[:5])), device_to_bits(h.gemm(x[:5])))
+    h.close()
+    h2.close()
+
+
+def test_m_zero_launches_nothing_and_leaves_y_untouched():
+    import torch
+    import weight_only_quantized_amd as wq
+    L = gi.make_layer(256, 64, 4, 128, seed=1)
+    h = repack_layer(L)
+    lib = wq.load_library()
+    y = torch.full((1, 64), 7.0, dtype=torch.float16, device="cuda")
+    x = torch.zeros((1, 256), dtype=torch.float16, device="cuda")
+    st = lib.gptq_gemm(h.ptr, x.data_ptr(), 0, 0, y.data_ptr(), None, 0, 0, None)
+    torch.cuda.synchronize()
+    assert st == 0 and torch.all(y == 7.0)
+    h.close()
+
+
+def test_gemm_argument_errors():
+    import ctypes
+    import torch
+    import weight_only_quantized_amd as wq
+    lib = wq.load_library()
+    L = gi.make_layer(256, 64, 4, 128, desc_act=True, seed=1)
+    h = repack_layer(L)
+    x = torch.zeros((130, 256), dtype=torch.float16, device="cuda")
+    y = torch.zeros((130, 64), dtype=torch.float16, device="cuda")
+    need = h.workspace_size(130, torch.float16)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    s = None
+    assert lib.gptq_gemm(h.ptr, x.data_ptr(), 130, 0, y.data_ptr(), ws.data_ptr(), need - 1, 0, s) == 7
+    assert lib.gptq_gemm(h.ptr, x.data_ptr(), 130, 0, y.data_ptr(), None, 0, 0, s) == 7
+    assert lib.gptq_gemm(h.ptr, x.data_ptr() + 2, 1, 0, y.data_ptr(), ws.data_ptr(), need, 0, s) == 1
+    assert lib.gptq_gemm(h.ptr, x.data_ptr(), 130, 0, y.data_ptr(), ws.data_ptr(), need, wq.PATH_SKINNY, s) == 1
+    assert lib.gptq_gemm(h.ptr, x.data_ptr(), 130, 2, y.data_ptr(), ws.data_ptr(), need, 0, s) == 1
+    assert lib.gptq_gemm(h.ptr, x.data_ptr(), -1, 0, y.data_ptr(), ws.data_ptr(), need, 0, s) == 1
+    assert lib.gptq_gemm(h.ptr, x.data_ptr(), 130, 0, x.data_ptr(), ws.data_ptr(), need, 0, s) == 1
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+    h.close()
+
+
+def test_repack_rejects_bad_layers_on_device():
+    import torch
+    import weight_only_quantized_amd as wq
+    L = gi.make_layer(256, 64, 4, 64, desc_act=True, seed=2)
+    qw = torch.from_numpy(L.qweight).cuda()
+    qz = torch.from_numpy(L.qzeros).cuda()
+    sc = bits_to_device(L.scales, "f16")
+    g = L.g_idx.copy(); g[5] = 4
+    with pytest.raises(wq.GPTQError) as e:
+        wq.repack(qw, qz, sc, torch.from_numpy(g).cuda(), bits=4, group_size=64)
+    assert e.value.name == "E_GIDX"
+    with pytest.raises(wq.GPTQError) as e:
+        wq.repack(qw, qz, sc, torch.from_numpy(L.g_idx).cuda(), bits=4, group_size=64, checkpoint_format="marlin")
+    assert e.value.name == "E_UNSUPPORTED"
+    with pytest.raises(wq.GPTQError) as e:
+        wq.repack(qw[:-1].contiguous(), qz, sc, torch.from_numpy(L.g_idx).cuda(), bits=4, group_size=64)
+    assert e.value.name in ("E_SHAPE", "E_GIDX")

@@ -1,0 +1,236 @@
+"""Python binding of the GPTQ weight-only quantized linear layer for MI355X (gfx950).
+
+The binding only marshals arguments: it passes device pointers of torch tensors and the current
+HIP stream to the C ABI declared in include/gptq_mi355x.h.  Every step of the layer runs in the
+library's HIP kernels.  If the library is not built, importing still works but every call raises.
+There is no CPU or PyTorch fallback.
+
+    h = repack(qweight, qzeros, scales, g_idx, bits=4, group_size=128)
+    y = h.gemm(x)          # x [M, K] fp16/bf16 on the GPU -> y [M, N], same dtype
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["LIB_PATH", "GPTQError", "Desc", "Handle", "load_library", "repack", "validate", "symbols",
+           "STATUS", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi355x.so")
+
+STATUS = {0: "OK", 1: "E_INVALID_ARG", 2: "E_SHAPE", 3: "E_GIDX", 4: "E_UNSUPPORTED", 5: "E_HIP",
+          6: "E_OOM", 7: "E_WORKSPACE", 8: "E_DEVICE"}
+F16, BF16, F32 = 0, 1, 2
+FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2}
+PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
+
+# Every symbol include/gptq_mi355x.h declares.
+symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_destroy",
+           "gptq_info", "gptq_decode_runtime", "gptq_status_str", "gptq_last_hip_error"]
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status, where, lib=None):
+        msg = STATUS.get(status, str(status))
+        if lib is not None:
+            msg += ": " + lib.gptq_status_str(status).decode()
+            if status == 5:
+                msg += f" (hipError {lib.gptq_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("desc_act", ctypes.c_int32), ("checkpoint_format", ctypes.c_int32),
+                ("scales_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("qweight_shape", ctypes.c_int64 * 2), ("qzeros_shape", ctypes.c_int64 * 2),
+                ("scales_shape", ctypes.c_int64 * 2), ("g_idx_len", ctypes.c_int64)]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("groups", ctypes.c_int32), ("padded_in_features", ctypes.c_int32),
+                ("has_perm", ctypes.c_int32), ("scales_dtype", ctypes.c_int32), ("runtime_bytes", ctypes.c_int64),
+                ("device", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                           "or `python weight_only_quantized_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.gptq_validate.argtypes = [ctypes.POINTER(Desc), P]
+    lib.gptq_repack.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, ctypes.POINTER(P)]
+    lib.gptq_workspace_size.argtypes = [P, I64, I32, I32, ctypes.POINTER(SZ)]
+    lib.gptq_gemm.argtypes = [P, P, I64, I32, P, P, SZ, I32, P]
+    lib.gptq_destroy.argtypes = [P]
+    lib.gptq_info.argtypes = [P, ctypes.POINTER(Info)]
+    lib.gptq_decode_runtime.argtypes = [P, P, P, P, P]
+    lib.gptq_status_str.argtypes = [I32]
+    lib.gptq_status_str.restype = ctypes.c_char_p
+    lib.gptq_last_hip_error.argtypes = []
+    for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_destroy", "gptq_info",
+              "gptq_decode_runtime", "gptq_last_hip_error"):
+        getattr(lib, f).restype = I32
+    _lib = lib
+    return lib
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.float16:
+        return F16
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def make_desc(K, N, bits, group_size, scales_dtype, qweight_shape, qzeros_shape, scales_shape, g_idx_len,
+              desc_act=False, checkpoint_format="gptq") -> Desc:
+    d = Desc()
+    d.in_features, d.out_features, d.bits, d.group_size = K, N, bits, group_size
+    d.desc_act = int(bool(desc_act))
+    d.checkpoint_format = FORMATS[checkpoint_format] if isinstance(checkpoint_format, str) else int(checkpoint_format)
+    d.scales_dtype = scales_dtype
+    d.reserved = 0
+    d.qweight_shape[:] = list(qweight_shape)
+    d.qzeros_shape[:] = list(qzeros_shape)
+    d.scales_shape[:] = list(scales_shape)
+    d.g_idx_len = g_idx_len
+    return d
+
+
+def validate(desc: Desc, g_idx_host=None) -> int:
+    """Host-only validation (needs no GPU).  g_idx_host: a numpy int32 array or None.  Returns the status."""
+    lib = load_library()
+    ptr = None
+    if g_idx_host is not None:
+        import numpy as np
+        g = np.ascontiguousarray(g_idx_host, dtype=np.int32)
+        ptr = g.ctypes.data_as(ctypes.c_void_p)
+        return lib.gptq_validate(ctypes.byref(desc), ptr)
+    return lib.gptq_validate(ctypes.byref(desc), None)
+
+
+def _stream_ptr(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Handle:
+    """A repacked layer living on one GPU.  Owns the runtime layout until close()."""
+
+    def __init__(self, lib, ptr, K, N, bits, group_size):
+        self._lib, self._ptr = lib, ptr
+        self.K, self.N, self.bits, self.group_size = K, N, bits, group_size
+
+    @property
+    def ptr(self):
+        if not self._ptr:
+            raise RuntimeError("handle is closed")
+        return self._ptr
+
+    def info(self) -> dict:
+        inf = Info()
+        st = self._lib.gptq_info(self.ptr, ctypes.byref(inf))
+        if st:
+            raise GPTQError(st, "gptq_info", self._lib)
+        return {f: getattr(inf, f) for f, _ in Info._fields_}
+
+    def workspace_size(self, M, dtype, path=PATH_AUTO) -> int:
+        n = ctypes.c_size_t(0)
+        st = self._lib.gptq_workspace_size(self.ptr, M, _dtype_code(dtype), path, ctypes.byref(n))
+        if st:
+            raise GPTQError(st, "gptq_workspace_size", self._lib)
+        return n.value
+
+    def gemm(self, x, out=None, workspace=None, path=PATH_AUTO, stream=None):
+        """y = x . W^T; x [M, K] fp16/bf16 on this handle's GPU.  `workspace` (uint8 tensor) is
+        allocated from torch's caching allocator when not given."""
+        import torch
+        if x.dim() != 2 or x.shape[1] != self.K:
+            raise ValueError(f"x must be [M, {self.K}]")
+        x = x.contiguous()
+        M = x.shape[0]
+        if out is None:
+            out = torch.empty((M, self.N), dtype=x.dtype, device=x.device)
+        elif out.shape != (M, self.N) or out.dtype != x.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [M, N] tensor of x's dtype")
+        need = self.workspace_size(M, x.dtype, path)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        st = self._lib.gptq_gemm(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), out.data_ptr(), ws_ptr, ws_n,
+                                 path, _stream_ptr(stream))
+        if st:
+            raise GPTQError(st, "gptq_gemm", self._lib)
+        return out
+
+    def decode(self) -> dict:
+        """Test hook: the runtime layout decoded back to logical codes / zeros / scale bits / perm."""
+        import numpy as np
+        codes = np.zeros((self.K, self.N), dtype=np.uint8)
+        inf = self.info()
+        G = inf["groups"]
+        zeros = np.zeros((G, self.N), dtype=np.int32)
+        scales = np.zeros((G, self.N), dtype=np.uint32)
+        perm = np.zeros(self.K, dtype=np.int32)
+        st = self._lib.gptq_decode_runtime(self.ptr, codes.ctypes.data, zeros.ctypes.data, scales.ctypes.data,
+                                           perm.ctypes.data)
+        if st:
+            raise GPTQError(st, "gptq_decode_runtime", self._lib)
+        return {"codes": codes, "zeros": zeros, "scales": scales, "perm": perm}
+
+    def close(self):
+        if self._ptr:
+            st = self._lib.gptq_destroy(self._ptr)
+            self._ptr = None
+            if st:
+                raise GPTQError(st, "gptq_destroy", self._lib)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def repack(qweight, qzeros, scales, g_idx=None, *, bits, group_size, desc_act=False, checkpoint_format="gptq",
+           stream=None) -> Handle:
+    """Build the runtime layout from checkpoint tensors on the current GPU (int32 qweight/qzeros,
+    fp16/bf16/fp32 scales, optional int32 g_idx).  The inputs may be freed afterwards."""
+    import torch
+    lib = load_library()
+    for name, t in (("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise TypeError("qweight and qzeros must be int32")
+    K = qweight.shape[0] * 32 // bits if bits in (2, 3, 4, 8) else 0
+    if g_idx is not None:
+        if g_idx.dtype != torch.int32 or not g_idx.is_cuda or not g_idx.is_contiguous():
+            raise TypeError("g_idx must be a contiguous int32 GPU tensor")
+        K = g_idx.shape[0]
+    N = qweight.shape[1]
+    d = make_desc(K, N, bits, group_size, _dtype_code(scales.dtype), qweight.shape, qzeros.shape, scales.shape,
+                  0 if g_idx is None else g_idx.shape[0], desc_act, checkpoint_format)
+    out = ctypes.c_void_p()
+    st = lib.gptq_repack(ctypes.byref(d), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                         None if g_idx is None else g_idx.data_ptr(), _stream_ptr(stream), ctypes.byref(out))
+    if st:
+        raise GPTQError(st, "gptq_repack", lib)
+    return Handle(lib, out, K, N, bits, group_size)

@@ -1,0 +1,370 @@
+// Host side of the C ABI: validation, handle lifecycle, dispatch and the decode test hook.
+//
+// Validation follows "GPTQ packed checkpoint (safetensors / torch)", section "Reject the file
+// when" (GPTQ-001 .. GPTQ-006), with the load-time sort of the inputs by g_idx from
+// "39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes", section "The format".
+// Caller-supplied scratch is checked for capacity and alignment and never silently replaced,
+// as "Kernel Backends Reference", section "Marlin and caller-owned scratch", asks of a scratch
+// contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+
+namespace gq {
+
+static thread_local int32_t t_last_hip = 0;
+
+gptq_status hip_fail(hipError_t e) {
+  t_last_hip = (int32_t)e;
+  return GPTQ_E_HIP;
+}
+
+static int groups_of(int K, int gs) { return gs == -1 ? 1 : (K + gs - 1) / gs; }
+
+// MFMA K steps (of 32 inputs) per scale-fixup segment: a whole 128-input chunk when groups are
+// whole chunks (group_size a multiple of 128, or -1: one group), else one step.
+static int seg_steps_of(int gs_eff, int gs) {
+  if (gs == -1) return 4;                 // one group: any segmentation of K is exact
+  return (gs_eff / 32) % 4 == 0 ? 4 : 1;
+}
+
+static bool is_gfx950_device(int dev) {
+  static std::mutex mu;
+  static int cache[64];
+  static bool init = false;
+  std::lock_guard<std::mutex> g(mu);
+  if (!init) { for (int i = 0; i < 64; ++i) cache[i] = -1; init = true; }
+  if (dev < 0 || dev >= 64) return false;
+  if (cache[dev] < 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return false;
+    cache[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  }
+  return cache[dev] == 1;
+}
+
+// Shape/format checks that need no g_idx values.
+static gptq_status validate_desc(const gptq_layer_desc* d) {
+  if (!d || d->reserved != 0) return GPTQ_E_INVALID_ARG;
+  const int b = d->bits;
+  if (b != 2 && b != 3 && b != 4 && b != 8) return GPTQ_E_UNSUPPORTED;           // GPTQ-001
+  if (d->checkpoint_format != GPTQ_FORMAT_GPTQ) return GPTQ_E_UNSUPPORTED;        // GPTQ-005
+  if (d->scales_dtype != GPTQ_F16 && d->scales_dtype != GPTQ_BF16 && d->scales_dtype != GPTQ_F32)
+    return GPTQ_E_INVALID_ARG;
+  const int gs = d->group_size;
+  if (gs != -1 && (gs <= 0 || gs % 32 != 0)) return GPTQ_E_UNSUPPORTED;
+  const int64_t K = d->in_features, N = d->out_features;
+  if (K <= 0 || K % 32 != 0 || K > (1 << 20)) return GPTQ_E_SHAPE;               // GPTQ-002
+  if (d->qweight_shape[0] != K / 32 * b || d->qweight_shape[1] != N) return GPTQ_E_SHAPE;
+  if (N <= 0 || N % 32 != 0 || N > (1 << 20) || K * N > (int64_t(1) << 36)) return GPTQ_E_SHAPE;
+  const int64_t G = groups_of((int)K, gs);
+  if (d->qzeros_shape[0] != G || d->qzeros_shape[1] != N / 32 * b) return GPTQ_E_SHAPE;  // GPTQ-003
+  if (d->scales_shape[0] != G || d->scales_shape[1] != N) return GPTQ_E_SHAPE;
+  if (d->g_idx_len != 0 && d->g_idx_len != K) return GPTQ_E_GIDX;                 // GPTQ-004
+  return GPTQ_OK;
+}
+
+// GPTQ-004 range check, the whole-group reading, and the stable sort (counting sort by group).
+// perm (size K) receives the input index at each sorted position.
+static gptq_status check_gidx_and_sort(const gptq_layer_desc* d, const int32_t* g, int32_t* perm,
+                                       int* has_perm) {
+  const int K = d->in_features;
+  const int G = groups_of(K, d->group_size);
+  const int gs_eff = d->group_size == -1 ? K : d->group_size;
+  std::vector<int32_t> count(G + 1, 0);
+  for (int k = 0; k < K; ++k) {
+    if (g[k] < 0 || g[k] >= G) return GPTQ_E_GIDX;
+    count[g[k] + 1]++;
+  }
+  // whole groups: group q must hold exactly the sorted positions [q*gs, min((q+1)*gs, K))
+  for (int q = 0; q < G; ++q) {
+    int want = (q + 1) * gs_eff < K ? gs_eff : K - q * gs_eff;
+    if (count[q + 1] != want) return GPTQ_E_UNSUPPORTED;
+  }
+  for (int q = 0; q < G; ++q) count[q + 1] += count[q];
+  int hp = 0;
+  for (int k = 0; k < K; ++k) {
+    int pos = count[g[k]]++;
+    if (perm) perm[pos] = k;
+    if (pos != k) hp = 1;
+  }
+  if (has_perm) *has_perm = hp;
+  return GPTQ_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+static void free_layer(gptq_layer* L) {
+  if (!L) return;
+  if (L->wq) (void)hipFree(L->wq);
+  if (L->scales_rt) (void)hipFree(L->scales_rt);
+  if (L->zeros_rt) (void)hipFree(L->zeros_rt);
+  if (L->perm) (void)hipFree(L->perm);
+  L->magic = 0;
+  delete L;
+}
+
+static gptq_status check_handle(gptq_handle_t h) {
+  if (!h || h->magic != GQ_MAGIC) return GPTQ_E_INVALID_ARG;
+  return GPTQ_OK;
+}
+
+}  // namespace gq
+
+using namespace gq;
+
+extern "C" {
+
+gptq_status gptq_validate(const gptq_layer_desc* desc, const int32_t* g_idx_host) {
+  gptq_status s = validate_desc(desc);
+  if (s != GPTQ_OK || !g_idx_host) return s;
+  if (desc->g_idx_len != desc->in_features) return GPTQ_E_GIDX;
+  return check_gidx_and_sort(desc, g_idx_host, nullptr, nullptr);
+}
+
+gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, const int32_t* qzeros,
+                        const void* scales, const int32_t* g_idx, void* stream_, gptq_handle_t* out) {
+  if (!out) return GPTQ_E_INVALID_ARG;
+  *out = nullptr;
+  gptq_status st = validate_desc(desc);
+  if (st != GPTQ_OK) return st;
+  if (!qweight || !qzeros || !scales) return GPTQ_E_INVALID_ARG;
+  if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 4)) return GPTQ_E_INVALID_ARG;
+  if (g_idx && desc->g_idx_len != desc->in_features) return GPTQ_E_GIDX;
+  if (!g_idx && desc->g_idx_len != 0) return GPTQ_E_INVALID_ARG;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (!is_gfx950_device(dev)) return GPTQ_E_DEVICE;
+  hipStream_t s = (hipStream_t)stream_;
+
+  const int K = desc->in_features, N = desc->out_features;
+  const int Kp = (K + kChunkK - 1) / kChunkK * kChunkK;
+  std::vector<int32_t> perm_host(Kp, -1);
+  int has_perm = 0;
+  if (g_idx) {
+    std::vector<int32_t> gh(K);
+    e = hipMemcpyAsync(gh.data(), g_idx, sizeof(int32_t) * K, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e);
+    st = check_gidx_and_sort(desc, gh.data(), perm_host.data(), &has_perm);
+    if (st != GPTQ_OK) return st;
+  } else {
+    for (int k = 0; k < K; ++k) perm_host[k] = k;
+  }
+
+  gptq_layer* L = new (std::nothrow) gptq_layer();
+  if (!L) return GPTQ_E_OOM;
+  std::memset(L, 0, sizeof(*L));
+  L->magic = GQ_MAGIC;
+  L->device = dev;
+  L->K = K; L->N = N; L->bits = desc->bits; L->group_size = desc->group_size;
+  L->gs_eff = desc->group_size == -1 ? K : desc->group_size;
+  L->G = groups_of(K, desc->group_size);
+  L->Kp = Kp; L->KC = Kp / kChunkK; L->CT = N / kTileN;
+  L->scales_dtype = desc->scales_dtype;
+  L->has_perm = has_perm;
+  L->seg_steps = seg_steps_of(L->gs_eff, desc->group_size);
+
+  const size_t wq_bytes = (size_t)L->CT * L->KC * unit_words(L->bits) * 4;
+  const size_t meta_n = (size_t)L->CT * L->G * kTileN;
+  const size_t sc_bytes = meta_n * (L->scales_dtype == GPTQ_F32 ? 4 : 2);
+  const size_t perm_bytes = sizeof(int32_t) * Kp;
+  if (hipMalloc((void**)&L->wq, wq_bytes) != hipSuccess ||
+      hipMalloc(&L->scales_rt, sc_bytes) != hipSuccess ||
+      hipMalloc((void**)&L->zeros_rt, meta_n) != hipSuccess ||
+      hipMalloc((void**)&L->perm, perm_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    free_layer(L);
+    return GPTQ_E_OOM;
+  }
+  L->bytes = (int64_t)(wq_bytes + sc_bytes + meta_n + (has_perm ? perm_bytes : 0));
+  e = hipMemcpyAsync(L->perm, perm_host.data(), perm_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = launch_repack(L, qweight, qzeros, scales, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    free_layer(L);
+    return hip_fail(e);
+  }
+  if (!has_perm) {  // identity order: the kernels do not need the table
+    (void)hipFree(L->perm);
+    L->perm = nullptr;
+  }
+  *out = L;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int32_t path,
+                                size_t* bytes) {
+  gptq_status st = check_handle(h);
+  if (st != GPTQ_OK) return st;
+  if (!bytes || M < 0 || (x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16)) return GPTQ_E_INVALID_ARG;
+  if (path == GPTQ_PATH_AUTO) path = M <= kSkinnyMaxM ? GPTQ_PATH_SKINNY : GPTQ_PATH_TILED;
+  if (path != GPTQ_PATH_SKINNY && path != GPTQ_PATH_TILED) return GPTQ_E_INVALID_ARG;
+  if (path == GPTQ_PATH_SKINNY && M > kSkinnyMaxM) return GPTQ_E_INVALID_ARG;
+  size_t b = 0;
+  if (M > 0) {
+    if (h->has_perm) b += ws_xsorted_bytes(h, M);
+    if (path == GPTQ_PATH_TILED && needs_nsb(h, x_dtype == GPTQ_BF16)) b += ws_nsb_bytes(h, M);
+  }
+  *bytes = b;
+  return GPTQ_OK;
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, void* y,
+                      void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  gptq_status st = check_handle(h);
+  if (st != GPTQ_OK) return st;
+  if (M < 0 || M > (int64_t(1) << 24)) return GPTQ_E_INVALID_ARG;
+  if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16) return GPTQ_E_INVALID_ARG;
+  if (path == GPTQ_PATH_AUTO) path = M <= kSkinnyMaxM ? GPTQ_PATH_SKINNY : GPTQ_PATH_TILED;
+  if (path != GPTQ_PATH_SKINNY && path != GPTQ_PATH_TILED) return GPTQ_E_INVALID_ARG;
+  if (path == GPTQ_PATH_SKINNY && M > kSkinnyMaxM) return GPTQ_E_INVALID_ARG;
+  if (M == 0) return GPTQ_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return GPTQ_E_INVALID_ARG;
+  const size_t xb = (size_t)M * h->K * 2, yb = (size_t)M * h->N * 2;
+  if (overlaps(x, xb, y, yb)) return GPTQ_E_INVALID_ARG;
+  size_t need = 0;
+  st = gptq_workspace_size(h, M, x_dtype, path, &need);
+  if (st != GPTQ_OK) return st;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return GPTQ_E_WORKSPACE;
+    if (overlaps(workspace, need, x, xb) || overlaps(workspace, need, y, yb)) return GPTQ_E_INVALID_ARG;
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev != h->device) return GPTQ_E_DEVICE;
+
+  GemmCall c{h, x, M, x_dtype == GPTQ_BF16 ? 1 : 0, y, workspace, workspace_bytes, (hipStream_t)stream};
+  e = path == GPTQ_PATH_SKINNY ? launch_skinny(c) : launch_tiled(c);
+  if (e != hipSuccess) return hip_fail(e);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_destroy(gptq_handle_t h) {
+  if (!h) return GPTQ_OK;
+  gptq_status st = check_handle(h);
+  if (st != GPTQ_OK) return st;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != h->device) (void)hipSetDevice(h->device);
+  hipError_t e = hipDeviceSynchronize();
+  free_layer(h);
+  if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
+  return e == hipSuccess ? GPTQ_OK : hip_fail(e);
+}
+
+gptq_status gptq_info(gptq_handle_t h, gptq_handle_info* info) {
+  gptq_status st = check_handle(h);
+  if (st != GPTQ_OK) return st;
+  if (!info) return GPTQ_E_INVALID_ARG;
+  info->in_features = h->K;
+  info->out_features = h->N;
+  info->bits = h->bits;
+  info->group_size = h->group_size;
+  info->groups = h->G;
+  info->padded_in_features = h->Kp;
+  info->has_perm = h->has_perm;
+  info->scales_dtype = h->scales_dtype;
+  info->runtime_bytes = h->bytes;
+  info->device = h->device;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t* zeros_gn_host,
+                                uint32_t* scales_gn_host, int32_t* perm_host) {
+  gptq_status st = check_handle(h);
+  if (st != GPTQ_OK) return st;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e);
+  const int K = h->K, N = h->N, G = h->G, bits = h->bits;
+  std::vector<int32_t> perm(h->Kp);
+  if (h->perm) {
+    e = hipMemcpy(perm.data(), h->perm, sizeof(int32_t) * h->Kp, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+  } else {
+    for (int k = 0; k < h->Kp; ++k) perm[k] = k < K ? k : -1;
+  }
+  if (perm_host) std::memcpy(perm_host, perm.data(), sizeof(int32_t) * K);
+  if (codes_kn_host) {
+    const size_t nw = (size_t)h->CT * h->KC * unit_words(bits);
+    std::vector<uint32_t> w(nw);
+    e = hipMemcpy(w.data(), h->wq, nw * 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int ct = 0; ct < h->CT; ++ct)
+      for (int kc = 0; kc < h->KC; ++kc) {
+        const uint32_t* u = w.data() + ((size_t)ct * h->KC + kc) * unit_words(bits);
+        for (int lane = 0; lane < kLanes; ++lane)
+          for (int i = 0; i < 32; ++i) {
+            Piece p[2];
+            int np = code_pieces(bits, i, p);
+            uint32_t code = 0;
+            for (int q = 0; q < np; ++q) {
+              uint32_t word = u[unit_word_offset(bits, lane, p[q].word)];
+              code |= ((word >> p[q].bit) & ((1u << p[q].nb) - 1)) << p[q].cbit;
+            }
+            const int ks = kc * kChunkK + code_k_in_chunk(lane, i);
+            const int n = ct * kTileN + lane_col(lane);
+            if (ks < K) codes_kn_host[(size_t)perm[ks] * N + n] = (uint8_t)code;
+          }
+      }
+  }
+  const size_t meta_n = (size_t)h->CT * G * kTileN;
+  if (zeros_gn_host) {
+    std::vector<uint8_t> z(meta_n);
+    e = hipMemcpy(z.data(), h->zeros_rt, meta_n, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int ct = 0; ct < h->CT; ++ct)
+      for (int g = 0; g < G; ++g)
+        for (int j = 0; j < kTileN; ++j)
+          zeros_gn_host[(size_t)g * N + ct * kTileN + j] = (int32_t)z[((size_t)ct * G + g) * kTileN + j] + 1;
+  }
+  if (scales_gn_host) {
+    const bool f32 = h->scales_dtype == GPTQ_F32;
+    std::vector<uint8_t> sraw(meta_n * (f32 ? 4 : 2));
+    e = hipMemcpy(sraw.data(), h->scales_rt, sraw.size(), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int ct = 0; ct < h->CT; ++ct)
+      for (int g = 0; g < G; ++g)
+        for (int j = 0; j < kTileN; ++j) {
+          size_t src = ((size_t)ct * G + g) * kTileN + j;
+          uint32_t v = f32 ? reinterpret_cast<uint32_t*>(sraw.data())[src]
+                           : reinterpret_cast<uint16_t*>(sraw.data())[src];
+          scales_gn_host[(size_t)g * N + ct * kTileN + j] = v;
+        }
+  }
+  return GPTQ_OK;
+}
+
+const char* gptq_status_str(gptq_status s) {
+  switch (s) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_E_INVALID_ARG: return "invalid argument";
+    case GPTQ_E_SHAPE: return "tensor shape does not match the layer (GPTQ-002/003)";
+    case GPTQ_E_GIDX: return "g_idx length or index out of range (GPTQ-004)";
+    case GPTQ_E_UNSUPPORTED: return "unsupported bits, format, group size or g_idx structure";
+    case GPTQ_E_HIP: return "HIP runtime error";
+    case GPTQ_E_OOM: return "out of device memory";
+    case GPTQ_E_WORKSPACE: return "workspace too small or misaligned";
+    case GPTQ_E_DEVICE: return "no gfx950 device, or handle used on another device";
+  }
+  return "unknown status";
+}
+
+int32_t gptq_last_hip_error(void) { return t_last_hip; }
+
+}  // extern "C"

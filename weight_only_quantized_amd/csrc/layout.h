@@ -1,0 +1,83 @@
+// Runtime (kernel-private) weight layout of the GPTQ linear layer on gfx950.
+//
+// The checkpoint layout ("GPTQ packed checkpoint (safetensors / torch)", sections "GptqLayer"
+// and "Reader") packs 32/bits codes per int32 along the input dimension K, row-major over N.
+// The kernels instead want every lane of a 64-wide wave to fetch, with one contiguous 16-byte
+// load, exactly the codes that feed its B operand of v_mfma_f32_16x16x32_{f16,bf16}:
+//
+//   16x16x32 B operand (verified on the device): lane l holds column j = l % 16 and the eight
+//   consecutive k = 8 * (l / 16) + e, e = 0..7, of a 32-deep K step.
+//
+// Units.  Columns are cut into tiles of 16 (CT = N / 16 tiles) and the load-time-sorted input
+// dimension into chunks of 128 (KC = Kp / 128, Kp = K rounded up to 128; padded inputs have
+// code 0 and are multiplied by x = 0).  One unit = one (tile, chunk) = 16 x 128 codes =
+// 256 * bits bytes, stored tile-major: unit index = ct * KC + kc.  Inside a unit, lane l owns the
+// 32 codes  i = 8 * t + e  (t = MFMA step 0..3, e = 0..7) at sorted k = 128 kc + 32 t + 8 (l/16) + e
+// and column n = 16 ct + l % 16, held in WPL = bits 32-bit words.  Word order inside a unit:
+// [part][lane][w] with parts of up to four words (8-bit: two parts), so each wave-wide load of a
+// part is one contiguous 64 x 16 B (or x 8 B / x 12 B) block.
+//
+// Code placement inside a lane's words is chosen so that four codes come out as the four bytes
+// of one register ("byte vector" BV_j holds codes 4j .. 4j+3 in bytes 0..3) with one shift and
+// one mask, for 2-, 3- and 4-bit codes:
+//   4-bit: code i = 8t + 4h + b  at word t, bit 8b + 4h            (BV_{2t+h} = (w_t >> 4h) & 0x0F0F0F0F)
+//   2-bit: code i = 16u + 4h + b at word u, bit 8b + 2h            (BV_{4u+h} = (w_u >> 2h) & 0x03030303)
+//   3-bit: code i < 24, i = 8u + 4h + b at word u, bit 8b + 3h      (BV_{2u+h} = (w_u >> 3h) & 0x07070707)
+//          code 24 + b: bits 0-1 at word 0 bit 8b+6, bit 2 at word 1 bit 8b+6
+//          code 28 + b: bit 0 at word 1 bit 8b+7, bits 1-2 at word 2 bit 8b+6
+//          (the two spare bits of every byte of the three words carry the last eight codes)
+//   8-bit: code i = 8t + 4h + c  at word 2t + h, byte {0, 2, 1, 3}[c]
+//          ((w & 0x00FF00FF) holds codes c = 0, 1 in its two 16-bit halves, (w >> 8) & 0x00FF00FF
+//          codes c = 2, 3)
+//
+// Group metadata is re-tiled the same way: scales_rt[(ct * G + g) * 16 + j] (16- or 32-bit raw
+// bits) and zeros_rt[(ct * G + g) * 16 + j] = stored zero (z - 1), uint8.
+#pragma once
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define GQ_HD __host__ __device__ __forceinline__
+#else
+#define GQ_HD inline
+#endif
+
+namespace gq {
+
+constexpr int kChunkK = 128;   // sorted-K chunk of one unit
+constexpr int kTileN = 16;     // columns per tile
+constexpr int kLanes = 64;
+
+GQ_HD int words_per_lane(int bits) { return bits; }
+GQ_HD int64_t unit_words(int bits) { return (int64_t)kLanes * bits; }
+
+// Word offset (within a unit) of lane `lane`'s word `w`.
+GQ_HD int unit_word_offset(int bits, int lane, int w) {
+  if (bits <= 4) return lane * bits + w;
+  return (w >> 2) * (kLanes * 4) + lane * 4 + (w & 3);
+}
+
+// A piece of a code: `nb` bits of word `word` starting at bit `bit` hold code bits
+// [cbit, cbit + nb).  Every code has one or two pieces.
+struct Piece { int word, bit, nb, cbit; };
+
+GQ_HD int code_pieces(int bits, int i, Piece* p) {
+  if (bits == 4) { int t = i >> 3, h = (i >> 2) & 1, b = i & 3; p[0] = {t, 8 * b + 4 * h, 4, 0}; return 1; }
+  if (bits == 2) { int u = i >> 4, h = (i >> 2) & 3, b = i & 3; p[0] = {u, 8 * b + 2 * h, 2, 0}; return 1; }
+  if (bits == 8) {
+    int t = i >> 3, h = (i >> 2) & 1, c = i & 3;
+    const int byte_of[4] = {0, 2, 1, 3};
+    p[0] = {2 * t + h, 8 * byte_of[c], 8, 0};
+    return 1;
+  }
+  // bits == 3
+  if (i < 24) { int u = i >> 3, h = (i >> 2) & 1, b = i & 3; p[0] = {u, 8 * b + 3 * h, 3, 0}; return 1; }
+  int b = i & 3;
+  if (i < 28) { p[0] = {0, 8 * b + 6, 2, 0}; p[1] = {1, 8 * b + 6, 1, 2}; return 2; }
+  p[0] = {1, 8 * b + 7, 1, 0}; p[1] = {2, 8 * b + 6, 2, 1}; return 2;
+}
+
+// Sorted-K offset within the chunk, and column within the tile, of lane code i.
+GQ_HD int code_k_in_chunk(int lane, int i) { return 32 * (i >> 3) + 8 * (lane >> 4) + (i & 7); }
+GQ_HD int lane_col(int lane) { return lane & 15; }
+
+}  // namespace gq

@@ -1,0 +1,113 @@
+// Load-time repack: checkpoint tensors -> runtime layout (see layout.h).
+//
+// Reads the AutoGPTQ pack of "GPTQ packed checkpoint (safetensors / torch)", section "Reader":
+// codes run along the input dimension, low bits first, 32/bits per word for 2/4/8 bits; 3-bit
+// codes form one 96-bit little-endian stream per 32 codes over three consecutive rows (the
+// "10 / split / 10" layout).  qzeros uses the same rule along the output dimension.  Inputs are
+// visited in the load-time sorted order ("39. Quantized checkpoints ...", "The format").
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace gq {
+
+// Code of input k, output n from a row-packed int32 array `w` with `ld` words per row.
+__device__ __forceinline__ uint32_t packed_field(const uint32_t* __restrict__ w, int64_t ld, int bits,
+                                                 int64_t k, int64_t n) {
+  if (bits == 3) {
+    const int64_t blk = k >> 5;
+    const int bit = 3 * (int)(k & 31);
+    const int64_t row = 3 * blk + (bit >> 5);
+    const int sh = bit & 31;
+    uint32_t v = w[row * ld + n] >> sh;
+    if (sh > 29) v |= w[(row + 1) * ld + n] << (32 - sh);
+    return v & 7u;
+  }
+  const int pack = 32 / bits;
+  const uint32_t v = w[(k / pack) * ld + n];
+  return (v >> (bits * (int)(k % pack))) & ((1u << bits) - 1u);
+}
+
+// Same rule along the row (qzeros: group row g, output column n).
+__device__ __forceinline__ uint32_t packed_field_cols(const uint32_t* __restrict__ w, int64_t ld, int bits,
+                                                      int64_t g, int64_t n) {
+  if (bits == 3) {
+    const int64_t blk = n >> 5;
+    const int bit = 3 * (int)(n & 31);
+    const int64_t col = 3 * blk + (bit >> 5);
+    const int sh = bit & 31;
+    uint32_t v = w[g * ld + col] >> sh;
+    if (sh > 29) v |= w[g * ld + col + 1] << (32 - sh);
+    return v & 7u;
+  }
+  const int pack = 32 / bits;
+  const uint32_t v = w[g * ld + n / pack];
+  return (v >> (bits * (int)(n % pack))) & ((1u << bits) - 1u);
+}
+
+// One thread per (unit, lane): gathers the lane's 32 codes and writes its `bits` words.
+__global__ void __launch_bounds__(256) repack_words_kernel(
+    const uint32_t* __restrict__ qweight, const int32_t* __restrict__ perm, uint32_t* __restrict__ out,
+    int K, int N, int bits, int KC, int64_t n_lanes) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_lanes) return;
+  const int lane = (int)(gid & 63);
+  const int64_t unit = gid >> 6;
+  const int kc = (int)(unit % KC);
+  const int64_t ct = unit / KC;
+  const int64_t n = ct * kTileN + lane_col(lane);
+  uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 0; i < 32; ++i) {
+    const int ks = kc * kChunkK + code_k_in_chunk(lane, i);
+    uint32_t code = 0;
+    if (ks < K) {
+      const int k = perm[ks];
+      code = packed_field(qweight, N, bits, k, n);
+    }
+    Piece p[2];
+    const int np = code_pieces(bits, i, p);
+    for (int q = 0; q < np; ++q) {
+      const uint32_t part = (code >> p[q].cbit) & ((1u << p[q].nb) - 1u);
+      words[p[q].word] |= part << p[q].bit;
+    }
+  }
+  uint32_t* u = out + unit * unit_words(bits);
+  for (int w = 0; w < bits; ++w) u[unit_word_offset(bits, lane, w)] = words[w];
+}
+
+// One thread per (tile, group, column-in-tile): scale bits and stored zero.
+__global__ void __launch_bounds__(256) repack_meta_kernel(
+    const uint32_t* __restrict__ qzeros, const void* __restrict__ scales, int scale_bytes,
+    void* __restrict__ scales_rt, uint8_t* __restrict__ zeros_rt, int N, int G, int bits, int64_t total) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int j = (int)(gid & 15);
+  const int64_t cg = gid >> 4;          // ct * G + g
+  const int g = (int)(cg % G);
+  const int64_t ct = cg / G;
+  const int64_t n = ct * kTileN + j;
+  const int64_t zld = (int64_t)N / 32 * bits;
+  zeros_rt[gid] = (uint8_t)packed_field_cols(qzeros, zld, bits, g, n);
+  if (scale_bytes == 4)
+    reinterpret_cast<uint32_t*>(scales_rt)[gid] = reinterpret_cast<const uint32_t*>(scales)[(int64_t)g * N + n];
+  else
+    reinterpret_cast<uint16_t*>(scales_rt)[gid] = reinterpret_cast<const uint16_t*>(scales)[(int64_t)g * N + n];
+}
+
+hipError_t launch_repack(const gptq_layer* L, const int32_t* qweight, const int32_t* qzeros,
+                         const void* scales, hipStream_t s) {
+  const int64_t n_lanes = (int64_t)L->CT * L->KC * kLanes;
+  const int64_t blocks = (n_lanes + 255) / 256;
+  hipLaunchKernelGGL(repack_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(qweight), L->perm, L->wq, L->K, L->N, L->bits,
+                     L->KC, n_lanes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)L->CT * L->G * kTileN;
+  hipLaunchKernelGGL(repack_meta_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(qzeros), scales, L->scales_dtype == GPTQ_F32 ? 4 : 2,
+                     L->scales_rt, L->zeros_rt, L->N, L->G, L->bits, total);
+  return hipGetLastError();
+}
+
+}  // namespace gq
