@@ -114,7 +114,8 @@ def time_calls(w: Workload, steps: int, warmup: int, copies=None, graph=False):
     ys = [torch.empty((w.M, w.N), dtype=tdt, device=dev) for _ in range(min(R, 4))]
     need = hs[0].workspace_size(w.M, tdt)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    # graph capture needs a side stream (default priority); eager calls use the current stream
+    stream = torch.cuda.Stream() if graph else torch.cuda.current_stream()
     sp = stream.cuda_stream
     xcode = 0 if w.xdt == "f16" else 1
     args = [(hs[i % R].ptr, xs[i % len(xs)].data_ptr(), ys[i % len(ys)].data_ptr()) for i in range(R * len(xs))]
@@ -125,8 +126,9 @@ def time_calls(w: Workload, steps: int, warmup: int, copies=None, graph=False):
         if st:
             raise wq.GPTQError(st, "gptq_gemm", lib)
 
-    for i in range(warmup):
-        call(i)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if graph:
@@ -134,11 +136,12 @@ def time_calls(w: Workload, steps: int, warmup: int, copies=None, graph=False):
         with torch.cuda.graph(g, stream=stream):
             for i in range(steps):
                 call(i)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
     else:
         e0.record(stream)
         for i in range(steps):

@@ -104,8 +104,8 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) =
 static void free_layer(gptq_layer* L) {
   if (!L) return;
   if (L->wq) (void)hipFree(L->wq);
-  if (L->scales_rt) (void)hipFree(L->scales_rt);
-  if (L->zeros_rt) (void)hipFree(L->zeros_rt);
+  if (L->meta) (void)hipFree(L->meta);
+  if (L->scale32) (void)hipFree(L->scale32);
   if (L->perm) (void)hipFree(L->perm);
   L->magic = 0;
   delete L;
@@ -175,17 +175,17 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
 
   const size_t wq_bytes = (size_t)L->CT * L->KC * unit_words(L->bits) * 4;
   const size_t meta_n = (size_t)L->CT * L->G * kTileN;
-  const size_t sc_bytes = meta_n * (L->scales_dtype == GPTQ_F32 ? 4 : 2);
+  const size_t s32_bytes = L->scales_dtype == GPTQ_F32 ? meta_n * 4 : 0;
   const size_t perm_bytes = sizeof(int32_t) * Kp;
   if (hipMalloc((void**)&L->wq, wq_bytes) != hipSuccess ||
-      hipMalloc(&L->scales_rt, sc_bytes) != hipSuccess ||
-      hipMalloc((void**)&L->zeros_rt, meta_n) != hipSuccess ||
+      hipMalloc((void**)&L->meta, meta_n * 4) != hipSuccess ||
+      (s32_bytes && hipMalloc((void**)&L->scale32, s32_bytes) != hipSuccess) ||
       hipMalloc((void**)&L->perm, perm_bytes) != hipSuccess) {
     (void)hipGetLastError();
     free_layer(L);
     return GPTQ_E_OOM;
   }
-  L->bytes = (int64_t)(wq_bytes + sc_bytes + meta_n + (has_perm ? perm_bytes : 0));
+  L->bytes = (int64_t)(wq_bytes + meta_n * 4 + s32_bytes + (has_perm ? perm_bytes : 0));
   e = hipMemcpyAsync(L->perm, perm_host.data(), perm_bytes, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = launch_repack(L, qweight, qzeros, scales, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -211,7 +211,7 @@ gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int
   if (path == GPTQ_PATH_SKINNY && M > kSkinnyMaxM) return GPTQ_E_INVALID_ARG;
   size_t b = 0;
   if (M > 0) {
-    if (h->has_perm) b += ws_xsorted_bytes(h, M);
+    if (h->has_perm && (path == GPTQ_PATH_TILED || skinny_needs_xsorted(h, M))) b += ws_xsorted_bytes(h, M);
     if (path == GPTQ_PATH_TILED && needs_nsb(h, x_dtype == GPTQ_BF16)) b += ws_nsb_bytes(h, M);
   }
   *bytes = b;
@@ -324,27 +324,18 @@ gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t
       }
   }
   const size_t meta_n = (size_t)h->CT * G * kTileN;
-  if (zeros_gn_host) {
-    std::vector<uint8_t> z(meta_n);
-    e = hipMemcpy(z.data(), h->zeros_rt, meta_n, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e);
-    for (int ct = 0; ct < h->CT; ++ct)
-      for (int g = 0; g < G; ++g)
-        for (int j = 0; j < kTileN; ++j)
-          zeros_gn_host[(size_t)g * N + ct * kTileN + j] = (int32_t)z[((size_t)ct * G + g) * kTileN + j] + 1;
-  }
-  if (scales_gn_host) {
+  if (zeros_gn_host || scales_gn_host) {
     const bool f32 = h->scales_dtype == GPTQ_F32;
-    std::vector<uint8_t> sraw(meta_n * (f32 ? 4 : 2));
-    e = hipMemcpy(sraw.data(), h->scales_rt, sraw.size(), hipMemcpyDeviceToHost);
+    std::vector<uint32_t> meta(meta_n), s32(f32 ? meta_n : 0);
+    e = hipMemcpy(meta.data(), h->meta, meta_n * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && f32) e = hipMemcpy(s32.data(), h->scale32, meta_n * 4, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e);
     for (int ct = 0; ct < h->CT; ++ct)
       for (int g = 0; g < G; ++g)
         for (int j = 0; j < kTileN; ++j) {
-          size_t src = ((size_t)ct * G + g) * kTileN + j;
-          uint32_t v = f32 ? reinterpret_cast<uint32_t*>(sraw.data())[src]
-                           : reinterpret_cast<uint16_t*>(sraw.data())[src];
-          scales_gn_host[(size_t)g * N + ct * kTileN + j] = v;
+          const size_t src = ((size_t)ct * G + g) * kTileN + j, dst = (size_t)g * N + ct * kTileN + j;
+          if (zeros_gn_host) zeros_gn_host[dst] = (int32_t)((meta[src] >> 16) & 0xFFFF) + 1;
+          if (scales_gn_host) scales_gn_host[dst] = f32 ? s32[src] : (meta[src] & 0xFFFF);
         }
   }
   return GPTQ_OK;

@@ -1,0 +1,52 @@
+// Buffer-resource loads (device only).
+//
+// A gfx9-family buffer resource lives in four scalar registers; a load then takes a per-lane
+// 32-bit byte offset (VGPR), a wave-uniform byte offset (SGPR) and an immediate.  Streaming
+// kernels keep each lane's offset fixed and advance only the scalar offset, so address
+// arithmetic costs no vector ALU at all.  Offsets at or past the resource's byte size return
+// zero without touching memory, which masks rows and tails without branches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dequant.h"
+
+namespace gq {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+constexpr int kRsrcWord3 = 0x00020000;   // untyped (raw) buffer descriptor, gfx9 family
+constexpr int kAuxStream = 2;            // nt: data read once, do not keep it in the caches
+constexpr uint32_t kOob = 0x80000000u;   // a lane offset past every resource: loads return 0
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// `words` consecutive 32-bit words at voff + soff of resource r.
+template <int WORDS, int AUX>
+__device__ __forceinline__ void load_words(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* out) {
+  if constexpr (WORDS == 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  } else if constexpr (WORDS == 3) {
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, AUX);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2];
+  } else if constexpr (WORDS == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
+    out[0] = v[0]; out[1] = v[1];
+  } else {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
+  }
+}
+
+__device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+}  // namespace gq

@@ -111,13 +111,15 @@ __device__ __forceinline__ u32x4 build_b(const uint32_t* w, int t, uint32_t zt) 
   return r;
 }
 
-// Scale bits -> float (kind: 0 f16, 1 bf16, 2 f32).
-__device__ __forceinline__ float scale_value(const void* base, int64_t idx, int kind) {
-  if (kind == 2) return reinterpret_cast<const float*>(base)[idx];
-  const uint16_t b = reinterpret_cast<const uint16_t*>(base)[idx];
-  if (kind == 0) return (float)__builtin_bit_cast(_Float16, b);
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
+// Group scale of a metadata record (see layout.h); s32 holds the f32 bits when kind == 2.
+// (Computed branch-free: a branch here would split the straight-line chunk code.)
+__device__ __forceinline__ float scale_of(uint32_t rec, uint32_t s32, int kind) {
+  const float f16v = (float)__builtin_bit_cast(_Float16, (uint16_t)(rec & 0xFFFFu));
+  const float bf16v = __builtin_bit_cast(float, rec << 16);
+  const float f32v = __builtin_bit_cast(float, s32);
+  return kind == 0 ? f16v : (kind == 1 ? bf16v : f32v);
 }
+__device__ __forceinline__ uint32_t stored_zero_of(uint32_t rec) { return rec >> 16; }
 
 template <int XT>
 __device__ __forceinline__ uint16_t to_out(float v) {

@@ -17,8 +17,8 @@ struct gptq_layer {
   int has_perm;       // 1 when the sorted order is not the identity
   int seg_steps;      // MFMA K steps (of 32) per scale-fixup segment: 4 or 1
   uint32_t* wq;       // runtime words, CT * KC * 64 * bits
-  void* scales_rt;    // [CT][G][16] of uint16 (f16/bf16 bits) or uint32 (f32)
-  uint8_t* zeros_rt;  // [CT][G][16] stored zeros
+  uint32_t* meta;     // [CT][G][16]: 16-bit scale bits | stored zero << 16 (see layout.h)
+  uint32_t* scale32;  // [CT][G][16] f32 scale bits when scales_dtype is F32, else NULL
   int32_t* perm;      // [Kp]: original input index at each sorted position (-1 = padding)
   int64_t bytes;
 };
@@ -49,6 +49,10 @@ size_t ws_xsorted_bytes(const gptq_layer* L, int64_t M);
 size_t ws_nsb_bytes(const gptq_layer* L, int64_t M);
 bool needs_nsb(const gptq_layer* L, int x_bf16);   // the tiled family's bias-correction table
 
+// True when the skinny family needs a sorted copy of x in the workspace (act-order with x too
+// large to gather into LDS).
+bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
+
 // Family launchers.  Both assume the call was validated.
 hipError_t launch_skinny(const GemmCall& c);
 hipError_t launch_tiled(const GemmCall& c);
@@ -56,5 +60,16 @@ hipError_t launch_tiled(const GemmCall& c);
 hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_nsb);
 
 constexpr int64_t kSkinnyMaxM = 64;
+
+// Segment -> group map: group = min(segment / div, G - 1), shift = log2(div) when div is a power
+// of two, else -1.  A segment is a 128-input chunk (seg_steps 4) or a 32-input step (seg_steps 1).
+inline void segment_divisor(const gptq_layer* L, int* div, int* shift) {
+  int d = L->group_size == -1 ? (1 << 30) : L->gs_eff / (32 * L->seg_steps);
+  int sh = -1;
+  for (int b = 0; b < 31; ++b)
+    if (d == (1 << b)) sh = b;
+  *div = d;
+  *shift = sh;
+}
 
 }  // namespace gq

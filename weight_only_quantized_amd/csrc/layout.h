@@ -30,8 +30,11 @@
 //          ((w & 0x00FF00FF) holds codes c = 0, 1 in its two 16-bit halves, (w >> 8) & 0x00FF00FF
 //          codes c = 2, 3)
 //
-// Group metadata is re-tiled the same way: scales_rt[(ct * G + g) * 16 + j] (16- or 32-bit raw
-// bits) and zeros_rt[(ct * G + g) * 16 + j] = stored zero (z - 1), uint8.
+// Group metadata is re-tiled the same way, one 32-bit record per (tile, group, column):
+//   meta[(ct * G + g) * 16 + j] = scale bits (fp16/bf16, bits 0-15; 0 for f32 scales)
+//                                 | stored zero (z - 1) << 16
+// plus, for f32 scales only, scale32[(ct * G + g) * 16 + j] = the f32 bits.  One record per lane
+// per segment keeps the kernels' metadata loads unconditional and width-uniform.
 #pragma once
 #include <stdint.h>
 

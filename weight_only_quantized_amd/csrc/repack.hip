@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256) repack_words_kernel(
 // One thread per (tile, group, column-in-tile): scale bits and stored zero.
 __global__ void __launch_bounds__(256) repack_meta_kernel(
     const uint32_t* __restrict__ qzeros, const void* __restrict__ scales, int scale_bytes,
-    void* __restrict__ scales_rt, uint8_t* __restrict__ zeros_rt, int N, int G, int bits, int64_t total) {
+    uint32_t* __restrict__ meta, uint32_t* __restrict__ scale32, int N, int G, int bits, int64_t total) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int j = (int)(gid & 15);
@@ -87,11 +87,13 @@ __global__ void __launch_bounds__(256) repack_meta_kernel(
   const int64_t ct = cg / G;
   const int64_t n = ct * kTileN + j;
   const int64_t zld = (int64_t)N / 32 * bits;
-  zeros_rt[gid] = (uint8_t)packed_field_cols(qzeros, zld, bits, g, n);
-  if (scale_bytes == 4)
-    reinterpret_cast<uint32_t*>(scales_rt)[gid] = reinterpret_cast<const uint32_t*>(scales)[(int64_t)g * N + n];
-  else
-    reinterpret_cast<uint16_t*>(scales_rt)[gid] = reinterpret_cast<const uint16_t*>(scales)[(int64_t)g * N + n];
+  const uint32_t z = packed_field_cols(qzeros, zld, bits, g, n);
+  if (scale_bytes == 4) {
+    meta[gid] = z << 16;
+    scale32[gid] = reinterpret_cast<const uint32_t*>(scales)[(int64_t)g * N + n];
+  } else {
+    meta[gid] = (uint32_t)reinterpret_cast<const uint16_t*>(scales)[(int64_t)g * N + n] | (z << 16);
+  }
 }
 
 hipError_t launch_repack(const gptq_layer* L, const int32_t* qweight, const int32_t* qzeros,
@@ -106,7 +108,7 @@ hipError_t launch_repack(const gptq_layer* L, const int32_t* qweight, const int3
   const int64_t total = (int64_t)L->CT * L->G * kTileN;
   hipLaunchKernelGGL(repack_meta_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(qzeros), scales, L->scales_dtype == GPTQ_F32 ? 4 : 2,
-                     L->scales_rt, L->zeros_rt, L->N, L->G, L->bits, total);
+                     L->meta, L->scale32, L->N, L->G, L->bits, total);
   return hipGetLastError();
 }
 

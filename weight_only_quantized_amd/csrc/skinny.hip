@@ -17,6 +17,7 @@
 //     accumulator.
 #include <hip/hip_runtime.h>
 
+#include "bufmem.h"
 #include "dequant.h"
 #include "internal.h"
 
@@ -24,103 +25,134 @@ namespace gq {
 
 struct SkinnyArgs {
   const uint32_t* wq;
-  const void* scales;
-  const uint8_t* zeros;
-  const uint16_t* x;      // [M, ld] activations in sorted input order
+  const uint32_t* meta;   // per (tile, group, column): scale bits | stored zero << 16
+  const uint32_t* scale32;  // f32 scale bits (scale_kind == 2 only)
+  const uint16_t* x;      // [M, ld] activations (original order when perm is set, else sorted)
+  const int32_t* perm;    // sorted position -> input index, or NULL (identity); LDS staging only
   uint16_t* y;            // [M, N]
   int64_t ld;             // row stride of x in elements
-  int M, K, N, KC, CT, G, gs_eff, scale_kind;
+  int M, K, Kp, N, KC, CT, G, scale_kind;
+  int gdiv, gshift;       // group of a segment = min(seg_index / gdiv, G - 1); gshift >= 0 when gdiv = 1 << gshift
 };
 
-template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG>
+// Group of segment `si` (a chunk index when segments are chunks, a 32-input step index when they
+// are steps).  Every operand is wave-uniform, so this runs on the scalar unit.
+__device__ __forceinline__ int segment_group(int si, int gdiv, int gshift, int G) {
+  const int g = gshift >= 0 ? (si >> gshift) : si / gdiv;
+  return g < G - 1 ? g : G - 1;
+}
+
+// XLDS = 1: the workgroup first copies x[0:M, sorted 0:Kp] (gathering through perm when set) into
+// LDS, rows padded by 16 bytes; A operands then come from LDS.  XLDS = 0: each chunk's A
+// operands are loaded from global memory (L2-resident) one chunk ahead.
+// DEPTH chunks of packed weights (and their group metadata) are kept in flight per wave in a
+// register ring, so a wave never waits on HBM latency more than once per DEPTH chunks.
+// All loads go through buffer resources (bufmem.h): a lane's offset is fixed, the chunk offset is
+// a scalar, and the loaded values are only touched at compute time -- an operation on a loaded
+// value right after its load (or at a branch join) would force a wait for every load in flight.
+// TCH > 0: every wave owns exactly TCH chunks (the dispatcher guarantees KC == KSPLIT * TCH) and
+// its whole K range is emitted as straight-line code, so each chunk waits only for its own loads
+// (a loop back-edge would make the compiler wait for every load in flight).
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH>
 __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
   constexpr int CGS = 4 / KSPLIT;               // column groups per workgroup
   constexpr int NSEG = 4 / SEG;                 // fixup segments per chunk
-  constexpr int PARTS = BITS == 8 ? 2 : 1;      // 16-byte (or smaller) loads per lane per unit
-  constexpr int PW = BITS == 8 ? 4 : BITS;      // words per part
+  constexpr int PARTS = BITS == 8 ? 2 : 1;      // loads per lane per unit
+  constexpr int PW = BITS == 8 ? 4 : BITS;      // words per load
+  constexpr uint32_t UNIT_BYTES = 256u * BITS;
   __shared__ float red[4][MT * TW * 4][64];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xlds[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Chunk and tile bookkeeping is wave-uniform (scalar registers).
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cg = wave / KSPLIT, ks = wave % KSPLIT;
   const int ct0 = (blockIdx.x * CGS + cg) * TW;
   const int cpw = (a.KC + KSPLIT - 1) / KSPLIT;
   const int kc0 = ks * cpw;
   const int kc1 = min(a.KC, kc0 + cpw);
   const int col = lane & 15, q = lane >> 4;
-
-  bool tvalid[TW];
-#pragma unroll
-  for (int i = 0; i < TW; ++i) tvalid[i] = ct0 + i < a.CT;
+  const int xrow = a.Kp + 8;                    // LDS row stride (halves)
 
   f32x4 acc[MT][TW];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int i = 0; i < TW; ++i) acc[m][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t unit_w = (int64_t)64 * BITS;
   u32x4 nb;
   nb[0] = nb[1] = nb[2] = nb[3] = Bias<BITS, XT>::neg2;
 
-  // ---- one chunk's loads -------------------------------------------------------------------
-  struct Chunk {
+  // One resource per tile (units, metadata records, f32 scales); tiles past the end of N alias
+  // the last tile -- they are computed but never stored.
+  rsrc_t rw[TW], rm[TW], rs[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    const int64_t cti = min(ct0 + i, a.CT - 1);
+    rw[i] = make_rsrc(a.wq + cti * a.KC * (64 * BITS), (uint32_t)a.KC * UNIT_BYTES);
+    rm[i] = make_rsrc(a.meta + cti * a.G * 16, (uint32_t)a.G * 64u);
+    rs[i] = make_rsrc(a.scale32 ? a.scale32 + cti * a.G * 16 : a.meta, a.scale32 ? (uint32_t)a.G * 64u : 0u);
+  }
+  const uint32_t voff_w = (uint32_t)lane * PW * 4u;
+  const uint32_t voff_m = (uint32_t)col * 4u;
+
+  struct WChunk {
     uint32_t w[TW][BITS];
-    u32x4 xa[MT][4];
-    uint32_t zs[TW][NSEG];
-    float sc[TW][NSEG];
+    uint32_t rec[TW][NSEG];      // metadata record
+    uint32_t s32[TW][NSEG];      // f32 scale bits
   };
-  auto load = [&](int kc, Chunk& c) {
+  auto load_w = [&](int kc, WChunk& c) {
 #pragma unroll
-    for (int i = 0; i < TW; ++i) {
-      if (tvalid[i]) {
-        const uint32_t* u = a.wq + ((int64_t)(ct0 + i) * a.KC + kc) * unit_w;
+    for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int p = 0; p < PARTS; ++p) {
-          const uint32_t* src = u + p * 64 * PW + lane * PW;
-          if constexpr (PW == 4) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-            c.w[i][4 * p + 0] = v[0]; c.w[i][4 * p + 1] = v[1]; c.w[i][4 * p + 2] = v[2]; c.w[i][4 * p + 3] = v[3];
-          } else {
-#pragma unroll
-            for (int j = 0; j < PW; ++j) c.w[i][j] = src[j];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < BITS; ++j) c.w[i][j] = 0u;
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int row = m * 16 + col;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int k = kc * kChunkK + 32 * t + 8 * q;
-        if (row < a.M && k < a.K)
-          c.xa[m][t] = *reinterpret_cast<const u32x4*>(a.x + (int64_t)row * a.ld + k);
-        else
-          c.xa[m][t] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+      for (int p = 0; p < PARTS; ++p)
+        load_words<PW, kAuxStream>(rw[i], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &c.w[i][4 * p]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      const int g = min((kc * kChunkK + s * 32 * SEG) / a.gs_eff, a.G - 1);
+      const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gdiv, a.gshift, a.G);
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
-        if (tvalid[i]) {
-          const int64_t mi = ((int64_t)(ct0 + i) * a.G + g) * 16 + col;
-          c.zs[i][s] = zero_term<BITS, XT>(a.zeros[mi]);
-          c.sc[i][s] = scale_value(a.scales, mi, a.scale_kind);
-        } else {
-          c.zs[i][s] = 0u;
-          c.sc[i][s] = 0.f;
-        }
+        c.rec[i][s] = load_b32(rm[i], voff_m, (uint32_t)g * 64u);
+        c.s32[i][s] = load_b32(rs[i], voff_m, (uint32_t)g * 64u);   // zero-size resource unless f32
       }
     }
   };
 
-  // ---- one chunk's arithmetic --------------------------------------------------------------
-  auto compute = [&](const Chunk& c) {
+  struct XChunk { u32x4 xa[MT][4]; };
+  // global A operands: lane (row m*16 + col, k = 128 kc + 32 t + 8 q); rows >= M read 0
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.ld * 2));
+  uint32_t voff_x[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = m * 16 + col;
+    voff_x[m] = row < a.M ? (uint32_t)(row * a.ld + 8 * q) * 2u : kOob;
+  }
+  auto load_x_global = [&](int kc, XChunk& c) {
+    const bool tail = (kc + 1) * kChunkK > a.K;   // last chunk of a K that is not a multiple of 128
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t vo = voff_x[m] + 64u * t;
+        if (tail && kc * kChunkK + 32 * t + 8 * q >= a.K) vo = kOob;
+        c.xa[m][t] = load_b128(rx, vo, (uint32_t)kc * 256u);
+      }
+  };
+  // rows >= M read a 16-byte zero slot placed after the staged rows (a broadcast read)
+  const int zero_slot = a.M * xrow;
+  int xbase[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xbase[m] = (m * 16 + col < a.M) ? (m * 16 + col) * xrow + 8 * q : -1;
+  auto load_x_lds = [&](int kc, XChunk& c) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int off = xbase[m] >= 0 ? xbase[m] + kc * kChunkK + 32 * t : zero_slot;
+        c.xa[m][t] = *reinterpret_cast<const u32x4*>(&xlds[off]);
+      }
+  };
+
+  auto compute = [&](const WChunk& c, const XChunk& xc) {
     f32x4 c0[MT][NSEG];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -129,7 +161,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
         f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (Bias<BITS, XT>::any) {
 #pragma unroll
-          for (int t = s * SEG; t < (s + 1) * SEG; ++t) v = mfma16<XT>(c.xa[m][t], nb, v);
+          for (int t = s * SEG; t < (s + 1) * SEG; ++t) v = mfma16<XT>(xc.xa[m][t], nb, v);
         }
         c0[m][s] = v;
       }
@@ -137,26 +169,105 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
     for (int i = 0; i < TW; ++i) {
       u32x4 b[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[t] = build_b<BITS, XT>(c.w[i], t, c.zs[i][t / SEG]);
+      for (int t = 0; t < 4; ++t) b[t] = build_b<BITS, XT>(c.w[i], t, zero_term<BITS, XT>(stored_zero_of(c.rec[i][t / SEG])));
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int s = 0; s < NSEG; ++s) {
           f32x4 tmp = c0[m][s];
 #pragma unroll
-          for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(c.xa[m][t], b[t], tmp);
-          acc[m][i] += c.sc[i][s] * tmp;
+          for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(xc.xa[m][t], b[t], tmp);
+          acc[m][i] += scale_of(c.rec[i][s], c.s32[i][s], a.scale_kind) * tmp;
         }
     }
   };
 
-  if (kc0 < kc1) {
-    Chunk cur, nxt;
-    load(kc0, cur);
-    for (int kc = kc0; kc < kc1; ++kc) {
-      if (kc + 1 < kc1) load(kc + 1, nxt);
-      compute(cur);
-      cur = nxt;
+  // ---- prologue ----------------------------------------------------------------------------
+  // Loads complete in issue order, so x staging loads (needed first) go out before the weight
+  // ring; an act-order gather needs its permutation first and goes after the ring.
+  constexpr int XPT = 4;                          // 16-byte x pieces per thread held in registers
+  u32x4 xreg[XPT];
+  const int per_row = a.Kp / 8;
+  const int n8 = XLDS ? a.M * per_row : 0;        // 16-byte pieces of sorted x
+  if constexpr (XLDS) {
+    if (!a.perm) {
+#pragma unroll
+      for (int r = 0; r < XPT; ++r) {
+        const int idx = threadIdx.x + 256 * r;
+        const int m = idx / per_row, j0 = (idx % per_row) * 8;
+        xreg[r] = load_b128(rx, (idx < n8 && j0 < a.K) ? (uint32_t)(m * a.ld + j0) * 2u : kOob, 0u);
+      }
+    }
+  }
+  WChunk ring[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j)
+    if (TCH > 0 || kc0 + j < kc1) load_w(kc0 + j, ring[j]);
+
+  if constexpr (XLDS) {
+    if (a.perm) {
+#pragma unroll
+      for (int r = 0; r < XPT; ++r) {
+        const int idx = threadIdx.x + 256 * r;
+        xreg[r] = u32x4{0u, 0u, 0u, 0u};
+        if (idx < n8) {
+          const int m = idx / per_row, j0 = (idx % per_row) * 8;
+          uint16_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = j0 + e;
+            h[e] = j < a.K ? a.x[(int64_t)m * a.ld + a.perm[j]] : (uint16_t)0;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xreg[r][e] = (uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < XPT; ++r) {
+      const int idx = threadIdx.x + 256 * r;
+      if (idx < n8) {
+        const int m = idx / per_row, j0 = (idx % per_row) * 8;
+        *reinterpret_cast<u32x4*>(&xlds[m * xrow + j0]) = xreg[r];
+      }
+    }
+    if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(&xlds[zero_slot]) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+
+  // ---- main loop: compute chunk kc from the ring slot, then refill the slot with kc + DEPTH ---
+  XChunk xcur, xnxt;
+  if constexpr (!XLDS) {
+    if (kc0 < kc1) load_x_global(kc0, xcur);
+  }
+  if constexpr (TCH > 0) {
+#pragma unroll
+    for (int j = 0; j < TCH; ++j) {
+      const int kc = kc0 + j;
+      if constexpr (XLDS) {
+        load_x_lds(kc, xcur);
+      } else {
+        if (j + 1 < TCH) load_x_global(kc + 1, xnxt);
+      }
+      compute(ring[j % DEPTH], xcur);
+      if (j + DEPTH < TCH) load_w(kc + DEPTH, ring[j % DEPTH]);
+      if constexpr (!XLDS) xcur = xnxt;
+    }
+  } else
+  for (int base = kc0; base < kc1; base += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      const int kc = base + j;
+      if (kc < kc1) {
+        if constexpr (XLDS) {
+          load_x_lds(kc, xcur);
+        } else {
+          if (kc + 1 < kc1) load_x_global(kc + 1, xnxt);
+        }
+        compute(ring[j], xcur);
+        if (kc + DEPTH < kc1) load_w(kc + DEPTH, ring[j]);
+        if constexpr (!XLDS) xcur = xnxt;
+      }
     }
   }
 
@@ -181,7 +292,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
-    if (!tvalid[i]) continue;
+    if (ct0 + i >= a.CT) continue;
     const int n = (ct0 + i) * 16 + col;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -194,26 +305,45 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Dispatch: tiles per wave grow with M so that x traffic (from L2) stays near the weight traffic.
+// Dispatch
 // ------------------------------------------------------------------------------------------------
-template <int BITS, int XT, int MT, int TW, int KSPLIT>
-static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
+constexpr int kXLdsMax = 64 * 1024;   // dynamic LDS budget for staged x
+
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH>
+static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   constexpr int CGS = 4 / KSPLIT;
   const int blocks = (a.CT + TW * CGS - 1) / (TW * CGS);
+  const size_t lds = XLDS ? (size_t)a.M * (a.Kp + 8) * 2 + 16 : 0;
   if (seg == 4)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH>), dim3(blocks), dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, TCH>), dim3(blocks), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
+// Straight-line variants when each of the KSPLIT waves gets exactly 8 or 16 chunks.
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH>
+static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
+  // ring depths measured best on MI355X for 4-bit M=1 (2 for 8 chunks per wave, 4 for 16)
+  if (a.KC == 8 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 8>(a, seg, s);
+  if (a.KC == 16 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 16>(a, seg, s);
+  return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 0>(a, seg, s);
+}
+
+// True when x for this call can be staged in LDS (small M): the call then needs no workspace.
+// The staging holds at most 4 pieces of 8 inputs per thread (M * Kp <= 8192).
+static bool x_fits_lds(int64_t M, int Kp) {
+  return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && M * (int64_t)(Kp + 8) * 2 + 16 <= kXLdsMax;
+}
+
+// Tiles per wave grow with M so that x traffic (from L2) stays near the weight traffic.
 template <int BITS, int XT>
 static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
-  if (a.M <= 4) return run<BITS, XT, 1, 1, 4>(a, seg, s);
-  if (a.M <= 8) return run<BITS, XT, 1, 2, 4>(a, seg, s);
-  if (a.M <= 16) return run<BITS, XT, 1, 2, 4>(a, seg, s);
-  if (a.M <= 32) return run<BITS, XT, 2, 2, 4>(a, seg, s);
-  return run<BITS, XT, 4, 2, 4>(a, seg, s);
+  if (x_fits_lds(a.M, a.Kp)) return run<BITS, XT, 1, 1, 4, 1, 4>(a, seg, s);
+  if (a.M <= 8) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
+  if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
+  if (a.M <= 32) return run<BITS, XT, 2, 2, 4, 0, 2>(a, seg, s);
+  return run<BITS, XT, 4, 2, 4, 0, 2>(a, seg, s);
 }
 
 template <int XT>
@@ -226,17 +356,20 @@ static hipError_t run_bits(const SkinnyArgs& a, int bits, int seg, hipStream_t s
   }
 }
 
+bool skinny_needs_xsorted(const gptq_layer* L, int64_t M) { return L->has_perm && !x_fits_lds(M, L->Kp); }
+
 hipError_t launch_skinny(const GemmCall& c) {
   const gptq_layer* L = c.L;
   SkinnyArgs a;
   a.wq = L->wq;
-  a.scales = L->scales_rt;
-  a.zeros = L->zeros_rt;
+  a.meta = L->meta;
+  a.scale32 = L->scale32;
   a.y = reinterpret_cast<uint16_t*>(c.y);
-  a.M = (int)c.M; a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
-  a.gs_eff = L->gs_eff;
+  a.M = (int)c.M; a.K = L->K; a.Kp = L->Kp; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
+  segment_divisor(L, &a.gdiv, &a.gshift);
   a.scale_kind = L->scales_dtype;
-  if (L->has_perm) {
+  a.perm = nullptr;
+  if (skinny_needs_xsorted(L, c.M)) {
     hipError_t e = launch_prep(c, true, false);
     if (e != hipSuccess) return e;
     a.x = reinterpret_cast<const uint16_t*>(c.ws);
@@ -244,6 +377,7 @@ hipError_t launch_skinny(const GemmCall& c) {
   } else {
     a.x = reinterpret_cast<const uint16_t*>(c.x);
     a.ld = L->K;
+    if (L->has_perm) a.perm = L->perm;     // gathered while staging x in LDS
   }
   return c.x_bf16 ? run_bits<1>(a, L->bits, L->seg_steps, c.stream)
                   : run_bits<0>(a, L->bits, L->seg_steps, c.stream);

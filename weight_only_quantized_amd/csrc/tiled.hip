@@ -99,8 +99,8 @@ hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_nsb) {
 // ---------------------------------------------------------------------------------------------
 struct TiledArgs {
   const uint32_t* wq;
-  const void* scales;
-  const uint8_t* zeros;
+  const uint32_t* meta;     // per (tile, group, column): scale bits | stored zero << 16
+  const uint32_t* scale32;  // f32 scale bits (scale_kind == 2 only)
   const uint16_t* x;     // [M, ld] sorted-order activations
   const float* nsb;      // [M, Kp / segk]
   uint16_t* y;
@@ -149,8 +149,8 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
     u32x4 xa[A_LOADS];
     float nsb[2];
     uint32_t w[WN][BITS];
-    uint32_t zs[WN][NSEG];
-    float sc[WN][NSEG];
+    uint32_t rec[WN][NSEG];     // metadata records (raw: converted at use)
+    uint32_t s32[WN][NSEG];
   };
 
   auto gload = [&](int kc, Stage& st) {
@@ -177,31 +177,25 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      if (tvalid[j]) {
-        const uint32_t* u = a.wq + ((int64_t)(ct0 + j) * a.KC + kc) * unit_w;
+      const int ctj = min(ct0 + j, a.CT - 1);     // past-the-end tiles read the last tile, unused
+      const uint32_t* u = a.wq + ((int64_t)ctj * a.KC + kc) * unit_w;
 #pragma unroll
-        for (int p = 0; p < PARTS; ++p) {
-          const uint32_t* src = u + p * 64 * PW + lane * PW;
-          if constexpr (PW == 4) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-            st.w[j][4 * p + 0] = v[0]; st.w[j][4 * p + 1] = v[1]; st.w[j][4 * p + 2] = v[2]; st.w[j][4 * p + 3] = v[3];
-          } else {
+      for (int p = 0; p < PARTS; ++p) {
+        const uint32_t* src = u + p * 64 * PW + lane * PW;
+        if constexpr (PW == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+          st.w[j][4 * p + 0] = v[0]; st.w[j][4 * p + 1] = v[1]; st.w[j][4 * p + 2] = v[2]; st.w[j][4 * p + 3] = v[3];
+        } else {
 #pragma unroll
-            for (int e = 0; e < PW; ++e) st.w[j][e] = src[e];
-          }
+          for (int e = 0; e < PW; ++e) st.w[j][e] = src[e];
         }
+      }
 #pragma unroll
-        for (int s = 0; s < NSEG; ++s) {
-          const int g = min((kc * kChunkK + s * 32 * SEG) / a.gs_eff, a.G - 1);
-          const int64_t mi = ((int64_t)(ct0 + j) * a.G + g) * 16 + col;
-          st.zs[j][s] = zero_term<BITS, XT>(a.zeros[mi]);
-          st.sc[j][s] = scale_value(a.scales, mi, a.scale_kind);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < BITS; ++e) st.w[j][e] = 0u;
-#pragma unroll
-        for (int s = 0; s < NSEG; ++s) { st.zs[j][s] = 0u; st.sc[j][s] = 0.f; }
+      for (int s = 0; s < NSEG; ++s) {
+        const int g = min((kc * kChunkK + s * 32 * SEG) / a.gs_eff, a.G - 1);
+        const int64_t mi = ((int64_t)ctj * a.G + g) * 16 + col;
+        st.rec[j][s] = a.meta[mi];
+        if (a.scale_kind == 2) st.s32[j][s] = a.scale32[mi];
       }
     }
   };
@@ -225,7 +219,8 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
 #pragma unroll
     for (int j = 0; j < WN; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[j][t] = build_b<BITS, XT>(st.w[j], t, st.zs[j][t / SEG]);
+      for (int t = 0; t < 4; ++t)
+        b[j][t] = build_b<BITS, XT>(st.w[j], t, zero_term<BITS, XT>(stored_zero_of(st.rec[j][t / SEG])));
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       u32x4 af[4];
@@ -244,7 +239,7 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
           f32x4 tmp = c0[s];
 #pragma unroll
           for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(af[t], b[j][t], tmp);
-          acc[i][j] += st.sc[j][s] * tmp;
+          acc[i][j] += scale_of(st.rec[j][s], st.s32[j][s], a.scale_kind) * tmp;
         }
     }
   };
@@ -319,8 +314,8 @@ hipError_t launch_tiled(const GemmCall& c) {
   }
   a.nsb = nsb ? reinterpret_cast<const float*>(base) : nullptr;
   a.wq = L->wq;
-  a.scales = L->scales_rt;
-  a.zeros = L->zeros_rt;
+  a.meta = L->meta;
+  a.scale32 = L->scale32;
   a.y = reinterpret_cast<uint16_t*>(c.y);
   a.M = (int)c.M; a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
   a.gs_eff = L->gs_eff;
