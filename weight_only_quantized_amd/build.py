@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
-SOURCES = ["api.cpp", "repack.hip", "skinny.hip", "tiled.hip"]
+SOURCES = ["api.cpp", "repack.hip", "skinny.hip", "skinny_b2.hip", "skinny_b3.hip", "skinny_b4.hip",
+           "skinny_b8.hip", "tiled.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -23,22 +24,40 @@ def hipcc_flags():
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into LIB (always rebuilds).  Returns the library path."""
-    tmp = LIB + ".tmp"
-    srcs = []
-    for s in SOURCES:
-        p = os.path.join(CSRC, s)
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source (in parallel, one hipcc per file) and link LIB.  Always rebuilds.
+    Returns the library path."""
+    import concurrent.futures
+    import tempfile
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    objdir = tempfile.mkdtemp(prefix="gq_build_")
+    flags = [f for f in hipcc_flags() if f != "-shared"]
+
+    def compile_one(s):
+        src = os.path.join(CSRC, s)
+        obj = os.path.join(objdir, s + ".o")
         # api.cpp holds host code only but calls the HIP runtime: compile it as HIP too
-        srcs += (["-x", "hip", p] if s.endswith(".hip") or s.endswith(".cpp") else [p])
-    cmd = [HIPCC] + hipcc_flags() + srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+        cmd = [HIPCC] + flags + ["-x", "hip", "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {s} ({r.returncode})")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed ({r.returncode})")
+        raise RuntimeError(f"link failed ({r.returncode})")
     os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
+    os.rmdir(objdir)
     return LIB
 
 

@@ -107,6 +107,7 @@ static void free_layer(gptq_layer* L) {
   if (L->meta) (void)hipFree(L->meta);
   if (L->scale32) (void)hipFree(L->scale32);
   if (L->perm) (void)hipFree(L->perm);
+  if (L->iperm) (void)hipFree(L->iperm);
   L->magic = 0;
   delete L;
 }
@@ -193,9 +194,23 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
     free_layer(L);
     return hip_fail(e);
   }
-  if (!has_perm) {  // identity order: the kernels do not need the table
+  if (!has_perm) {  // identity order: the kernels do not need the tables
     (void)hipFree(L->perm);
     L->perm = nullptr;
+  } else {
+    std::vector<int32_t> ip(K);
+    for (int j = 0; j < K; ++j) ip[perm_host[j]] = j;
+    if (hipMalloc((void**)&L->iperm, sizeof(int32_t) * K) != hipSuccess) {
+      (void)hipGetLastError();
+      free_layer(L);
+      return GPTQ_E_OOM;
+    }
+    e = hipMemcpy(L->iperm, ip.data(), sizeof(int32_t) * K, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      free_layer(L);
+      return hip_fail(e);
+    }
+    L->bytes += (int64_t)sizeof(int32_t) * K;
   }
   *out = L;
   return GPTQ_OK;

@@ -1,0 +1,359 @@
+// Skinny family (M <= 64): a memory-bound streaming kernel.
+//
+// "Formats and kernels: FP8, INT8, INT4, Marlin, Machete" (its roofline opening and the tiny-M
+// tile discussion) explains why small M is bound by the packed weight stream: every byte of the
+// weights must be read once, with every compute unit pulling, and the arithmetic hides in the
+// slack.  Design on gfx950:
+//   * one wave owns TW column tiles (16 columns each) and a slice of the sorted K chunks; the
+//     KSPLIT waves of a workgroup that share column tiles split K between them and meet in LDS at
+//     the end (deterministic, no atomics, no workspace);
+//   * per 128-input chunk a lane issues one 16-byte load per tile (4-bit) of packed runtime words
+//     (layout.h), plus one 16-byte load per 16-row block of x for its MFMA A operand; the next
+//     chunk's loads are in flight while the current chunk is dequantised and multiplied;
+//   * the dequantised operand never leaves registers (dequant.h): B = code - zero exactly for
+//     fp16; for bf16 B = 144 + (code - zero) exactly and one extra MFMA per step against a
+//     constant -144 operand yields the correction -144 * sum_k x as the starting accumulator of
+//     each segment; after a segment the group scale multiplies the fp32 partial into the output
+//     accumulator.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "bufmem.h"
+#include "dequant.h"
+#include "internal.h"
+
+namespace gq {
+
+struct SkinnyArgs {
+  const uint32_t* wq;
+  const uint32_t* meta;   // per (tile, group, column): scale bits | stored zero << 16
+  const uint32_t* scale32;  // f32 scale bits (scale_kind == 2 only)
+  const uint16_t* x;      // [M, ld] activations (original order when perm is set, else sorted)
+  const int32_t* iperm;   // input index -> sorted position, or NULL (identity); LDS staging only
+  uint16_t* y;            // [M, N]
+  int64_t ld;             // row stride of x in elements
+  int M, K, Kp, N, KC, CT, G, scale_kind;
+  int gdiv, gshift;       // group of a segment = min(seg_index / gdiv, G - 1); gshift >= 0 when gdiv = 1 << gshift
+};
+
+// Group of segment `si` (a chunk index when segments are chunks, a 32-input step index when they
+// are steps).  Every operand is wave-uniform, so this runs on the scalar unit.
+__device__ __forceinline__ int segment_group(int si, int gdiv, int gshift, int G) {
+  const int g = gshift >= 0 ? (si >> gshift) : si / gdiv;
+  return g < G - 1 ? g : G - 1;
+}
+
+// XLDS = 1: the workgroup first copies x[0:M, sorted 0:Kp] (gathering through perm when set) into
+// LDS, rows padded by 16 bytes; A operands then come from LDS.  XLDS = 0: each chunk's A
+// operands are loaded from global memory (L2-resident) one chunk ahead.
+// DEPTH chunks of packed weights (and their group metadata) are kept in flight per wave in a
+// register ring, so a wave never waits on HBM latency more than once per DEPTH chunks.
+// All loads go through buffer resources (bufmem.h): a lane's offset is fixed, the chunk offset is
+// a scalar, and the loaded values are only touched at compute time -- an operation on a loaded
+// value right after its load (or at a branch join) would force a wait for every load in flight.
+// TCH > 0: every wave owns exactly TCH chunks (the dispatcher guarantees KC == KSPLIT * TCH) and
+// its whole K range is emitted as straight-line code, so each chunk waits only for its own loads
+// (a loop back-edge would make the compiler wait for every load in flight).
+// XLDS == 2: as XLDS == 1 for an act-order layer (x is scattered into sorted order).
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH>
+__global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
+  constexpr int CGS = 4 / KSPLIT;               // column groups per workgroup
+  constexpr int NSEG = 4 / SEG;                 // fixup segments per chunk
+  constexpr int PARTS = BITS == 8 ? 2 : 1;      // loads per lane per unit
+  constexpr int PW = BITS == 8 ? 4 : BITS;      // words per load
+  constexpr uint32_t UNIT_BYTES = 256u * BITS;
+  __shared__ float red[4][MT * TW * 4][64];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xlds[];
+
+  // Chunk and tile bookkeeping is wave-uniform (scalar registers).
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cg = wave / KSPLIT, ks = wave % KSPLIT;
+  const int ct0 = (blockIdx.x * CGS + cg) * TW;
+  const int cpw = (a.KC + KSPLIT - 1) / KSPLIT;
+  const int kc0 = ks * cpw;
+  const int kc1 = min(a.KC, kc0 + cpw);
+  const int col = lane & 15, q = lane >> 4;
+  const int xrow = a.Kp + 8;                    // LDS row stride (halves)
+
+  f32x4 acc[MT][TW];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < TW; ++i) acc[m][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 nb;
+  nb[0] = nb[1] = nb[2] = nb[3] = Bias<BITS, XT>::neg2;
+
+  // One resource per tile (units, metadata records, f32 scales); tiles past the end of N alias
+  // the last tile -- they are computed but never stored.
+  rsrc_t rw[TW], rm[TW], rs[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    const int64_t cti = min(ct0 + i, a.CT - 1);
+    rw[i] = make_rsrc(a.wq + cti * a.KC * (64 * BITS), (uint32_t)a.KC * UNIT_BYTES);
+    rm[i] = make_rsrc(a.meta + cti * a.G * 16, (uint32_t)a.G * 64u);
+    rs[i] = make_rsrc(a.scale32 ? a.scale32 + cti * a.G * 16 : a.meta, a.scale32 ? (uint32_t)a.G * 64u : 0u);
+  }
+  const uint32_t voff_w = (uint32_t)lane * PW * 4u;
+  const uint32_t voff_m = (uint32_t)col * 4u;
+
+  struct WChunk {
+    uint32_t w[TW][BITS];
+    uint32_t rec[TW][NSEG];      // metadata record
+    uint32_t s32[TW][NSEG];      // f32 scale bits
+  };
+  auto load_w = [&](int kc, WChunk& c) {
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p)
+        load_words<PW, kAuxStream>(rw[i], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &c.w[i][4 * p]);
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gdiv, a.gshift, a.G);
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        c.rec[i][s] = load_b32(rm[i], voff_m, (uint32_t)g * 64u);
+        c.s32[i][s] = load_b32(rs[i], voff_m, (uint32_t)g * 64u);   // zero-size resource unless f32
+      }
+    }
+  };
+
+  struct XChunk { u32x4 xa[MT][4]; };
+  // global A operands: lane (row m*16 + col, k = 128 kc + 32 t + 8 q); rows >= M read 0
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.ld * 2));
+  uint32_t voff_x[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = m * 16 + col;
+    voff_x[m] = row < a.M ? (uint32_t)(row * a.ld + 8 * q) * 2u : kOob;
+  }
+  auto load_x_global = [&](int kc, XChunk& c) {
+    const bool tail = (kc + 1) * kChunkK > a.K;   // last chunk of a K that is not a multiple of 128
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t vo = voff_x[m] + 64u * t;
+        if (tail && kc * kChunkK + 32 * t + 8 * q >= a.K) vo = kOob;
+        c.xa[m][t] = load_b128(rx, vo, (uint32_t)kc * 256u);
+      }
+  };
+  // rows >= M read a 16-byte zero slot placed after the staged rows (a broadcast read)
+  const int zero_slot = a.M * xrow;
+  int xbase[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xbase[m] = (m * 16 + col < a.M) ? (m * 16 + col) * xrow + 8 * q : -1;
+  auto load_x_lds = [&](int kc, XChunk& c) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int off = xbase[m] >= 0 ? xbase[m] + kc * kChunkK + 32 * t : zero_slot;
+        c.xa[m][t] = *reinterpret_cast<const u32x4*>(&xlds[off]);
+      }
+  };
+
+  auto compute = [&](const WChunk& c, const XChunk& xc) {
+    f32x4 c0[MT][NSEG];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) {
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (Bias<BITS, XT>::any) {
+#pragma unroll
+          for (int t = s * SEG; t < (s + 1) * SEG; ++t) v = mfma16<XT>(xc.xa[m][t], nb, v);
+        }
+        c0[m][s] = v;
+      }
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      u32x4 b[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b[t] = build_b<BITS, XT>(c.w[i], t, zero_term<BITS, XT>(stored_zero_of(c.rec[i][t / SEG])));
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int s = 0; s < NSEG; ++s) {
+          f32x4 tmp = c0[m][s];
+#pragma unroll
+          for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(xc.xa[m][t], b[t], tmp);
+          acc[m][i] += scale_of(c.rec[i][s], c.s32[i][s], a.scale_kind) * tmp;
+        }
+    }
+  };
+
+  // ---- prologue ----------------------------------------------------------------------------
+  // x staging loads go out before the weight ring (loads complete in issue order).  Act-order
+  // layers scatter x into sorted order in LDS through the inverse permutation: both global reads
+  // stay coalesced and independent, and the scatter is eight 2-byte LDS writes per piece.
+  constexpr int XPT = 4;                          // 16-byte x pieces per thread held in registers
+  constexpr bool PERMUTE = XLDS == 2;
+  u32x4 xreg[XPT];
+  u32x4 ipreg[PERMUTE ? XPT : 1][2];
+  const int per_row = a.Kp / 8;
+  const int n8 = XLDS ? a.M * per_row : 0;        // 16-byte pieces of x (original order if iperm)
+  if constexpr (XLDS) {
+#pragma unroll
+    for (int r = 0; r < XPT; ++r) {
+      const int idx = threadIdx.x + 256 * r;
+      const int m = idx / per_row, j0 = (idx % per_row) * 8;
+      const bool real = idx < n8 && j0 < a.K;
+      xreg[r] = load_b128(rx, real ? (uint32_t)(m * a.ld + j0) * 2u : kOob, 0u);
+      if constexpr (PERMUTE) {
+        const rsrc_t rip = make_rsrc(a.iperm, (uint32_t)a.K * 4u);
+        ipreg[r][0] = load_b128(rip, real ? (uint32_t)j0 * 4u : kOob, 0u);
+        ipreg[r][1] = load_b128(rip, real ? (uint32_t)j0 * 4u + 16u : kOob, 0u);
+      }
+    }
+  }
+  WChunk ring[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j)
+    if (TCH > 0 || kc0 + j < kc1) load_w(kc0 + j, ring[j]);
+
+  if constexpr (XLDS) {
+#pragma unroll
+    for (int r = 0; r < XPT; ++r) {
+      const int idx = threadIdx.x + 256 * r;
+      if (idx < n8) {
+        const int m = idx / per_row, j0 = (idx % per_row) * 8;
+        if (PERMUTE && j0 < a.K) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t h = (uint16_t)(xreg[r][e >> 1] >> (16 * (e & 1)));
+            xlds[m * xrow + (int)ipreg[PERMUTE ? r : 0][e >> 2][e & 3]] = h;
+          }
+        } else {
+          *reinterpret_cast<u32x4*>(&xlds[m * xrow + j0]) = xreg[r];   // zeros past K
+        }
+      }
+    }
+    if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(&xlds[zero_slot]) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+
+  // ---- main loop: compute chunk kc from the ring slot, then refill the slot with kc + DEPTH ---
+  XChunk xcur, xnxt;
+  if constexpr (!XLDS) {
+    if (kc0 < kc1) load_x_global(kc0, xcur);
+  }
+  if constexpr (TCH > 0) {
+#pragma unroll
+    for (int j = 0; j < TCH; ++j) {
+      const int kc = kc0 + j;
+      if constexpr (XLDS) {
+        load_x_lds(kc, xcur);
+      } else {
+        if (j + 1 < TCH) load_x_global(kc + 1, xnxt);
+      }
+      compute(ring[j % DEPTH], xcur);
+      if (j + DEPTH < TCH) load_w(kc + DEPTH, ring[j % DEPTH]);
+      if constexpr (!XLDS) xcur = xnxt;
+    }
+  } else
+  for (int base = kc0; base < kc1; base += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      const int kc = base + j;
+      if (kc < kc1) {
+        if constexpr (XLDS) {
+          load_x_lds(kc, xcur);
+        } else {
+          if (kc + 1 < kc1) load_x_global(kc + 1, xnxt);
+        }
+        compute(ring[j], xcur);
+        if (kc + DEPTH < kc1) load_w(kc + DEPTH, ring[j]);
+        if constexpr (!XLDS) xcur = xnxt;
+      }
+    }
+  }
+
+  // ---- reduce the KSPLIT partial sums of each column group, then store ---------------------
+  if constexpr (KSPLIT > 1) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][(m * TW + i) * 4 + r][lane] = acc[m][i][r];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int w2 = 1; w2 < KSPLIT; ++w2)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[m][i][r] += red[wave + w2][(m * TW + i) * 4 + r][lane];
+  }
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    if (ct0 + i >= a.CT) continue;
+    const int n = (ct0 + i) * 16 + col;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m * 16 + 4 * q + r;
+        if (row < a.M) a.y[(int64_t)row * a.N + n] = to_out<XT>(acc[m][i][r]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Dispatch of one bit width (instantiated in skinny_b<bits>.hip)
+// ------------------------------------------------------------------------------------------------
+constexpr int kXLdsMax = 64 * 1024;   // dynamic LDS budget for staged x
+
+// True when x for this call can be staged in LDS (small M): the call then needs no workspace.
+// The staging holds at most 4 pieces of 8 inputs per thread (M * Kp <= 8192).
+inline bool x_fits_lds(int64_t M, int Kp) {
+  return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && M * (int64_t)(Kp + 8) * 2 + 16 <= kXLdsMax;
+}
+
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH>
+static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
+  constexpr int CGS = 4 / KSPLIT;
+  const int blocks = (a.CT + TW * CGS - 1) / (TW * CGS);
+  const size_t lds = XLDS ? (size_t)a.M * (a.Kp + 8) * 2 + 16 : 0;
+  if (seg == 4)
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH>), dim3(blocks), dim3(256), lds, s, a);
+  else if constexpr (TCH == 0)
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH>
+static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
+  // Straight-line variants for the LDS-staged (small M), whole-chunk-segment case; ring depths
+  // measured best on MI355X for 4-bit M=1 (2 for 8 chunks per wave, 4 for 16).
+  if constexpr (XLDS != 0) {
+    if (seg == 4 && a.KC == 8 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 8>(a, seg, s);
+    if (seg == 4 && a.KC == 16 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 16>(a, seg, s);
+  }
+  return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 0>(a, seg, s);
+}
+
+// Tiles per wave grow with M so that x traffic (from L2) stays near the weight traffic.
+template <int BITS, int XT>
+static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
+  if (x_fits_lds(a.M, a.Kp))
+    return a.iperm ? run<BITS, XT, 1, 1, 4, 2, 4>(a, seg, s) : run<BITS, XT, 1, 1, 4, 1, 4>(a, seg, s);
+  if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
+  if (a.M <= 32) return run<BITS, XT, 2, 2, 4, 0, 2>(a, seg, s);
+  return run<BITS, XT, 4, 2, 4, 0, 2>(a, seg, s);
+}
+
+template <int BITS>
+hipError_t skinny_bits(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s) {
+  return x_bf16 ? run_m<BITS, 1>(a, seg, s) : run_m<BITS, 0>(a, seg, s);
+}
+hipError_t skinny_b2(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
+hipError_t skinny_b3(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
+hipError_t skinny_b4(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
+hipError_t skinny_b8(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
+
+}  // namespace gq
