@@ -212,6 +212,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="time one extra workload (by label prefix) and exit")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run 3 plain device copies of this many MiB (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings); outside the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
@@ -222,6 +225,15 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     wq.load_library()
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.only:
         for w in [HEADLINE] + extra_workloads():
