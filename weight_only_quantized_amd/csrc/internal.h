@@ -47,8 +47,8 @@ struct GemmCall {
 
 // Workspace layout helpers (tiled.hip): sizes in bytes, 256-B aligned parts.
 size_t ws_xsorted_bytes(const gptq_layer* L, int64_t M);
-size_t ws_nsb_bytes(const gptq_layer* L, int64_t M);
-bool needs_nsb(const gptq_layer* L, int x_bf16);   // the tiled family's bias-correction table
+size_t ws_bias_bytes(const gptq_layer* L, int64_t M);
+bool needs_bias_planes(const gptq_layer* L, int x_bf16);   // the tiled family's bf16 bias correction
 
 // True when the skinny family needs a sorted copy of x in the workspace (act-order with x too
 // large to gather into LDS).
@@ -57,8 +57,8 @@ bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
 // Family launchers.  Both assume the call was validated.
 hipError_t launch_skinny(const GemmCall& c);
 hipError_t launch_tiled(const GemmCall& c);
-// x -> sorted copy (act-order) and/or per-segment sums of x times -bias (tiled family).
-hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_nsb);
+// x -> sorted copy (act-order) and/or the tiled family's bias-correction planes.
+hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_planes);
 
 constexpr int64_t kSkinnyMaxM = 64;
 

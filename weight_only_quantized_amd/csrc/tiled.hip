@@ -5,22 +5,28 @@
 // packed from HBM to the registers that feed the matrix instruction, conversion runs on the
 // vector ALU in the matrix core's slack, and loads of tile k+1 are in flight while tile k
 // multiplies; group scales act inside the K reduction.  Design on gfx950:
-//   * workgroup tile BM x BN = (16 WM) x (64 WN) with four waves side by side along N, each wave
-//     owning WM x WN tiles of 16 x 16 (v_mfma_f32_16x16x32); WM = 8, WN = 2 keeps a wave under
-//     256 registers so two workgroups share a CU;
+//   * workgroup tile BM x BN = (16 WM) x (16 WN NW) with NW waves side by side along N, each
+//     wave owning WM x WN tiles of 16 x 16 (v_mfma_f32_16x16x32); the large-M tile is 256 x 256
+//     (WM = 16, WN = 2, eight waves, two per SIMD, under 256 registers each);
 //   * the x tile of one 128-input chunk goes global -> LDS directly (buffer_load ... lds,
 //     double-buffered, XOR-swizzled so a 16-row A-operand read hits distinct banks); each wave
-//     reads its A operands from LDS;
+//     reads its A operands from LDS one 16-row block ahead of the matrix instructions that use
+//     them, and applies a block's group scales after the next block's MFMAs are issued;
 //   * each wave loads its own packed weight units straight into registers (one 16-byte load per
 //     unit per lane, 4-bit) and builds exact B operands (dequant.h) -- nothing dequantised is ever
 //     written to LDS or HBM;
-//   * for bf16 activations the operand carries a constant bias of 144; its correction
-//     -144 * sum_k x comes from a per-row, per-segment table computed once per call by
-//     prep_kernel (the call's workspace) and enters as the MFMA starting accumulator; fp16
-//     operands are exact and need no table; the group scale multiplies each segment's fp32
-//     partial;
+//   * the group scale multiplies each segment's fp32 partial; fp16 operands are exact
+//   * for bf16 activations the operand carries a constant bias of 144 (dequant.h).  Its
+//     correction  sum_seg scale[seg, n] * (-144 * sum_{k in seg} x[m, k])  is a small GEMM over
+//     segments, done once per output tile after the main loop on the matrix cores: prep_kernel
+//     writes -144 * sum x split into three bf16 planes (hi + mid + lo carry its 24 fp32 bits),
+//     the scales are split into bf16 hi + lo, and every product is exact in fp32;
 //   * workgroup ids are remapped so that the 32 workgroups resident on one XCD share an x row
-//     block (L2) while all XCDs walk the same weight column blocks (MALL).
+//     block (L2) while all XCDs walk the same weight column blocks (MALL);
+//   * each workgroup starts its K loop at a different chunk (the loop wraps around), so the
+//     weight loads in flight at one moment spread over all chunk offsets instead of sitting at
+//     one stride of the tile-major layout; the packed units and metadata of the next chunk are
+//     requested before its x tile.
 #include <hip/hip_runtime.h>
 
 #include "bufmem.h"
@@ -34,66 +40,93 @@ static inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 static inline int seg_k(const gptq_layer* L) { return 32 * L->seg_steps; }
 
 size_t ws_xsorted_bytes(const gptq_layer* L, int64_t M) { return align256((size_t)M * L->Kp * 2); }
-size_t ws_nsb_bytes(const gptq_layer* L, int64_t M) { return align256((size_t)M * (L->Kp / seg_k(L)) * 4); }
+// segments of the sorted K and that count padded to whole 32-deep MFMA steps
+static inline int n_segments(const gptq_layer* L) { return L->Kp / seg_k(L); }
+static inline int n_segments_padded(const gptq_layer* L) { return (n_segments(L) + 31) / 32 * 32; }
+size_t ws_bias_bytes(const gptq_layer* L, int64_t M) { return align256((size_t)3 * M * n_segments_padded(L) * 2); }
 
 // ---------------------------------------------------------------------------------------------
-// prep: xs[m, j] = x[m, perm[j]] (0 past K) and/or nsb[m, s] = -bias * sum_{j in segment s} x.
+// prep: xs[m, j] = x[m, perm[j]] (0 past K) and/or the bias-correction planes: for every row m and
+// segment s, v = -144 * sum_{j in s} x[m, j] (fp32) split as hi + mid + lo in bf16, stored as
+// planes[m][p][s] with the segment count padded to a multiple of 32 (padding written as 0).
 // One thread per 8 sorted inputs of one row.
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t bf16_rne(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
 __global__ void __launch_bounds__(256) prep_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-                                                   uint16_t* __restrict__ xs, float* __restrict__ nsb,
-                                                   int M, int K, int Kp, int segk, int bf16, float neg_bias) {
+                                                   uint16_t* __restrict__ xs, uint16_t* __restrict__ planes,
+                                                   int M, int K, int Kp, int segk, int nsp, int bf16, float neg_bias) {
+  const int nseg = Kp / segk;
+  if (planes && blockIdx.x == 0) {           // zero the padded segments of every row
+    for (int m = blockIdx.y; m < M; m += gridDim.y)
+      for (int i = threadIdx.x; i < 3 * (nsp - nseg); i += 256) {
+        const int p = i / (nsp - nseg), sg = nseg + i % (nsp - nseg);
+        planes[((int64_t)m * 3 + p) * nsp + sg] = 0;
+      }
+  }
   const int j0 = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (j0 >= Kp) return;  // Kp is a multiple of 128: whole 16-thread groups leave together
   for (int m = blockIdx.y; m < M; m += gridDim.y) {
-  const uint16_t* xr = x + (int64_t)m * K;
-  uint16_t v[8];
-  if (perm) {
+    const uint16_t* xr = x + (int64_t)m * K;
+    uint16_t v[8];
+    if (perm) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + e;
-      v[e] = j < K ? xr[perm[j]] : (uint16_t)0;
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + e;
+        v[e] = j < K ? xr[perm[j]] : (uint16_t)0;
+      }
+    } else if (j0 < K) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(xr + j0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[2 * e] = (uint16_t)(w[e] & 0xFFFF); v[2 * e + 1] = (uint16_t)(w[e] >> 16); }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0;
     }
-  } else if (j0 < K) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(xr + j0);
+    if (xs) {
+      u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { v[2 * e] = (uint16_t)(w[e] & 0xFFFF); v[2 * e + 1] = (uint16_t)(w[e] >> 16); }
-  } else {
+      for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+      *reinterpret_cast<u32x4*>(xs + (int64_t)m * Kp + j0) = w;
+    }
+    if (planes) {
+      float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0;
-  }
-  if (xs) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
-    *reinterpret_cast<u32x4*>(xs + (int64_t)m * Kp + j0) = w;
-  }
-  if (nsb) {
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      s += bf16 ? __builtin_bit_cast(float, (uint32_t)v[e] << 16) : (float)__builtin_bit_cast(_Float16, v[e]);
-    const int per = segk / 8;  // threads per segment: 16 or 4, aligned groups of lanes
-    for (int o = per / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if ((threadIdx.x & (per - 1)) == 0) nsb[(int64_t)m * (Kp / segk) + j0 / segk] = neg_bias * s;
-  }
+      for (int e = 0; e < 8; ++e)
+        s += bf16 ? __builtin_bit_cast(float, (uint32_t)v[e] << 16) : (float)__builtin_bit_cast(_Float16, v[e]);
+      const int per = segk / 8;  // threads per segment: 16 or 4, aligned groups of lanes
+      for (int o = per / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if ((threadIdx.x & (per - 1)) == 0) {
+        const float val = neg_bias * s;
+        const uint16_t hi = bf16_rne(val);
+        const float r1 = val - bf16_val(hi);
+        const uint16_t mid = bf16_rne(r1);
+        const uint16_t lo = bf16_rne(r1 - bf16_val(mid));
+        const int sg = j0 / segk;
+        uint16_t* pr = planes + (int64_t)m * 3 * nsp + sg;
+        pr[0] = hi;
+        pr[nsp] = mid;
+        pr[2 * nsp] = lo;
+      }
+    }
   }
 }
 
 static float bias_of(int bits, int bf16) { return (bf16 && bits <= 4) ? 144.f : 0.f; }
-bool needs_nsb(const gptq_layer* L, int x_bf16) { return bias_of(L->bits, x_bf16) != 0.f; }
+bool needs_bias_planes(const gptq_layer* L, int x_bf16) { return bias_of(L->bits, x_bf16) != 0.f; }
 
-hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_nsb) {
+hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_planes) {
   const gptq_layer* L = c.L;
   uint16_t* xs = nullptr;
-  float* nsb = nullptr;
+  uint16_t* planes = nullptr;
   uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
   if (write_xsorted) { xs = reinterpret_cast<uint16_t*>(base); base += ws_xsorted_bytes(L, c.M); }
-  if (write_nsb) nsb = reinterpret_cast<float*>(base);
+  if (write_planes) planes = reinterpret_cast<uint16_t*>(base);
   dim3 grid((unsigned)((L->Kp / 8 + 255) / 256), (unsigned)(c.M < 65535 ? c.M : 65535));
   hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, c.stream, reinterpret_cast<const uint16_t*>(c.x),
-                     write_xsorted ? L->perm : nullptr, xs, nsb, (int)c.M, L->K, L->Kp, seg_k(L), c.x_bf16,
-                     -bias_of(L->bits, c.x_bf16));
+                     write_xsorted ? L->perm : nullptr, xs, planes, (int)c.M, L->K, L->Kp, seg_k(L),
+                     n_segments_padded(L), c.x_bf16, -bias_of(L->bits, c.x_bf16));
   return hipGetLastError();
 }
 
@@ -105,11 +138,12 @@ struct TiledArgs {
   const uint32_t* meta;     // per (tile, group, column): scale bits | stored zero << 16
   const uint32_t* scale32;  // f32 scale bits (scale_kind == 2 only)
   const uint16_t* x;     // [M, ld] sorted-order activations
-  const float* nsb;      // [M, Kp / segk] (bf16 only)
+  const uint16_t* planes;  // bias correction: [M][3][nsp] bf16 (bf16 activations only)
   uint16_t* y;
   int ld;
   int M, K, N, KC, CT, G, scale_kind, MB, NB;
   int gdiv, gshift;      // segment -> group map (see segment_divisor)
+  int nseg, nsp;         // segments of the sorted K, padded to a multiple of 32
 };
 
 // x tile of one chunk in LDS: BM rows x 16 pieces of 16 bytes, no padding, piece c of row r at
@@ -117,18 +151,19 @@ struct TiledArgs {
 // rows (an A operand) then hit sixteen different 16-byte bank groups.  The tile is filled with
 // buffer_load ... lds (lane i of a load writes slot i of its 1 KB destination), so each lane
 // simply fetches the global piece that belongs in its slot.
-template <int BITS, int XT, int WM, int WN, int SEG>
-__global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
+template <int BITS, int XT, int WM, int WN, int SEG, int NW>
+__global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   constexpr int BM = 16 * WM;
   constexpr int NSEG = 4 / SEG;
   constexpr int PARTS = BITS == 8 ? 2 : 1;
   constexpr int PW = BITS == 8 ? 4 : BITS;
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
   constexpr int A_BYTES = BM * 256;            // one chunk of x for the tile
-  constexpr int A_INST = BM / 16;              // 1 KB LDS loads per wave per chunk
+  constexpr int A_INST = BM / (4 * NW);        // 1 KB LDS loads per wave per chunk
+  constexpr int NT = 64 * NW;                  // threads per workgroup
+  static_assert(A_INST * NW * 64 == BM * 16, "x tile must split evenly over the waves");
   constexpr bool BIAS = Bias<BITS, XT>::any;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2][A_BYTES];
-  __shared__ __attribute__((aligned(16))) float nsb_s[2][NSEG][BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,7 +175,8 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
   if ((total & 7) == 0) lid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int mb = lid / a.NB, nb = lid % a.NB;
   const int m0 = mb * BM;
-  const int ct0 = nb * (4 * WN) + wave * WN;
+  const int ct0 = nb * (NW * WN) + wave * WN;
+  const int kshift = (nb * 13) % a.KC;          // first chunk of this workgroup's K loop
 
   f32x4 acc[WM][WN];
 #pragma unroll
@@ -170,8 +206,6 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
   }
   const uint32_t voff_w = (uint32_t)lane * PW * 4u;
   const uint32_t voff_m = (uint32_t)col * 4u;
-  const int nseg_row = a.KC * NSEG;
-  const rsrc_t rn = make_rsrc(a.nsb, BIAS ? (uint32_t)((int64_t)a.M * nseg_row * 4) : 0u);
   // A operand reads: row i*16 + col, piece 4t + q  ->  byte (col * 16 + ((4t + q) ^ col)) * 16 + i * 4096
   uint32_t a_off[4];
 #pragma unroll
@@ -181,20 +215,13 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
     uint32_t w[WN][BITS];
     uint32_t rec[WN][NSEG];
     uint32_t s32[WN][NSEG];
-    float nsb[2];
   };
 
-  // x chunk kc -> xs[buf] by LDS DMA; packed units, metadata and bias sums -> registers.
-  auto issue = [&](int kc, int buf, Stage& st) {
-    const bool tail = ktail && kc == a.KC - 1;
-#pragma unroll
-    for (int j = 0; j < A_INST; ++j) {
-      uint32_t vo = voff_a[j];
-      if (tail && kc * kChunkK + kpiece_a[j] >= a.K) vo = kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void*)(&xs[buf][(wave * A_INST + j) * 1024]), 16, vo,
-          (uint32_t)kc * 256u, 0, 0);
-    }
+  // Step it of the K loop works on chunk kc = (it + kshift) mod KC: packed units and metadata ->
+  // registers, then the x chunk -> xs[buf] by LDS DMA.
+  auto issue = [&](int it, int buf, Stage& st) {
+    int kc = it + kshift;
+    if (kc >= a.KC) kc -= a.KC;
 #pragma unroll
     for (int j = 0; j < WN; ++j)
 #pragma unroll
@@ -209,23 +236,14 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
         st.s32[j][s] = load_b32(rs[j], voff_m, (uint32_t)g * 64u);
       }
     }
-    if constexpr (BIAS) {
+    const bool tail = ktail && kc == a.KC - 1;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int idx = p * 256 + tid;
-        const int r = idx % BM, s = idx / BM;
-        const bool ok = idx < BM * NSEG && m0 + r < a.M;
-        st.nsb[p] = __builtin_bit_cast(float, load_b32(rn, ok ? (uint32_t)((m0 + r) * nseg_row + kc * NSEG + s) * 4u : kOob, 0u));
-      }
-    }
-  };
-  auto store_nsb = [&](int buf, const Stage& st) {
-    if constexpr (BIAS) {
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int idx = p * 256 + tid;
-        if (idx < BM * NSEG) nsb_s[buf][idx / BM][idx % BM] = st.nsb[p];
-      }
+    for (int j = 0; j < A_INST; ++j) {
+      uint32_t vo = voff_a[j];
+      if (tail && kc * kChunkK + kpiece_a[j] >= a.K) vo = kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(&xs[buf][(wave * A_INST + j) * 1024]), 16, vo,
+          (uint32_t)kc * 256u, 0, 0);
     }
   };
 
@@ -242,42 +260,129 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) sc[j][s] = scale_of(st.rec[j][s], st.s32[j][s], a.scale_kind);
     const uint8_t* xb = &xs[buf][0];
+    if constexpr (SEG == 1) {
+      // four scales per chunk: the plain order keeps the wave within four waves per SIMD
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        u32x4 af[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) af[t] = *reinterpret_cast<const u32x4*>(xb + a_off[t] + i * 4096);
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int s = 0; s < NSEG; ++s) {
+            f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(af[t], b[j][t], tmp);
+            acc[i][j] += sc[j][s] * tmp;
+          }
+      }
+      return;
+    }
+    // Row block i: its A operands were read during block i-1; block i+1's are read now, and
+    // block i-1's segment partials are scaled into acc while block i's MFMAs run.
+    u32x4 afc[4], afn[4];
+    f32x4 prev[WN][NSEG];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) afc[t] = *reinterpret_cast<const u32x4*>(xb + a_off[t]);
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      u32x4 af[4];
+      if (i + 1 < WM) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) af[t] = *reinterpret_cast<const u32x4*>(xb + a_off[t] + i * 4096);
-      f32x4 c0[NSEG];
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s)
-        c0[s] = BIAS ? *reinterpret_cast<const f32x4*>(&nsb_s[buf][s][i * 16 + 4 * q]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 4; ++t) afn[t] = *reinterpret_cast<const u32x4*>(xb + a_off[t] + (i + 1) * 4096);
+      }
+      f32x4 part[WN][NSEG];
 #pragma unroll
       for (int j = 0; j < WN; ++j)
 #pragma unroll
         for (int s = 0; s < NSEG; ++s) {
-          f32x4 tmp = c0[s];
+          f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(af[t], b[j][t], tmp);
-          acc[i][j] += sc[j][s] * tmp;
+          for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(afc[t], b[j][t], tmp);
+          part[j][s] = tmp;
         }
+      if (i > 0) {
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int s = 0; s < NSEG; ++s) acc[i - 1][j] += sc[j][s] * prev[j][s];
+      }
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int s = 0; s < NSEG; ++s) prev[j][s] = part[j][s];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) afc[t] = afn[t];
     }
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) acc[WM - 1][j] += sc[j][s] * prev[j][s];
   };
 
   Stage cur, nxt;
   issue(0, 0, cur);
   __builtin_amdgcn_s_waitcnt(0);
-  store_nsb(0, cur);
   __syncthreads();
-  for (int kc = 0; kc < a.KC; ++kc) {
-    const int buf = kc & 1;
-    const bool more = kc + 1 < a.KC;
-    if (more) issue(kc + 1, buf ^ 1, nxt);
+  for (int it = 0; it < a.KC; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < a.KC;
+    if (more) issue(it + 1, buf ^ 1, nxt);
     compute(buf, cur);
-    // the next chunk's x tile, units and sums were issued before this chunk's compute
+    // the next chunk's x tile, units and metadata were issued before this chunk's compute
     __builtin_amdgcn_s_waitcnt(0);
-    if (more) store_nsb(buf ^ 1, nxt);
     __syncthreads();
     cur = nxt;
+  }
+
+  // ---- bf16: add the bias correction, a GEMM over segments on the matrix cores -------------
+  // acc[m, n] += sum_seg (-144 sum_{k in seg} x[m, k]) * scale[g(seg), n].  A: the three bf16
+  // planes of prep_kernel (rows past M read 0); B: this lane's column scale for 8 consecutive
+  // segments split as bf16 hi + lo (0 past the last segment).  All products are exact in fp32.
+  if constexpr (BIAS) {
+    const rsrc_t rp = make_rsrc(a.planes, (uint32_t)((int64_t)3 * a.M * a.nsp * 2));
+    const uint32_t plane_bytes = (uint32_t)a.nsp * 2u;
+    for (int step = 0; step < a.nsp / 32; ++step) {
+      u32x4 bh[WN], bl[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          uint32_t hv[2], lv[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int sg = step * 32 + 8 * q + 2 * e2 + h;
+            float sv = 0.f;
+            if (sg < a.nseg) {
+              const int g = segment_group(sg, a.gdiv, a.gshift, a.G);
+              sv = scale_of(load_b32(rm[j], voff_m, (uint32_t)g * 64u), load_b32(rs[j], voff_m, (uint32_t)g * 64u),
+                            a.scale_kind);
+            }
+            const uint16_t shi = bf16_rne(sv);
+            hv[h] = shi;
+            lv[h] = bf16_rne(sv - bf16_val(shi));
+          }
+          bh[j][e2] = hv[0] | (hv[1] << 16);
+          bl[j][e2] = lv[0] | (lv[1] << 16);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const int row = m0 + i * 16 + col;
+        const uint32_t vo = row < a.M ? (uint32_t)(row * 3 * a.nsp + step * 32 + 8 * q) * 2u : kOob;
+        const u32x4 ph = load_b128(rp, vo, 0u), pm = load_b128(rp, vo, plane_bytes), pl = load_b128(rp, vo, 2u * plane_bytes);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          f32x4 c2 = f32x4{0.f, 0.f, 0.f, 0.f};
+          c2 = mfma16<1>(ph, bh[j], c2);
+          c2 = mfma16<1>(ph, bl[j], c2);
+          c2 = mfma16<1>(pm, bh[j], c2);
+          c2 = mfma16<1>(pm, bl[j], c2);
+          c2 = mfma16<1>(pl, bh[j], c2);
+          acc[i][j] += c2;
+        }
+      }
+    }
   }
 
 #pragma unroll
@@ -294,59 +399,78 @@ __global__ void __launch_bounds__(256) tiled_kernel(const TiledArgs a) {
   }
 }
 
-template <int BITS, int XT, int WM, int WN>
-static hipError_t run_tiled(const TiledArgs& a0, int seg, hipStream_t s) {
+template <int BITS, int XT, int WM, int WN, int SEG, int NW>
+static hipError_t run_tiled(const TiledArgs& a0, hipStream_t s) {
   TiledArgs a = a0;
   a.MB = (a.M + 16 * WM - 1) / (16 * WM);
-  a.NB = (a.CT + 4 * WN - 1) / (4 * WN);
-  const unsigned blocks = (unsigned)(a.MB * a.NB);
-  if (seg == 4)
-    hipLaunchKernelGGL((tiled_kernel<BITS, XT, WM, WN, 4>), dim3(blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((tiled_kernel<BITS, XT, WM, WN, 1>), dim3(blocks), dim3(256), 0, s, a);
+  a.NB = (a.CT + NW * WN - 1) / (NW * WN);
+  hipLaunchKernelGGL((tiled_kernel<BITS, XT, WM, WN, SEG, NW>), dim3((unsigned)(a.MB * a.NB)), dim3(64 * NW), 0, s,
+                     a);
   return hipGetLastError();
+}
+
+// M > 128: wave tile 256 x 32, eight waves (workgroup tile 256 x 256, two waves per SIMD).
+// Smaller M, and 32-input segments (group sizes that are not a multiple of 128, whose four scales
+// per chunk do not fit the larger tile's registers): wave tile 128 x 16, eight waves (128 x 128).
+template <int BITS, int XT>
+static hipError_t run_tiled_m(const TiledArgs& a, int seg, hipStream_t s) {
+  if (seg != 4) return run_tiled<BITS, XT, 8, 1, 1, 8>(a, s);
+  if (a.M > 128) return run_tiled<BITS, XT, 16, 2, 4, 8>(a, s);
+  return run_tiled<BITS, XT, 8, 1, 4, 8>(a, s);
 }
 
 template <int XT>
 static hipError_t run_tiled_bits(const TiledArgs& a, int bits, int seg, hipStream_t s) {
   switch (bits) {
-    // wave tile 128 x 32 (WG tile 128 x 128): ~250 registers -> two workgroups per CU, measured
-    // 1.4-1.6x faster on MI355X than a 128 x 64 wave tile at one workgroup per CU
-    case 2: return run_tiled<2, XT, 8, 2>(a, seg, s);
-    case 3: return run_tiled<3, XT, 8, 2>(a, seg, s);
-    case 4: return run_tiled<4, XT, 8, 2>(a, seg, s);
-    default: return run_tiled<8, XT, 8, 2>(a, seg, s);
+    case 2: return run_tiled_m<2, XT>(a, seg, s);
+    case 3: return run_tiled_m<3, XT>(a, seg, s);
+    case 4: return run_tiled_m<4, XT>(a, seg, s);
+    default: return run_tiled_m<8, XT>(a, seg, s);
   }
 }
 
+// Rows are processed in slices small enough that every byte offset inside a slice (x rows of
+// up to 2^20 inputs, bias planes, y) fits the 32-bit buffer offsets the kernel uses.
 hipError_t launch_tiled(const GemmCall& c) {
   const gptq_layer* L = c.L;
-  const bool nsb = needs_nsb(L, c.x_bf16);
-  if (L->has_perm || nsb) {
-    hipError_t e = launch_prep(c, L->has_perm != 0, nsb);
+  const bool planes = needs_bias_planes(L, c.x_bf16);
+  if (L->has_perm || planes) {
+    hipError_t e = launch_prep(c, L->has_perm != 0, planes);
     if (e != hipSuccess) return e;
   }
   TiledArgs a;
-  uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(c.ws);
+  const uint16_t* x;
   if (L->has_perm) {
-    a.x = reinterpret_cast<const uint16_t*>(base);
+    x = reinterpret_cast<const uint16_t*>(base);
     a.ld = L->Kp;
     base += ws_xsorted_bytes(L, c.M);
   } else {
-    a.x = reinterpret_cast<const uint16_t*>(c.x);
+    x = reinterpret_cast<const uint16_t*>(c.x);
     a.ld = L->K;
   }
-  a.nsb = nsb ? reinterpret_cast<const float*>(base) : nullptr;
+  const uint16_t* pl = planes ? reinterpret_cast<const uint16_t*>(base) : nullptr;
   a.wq = L->wq;
   a.meta = L->meta;
   a.scale32 = L->scale32;
-  a.y = reinterpret_cast<uint16_t*>(c.y);
-  a.M = (int)c.M; a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
+  a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
   segment_divisor(L, &a.gdiv, &a.gshift);
+  a.nseg = n_segments(L);
+  a.nsp = n_segments_padded(L);
   a.scale_kind = L->scales_dtype;
   a.MB = a.NB = 0;
-  return c.x_bf16 ? run_tiled_bits<1>(a, L->bits, L->seg_steps, c.stream)
-                  : run_tiled_bits<0>(a, L->bits, L->seg_steps, c.stream);
+  const int64_t row_bytes = 2 * (int64_t)(a.ld > 3 * a.nsp ? a.ld : 3 * a.nsp);
+  const int64_t slice = ((int64_t(1) << 31) - 1) / row_bytes / 256 * 256;   // >= 1024 for K <= 2^20
+  for (int64_t m0 = 0; m0 < c.M; m0 += slice) {
+    a.M = (int)(c.M - m0 < slice ? c.M - m0 : slice);
+    a.x = x + m0 * a.ld;
+    a.planes = pl ? pl + m0 * 3 * a.nsp : nullptr;
+    a.y = reinterpret_cast<uint16_t*>(c.y) + m0 * a.N;
+    const hipError_t e = c.x_bf16 ? run_tiled_bits<1>(a, L->bits, L->seg_steps, c.stream)
+                                  : run_tiled_bits<0>(a, L->bits, L->seg_steps, c.stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gq
