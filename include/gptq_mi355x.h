@@ -106,8 +106,9 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
                         const void* scales, const int32_t* g_idx, void* stream, gptq_handle_t* out);
 
 /* Device bytes of workspace gptq_gemm needs for this handle, M, activation dtype and path
- * (0 when none).  The size depends only on (handle, M, path): act-order layers need a sorted copy
- * of x, and the TILED family needs per-row segment sums of x. */
+ * (0 when none).  The size depends only on (handle, M, x_dtype, path): act-order layers need a
+ * sorted copy of x, and the TILED family with BF16 activations an fp16 copy of x (exactly
+ * rescaled per row by a power of two) plus one exponent per row. */
 gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int32_t path,
                                 size_t* bytes);
 

@@ -97,9 +97,10 @@ def test_gemm_small_shapes_both_paths(K, N, bits, gs, desc, sdt, xdt):
 
 @pytest.mark.parametrize("bits,xdt", [(4, "f16"), (4, "bf16"), (2, "f16"), (3, "bf16"), (8, "f16"), (8, "bf16")])
 def test_identity_weight(bits, xdt):
-    """W = 0.5 * I.  fp16 operands (code - zero) and 8-bit bf16 operands are exact, so each output
-    is one exact product and must be bit-exact; the 2/3/4-bit bf16 operand carries a constant bias
-    of 144 removed in fp32 (see dequant.h), so there the bar is the bf16 tolerance."""
+    """W = 0.5 * I.  Exact operands make each output one exact product, so it must be bit-exact:
+    fp16 activations, 8-bit codes, and the tiled path (which runs bf16 activations as exactly
+    rescaled fp16).  The skinny path's 2/3/4-bit bf16 operand carries a constant bias of 144 that
+    is removed in fp32 (see dequant.h), so there the bar is the bf16 tolerance."""
     import torch
     import weight_only_quantized_amd as wq
     K = N = 256
@@ -114,10 +115,38 @@ def test_identity_weight(bits, xdt):
     want = o.round_to_dtype_bits(o.decode_float_bits(x, xdt) * 0.5, xdt)
     for M, p in [(1, wq.PATH_SKINNY), (16, wq.PATH_SKINNY), (64, wq.PATH_SKINNY), (1, wq.PATH_TILED), (130, wq.PATH_TILED)]:
         y = run_gemm(h, x[:M], xdt, path=p)
-        if xdt == "f16" or bits == 8:
+        if xdt == "f16" or bits == 8 or p == wq.PATH_TILED:
             assert np.array_equal(y, want[:M]), (M, p)
         else:
             check(y, xdt, o.decode_float_bits(x[:M], xdt) * 0.5, label=(M, p))
+    h.close()
+
+
+@pytest.mark.parametrize("K,desc", [(320, False), (512, True)])
+def test_bf16_rows_of_extreme_magnitude(K, desc):
+    """bf16 activations span 2^-126 .. 2^127; rows scaled by 2^-100 .. 2^100 (and an all-zero row)
+    must each stay within tolerance of the oracle, row by row, on both paths."""
+    import weight_only_quantized_amd as wq
+    N, bits, gs = 192, 4, 64
+    say("bf16-extreme-rows", K, desc)
+    L = gi.make_layer(K, N, bits, gs, desc_act=desc, scales_dtype="bf16", seed=31 + K)
+    h = repack_layer(L)
+    M = 130
+    xf = o.decode_float_bits(gi.make_x(M, K, "bf16", seed=32 + K), "bf16")
+    exps = np.array([-100, -40, 0, 40, 100])[np.arange(M) % 5]
+    xf = xf * np.ldexp(1.0, exps)[:, None]
+    xf[7] = 0.0
+    x = o.round_to_dtype_bits(xf, "bf16")
+    assert np.array_equal(o.decode_float_bits(x, "bf16"), xf)       # the scaling itself is exact
+    y_ref = o.gemm(x, "bf16", L.qweight, L.qzeros, L.scales, "bf16", L.g_idx, bits)
+    for Mc, p in [(M, wq.PATH_TILED), (64, wq.PATH_TILED), (40, wq.PATH_SKINNY), (3, wq.PATH_SKINNY)]:
+        y = run_gemm(h, x[:Mc], "bf16", path=p)
+        if Mc > 7:
+            assert np.all((y[7] & 0x7FFF) == 0), p
+        for r in range(Mc):
+            if r == 7:
+                continue
+            check(y[r:r + 1], "bf16", y_ref[r:r + 1], label=(Mc, p, r, int(exps[r])))
     h.close()
 
 

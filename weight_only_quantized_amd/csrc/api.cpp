@@ -226,8 +226,13 @@ gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int
   if (path == GPTQ_PATH_SKINNY && M > kSkinnyMaxM) return GPTQ_E_INVALID_ARG;
   size_t b = 0;
   if (M > 0) {
-    if (h->has_perm && (path == GPTQ_PATH_TILED || skinny_needs_xsorted(h, M))) b += ws_xsorted_bytes(h, M);
-    if (path == GPTQ_PATH_TILED && needs_bias_planes(h, x_dtype == GPTQ_BF16)) b += ws_bias_bytes(h, M);
+    const int bf16 = x_dtype == GPTQ_BF16;
+    if (path == GPTQ_PATH_TILED) {
+      if (tiled_needs_xsorted(h, bf16)) b += ws_xsorted_bytes(h, M);
+      if (bf16) b += ws_rowexp_bytes(M);
+    } else if (skinny_needs_xsorted(h, M)) {
+      b += ws_xsorted_bytes(h, M);
+    }
   }
   *bytes = b;
   return GPTQ_OK;

@@ -47,8 +47,9 @@ struct GemmCall {
 
 // Workspace layout helpers (tiled.hip): sizes in bytes, 256-B aligned parts.
 size_t ws_xsorted_bytes(const gptq_layer* L, int64_t M);
-size_t ws_bias_bytes(const gptq_layer* L, int64_t M);
-bool needs_bias_planes(const gptq_layer* L, int x_bf16);   // the tiled family's bf16 bias correction
+size_t ws_rowexp_bytes(int64_t M);
+// the tiled family reads a prepared copy of x: act-order layers, and bf16 activations (fp16 copy)
+bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16);
 
 // True when the skinny family needs a sorted copy of x in the workspace (act-order with x too
 // large to gather into LDS).
@@ -57,8 +58,9 @@ bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
 // Family launchers.  Both assume the call was validated.
 hipError_t launch_skinny(const GemmCall& c);
 hipError_t launch_tiled(const GemmCall& c);
-// x -> sorted copy (act-order) and/or the tiled family's bias-correction planes.
-hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_planes);
+// x -> workspace copy in the sorted input order (identity without act-order); with to_f16, a bf16
+// x becomes fp16 after a per-row power-of-two scaling whose exponents follow the copy.
+hipError_t launch_prep(const GemmCall& c, bool to_f16);
 
 constexpr int64_t kSkinnyMaxM = 64;
 

@@ -19,7 +19,7 @@ hipError_t launch_skinny(const GemmCall& c) {
   a.scale_kind = L->scales_dtype;
   a.iperm = nullptr;
   if (skinny_needs_xsorted(L, c.M)) {
-    hipError_t e = launch_prep(c, true, false);
+    hipError_t e = launch_prep(c, false);
     if (e != hipSuccess) return e;
     a.x = reinterpret_cast<const uint16_t*>(c.ws);
     a.ld = L->Kp;

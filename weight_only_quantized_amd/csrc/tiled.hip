@@ -15,12 +15,13 @@
 //   * each wave loads its own packed weight units straight into registers (one 16-byte load per
 //     unit per lane, 4-bit) and builds exact B operands (dequant.h) -- nothing dequantised is ever
 //     written to LDS or HBM;
-//   * the group scale multiplies each segment's fp32 partial; fp16 operands are exact
-//   * for bf16 activations the operand carries a constant bias of 144 (dequant.h).  Its
-//     correction  sum_seg scale[seg, n] * (-144 * sum_{k in seg} x[m, k])  is a small GEMM over
-//     segments, done once per output tile after the main loop on the matrix cores: prep_kernel
-//     writes -144 * sum x split into three bf16 planes (hi + mid + lo carry its 24 fp32 bits),
-//     the scales are split into bf16 hi + lo, and every product is exact in fp32;
+//   * the group scale multiplies each segment's fp32 partial; the operands are exact fp16
+//     (activation, and code - zero);
+//   * bf16 activations are converted to fp16 once per call by prep_kernel, exactly, after an
+//     exact power-of-two scaling of each row that puts its largest magnitude in [2^14, 2^15); the
+//     row's outputs are multiplied back by the same power of two before rounding to bf16.  (bf16
+//     B operands would need the +144 bias of dequant.h, whose eight busy mantissa bits measured
+//     about 10% slower on the matrix cores than exact small fp16 integers, plus a correction.)
 //   * workgroup ids are remapped so that the 32 workgroups resident on one XCD share an x row
 //     block (L2) while all XCDs walk the same weight column blocks (MALL);
 //   * each workgroup starts its K loop at a different chunk (the loop wraps around), so the
@@ -37,96 +38,82 @@
 namespace gq {
 
 static inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
-static inline int seg_k(const gptq_layer* L) { return 32 * L->seg_steps; }
-
 size_t ws_xsorted_bytes(const gptq_layer* L, int64_t M) { return align256((size_t)M * L->Kp * 2); }
-// segments of the sorted K and that count padded to whole 32-deep MFMA steps
-static inline int n_segments(const gptq_layer* L) { return L->Kp / seg_k(L); }
-static inline int n_segments_padded(const gptq_layer* L) { return (n_segments(L) + 31) / 32 * 32; }
-size_t ws_bias_bytes(const gptq_layer* L, int64_t M) { return align256((size_t)3 * M * n_segments_padded(L) * 2); }
+size_t ws_rowexp_bytes(int64_t M) { return align256((size_t)M * 4); }
+bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16) { return L->has_perm || x_bf16; }
 
 // ---------------------------------------------------------------------------------------------
-// prep: xs[m, j] = x[m, perm[j]] (0 past K) and/or the bias-correction planes: for every row m and
-// segment s, v = -144 * sum_{j in s} x[m, j] (fp32) split as hi + mid + lo in bf16, stored as
-// planes[m][p][s] with the segment count padded to a multiple of 32 (padding written as 0).
-// One thread per 8 sorted inputs of one row.
+// prep: one workgroup per row m.  xs[m, j] = x[m, perm[j]] (perm may be the identity), 0 for
+// K <= j < Kp.  With to_f16 (bf16 input): e_m = ilogb(max_k |x[m, k]|) - 14 (0 for an all-zero or
+// non-finite maximum), xs holds fp16(x * 2^-e_m) and rowexp[m] = e_m.  The conversion is exact
+// except for magnitudes below 2^-17 after scaling (more than 2^31 below the row maximum), which
+// land on fp16's subnormal grid.  Without to_f16 the 16-bit values are copied unchanged.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint16_t bf16_rne(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
-__device__ __forceinline__ float bf16_val(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
-
 __global__ void __launch_bounds__(256) prep_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-                                                   uint16_t* __restrict__ xs, uint16_t* __restrict__ planes,
-                                                   int M, int K, int Kp, int segk, int nsp, int bf16, float neg_bias) {
-  const int nseg = Kp / segk;
-  if (planes && blockIdx.x == 0) {           // zero the padded segments of every row
-    for (int m = blockIdx.y; m < M; m += gridDim.y)
-      for (int i = threadIdx.x; i < 3 * (nsp - nseg); i += 256) {
-        const int p = i / (nsp - nseg), sg = nseg + i % (nsp - nseg);
-        planes[((int64_t)m * 3 + p) * nsp + sg] = 0;
-      }
-  }
-  const int j0 = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (j0 >= Kp) return;  // Kp is a multiple of 128: whole 16-thread groups leave together
-  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+                                                   uint16_t* __restrict__ xs, int32_t* __restrict__ rowexp, int M,
+                                                   int K, int Kp, int to_f16) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int m = blockIdx.x; m < M; m += gridDim.x) {
     const uint16_t* xr = x + (int64_t)m * K;
-    uint16_t v[8];
-    if (perm) {
+    int e = 0;
+    if (to_f16) {
+      float mx = 0.f;
+      for (int k = tid * 8; k < K; k += 2048) {   // K is a multiple of 32
+        const u32x4 w = *reinterpret_cast<const u32x4*>(xr + k);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = j0 + e;
-        v[e] = j < K ? xr[perm[j]] : (uint16_t)0;
+        for (int q = 0; q < 4; ++q) {
+          mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w[q] << 16)));
+          mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w[q] & 0xFFFF0000u)));
+        }
       }
-    } else if (j0 < K) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(xr + j0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { v[2 * e] = (uint16_t)(w[e] & 0xFFFF); v[2 * e + 1] = (uint16_t)(w[e] >> 16); }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0;
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (lane == 0) red[wave] = mx;
+      __syncthreads();
+      mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      __syncthreads();
+      if (mx > 0.f && mx <= 3.4028235e38f) e = ilogbf(mx) - 14;
+      if (tid == 0) rowexp[m] = e;
     }
-    if (xs) {
+    for (int j0 = tid * 8; j0 < Kp; j0 += 2048) {
+      uint16_t v[8];
+      if (perm) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int j = j0 + q;
+          v[q] = j < K ? xr[perm[j]] : (uint16_t)0;
+        }
+      } else if (j0 < K) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(xr + j0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { v[2 * q] = (uint16_t)(w[q] & 0xFFFF); v[2 * q + 1] = (uint16_t)(w[q] >> 16); }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = 0;
+      }
+      if (to_f16) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float f = ldexpf(__builtin_bit_cast(float, (uint32_t)v[q] << 16), -e);
+          v[q] = __builtin_bit_cast(uint16_t, (_Float16)f);
+        }
+      }
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+      for (int q = 0; q < 4; ++q) w[q] = (uint32_t)v[2 * q] | ((uint32_t)v[2 * q + 1] << 16);
       *reinterpret_cast<u32x4*>(xs + (int64_t)m * Kp + j0) = w;
-    }
-    if (planes) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        s += bf16 ? __builtin_bit_cast(float, (uint32_t)v[e] << 16) : (float)__builtin_bit_cast(_Float16, v[e]);
-      const int per = segk / 8;  // threads per segment: 16 or 4, aligned groups of lanes
-      for (int o = per / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-      if ((threadIdx.x & (per - 1)) == 0) {
-        const float val = neg_bias * s;
-        const uint16_t hi = bf16_rne(val);
-        const float r1 = val - bf16_val(hi);
-        const uint16_t mid = bf16_rne(r1);
-        const uint16_t lo = bf16_rne(r1 - bf16_val(mid));
-        const int sg = j0 / segk;
-        uint16_t* pr = planes + (int64_t)m * 3 * nsp + sg;
-        pr[0] = hi;
-        pr[nsp] = mid;
-        pr[2 * nsp] = lo;
-      }
     }
   }
 }
 
-static float bias_of(int bits, int bf16) { return (bf16 && bits <= 4) ? 144.f : 0.f; }
-bool needs_bias_planes(const gptq_layer* L, int x_bf16) { return bias_of(L->bits, x_bf16) != 0.f; }
-
-hipError_t launch_prep(const GemmCall& c, bool write_xsorted, bool write_planes) {
+hipError_t launch_prep(const GemmCall& c, bool to_f16) {
   const gptq_layer* L = c.L;
-  uint16_t* xs = nullptr;
-  uint16_t* planes = nullptr;
   uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
-  if (write_xsorted) { xs = reinterpret_cast<uint16_t*>(base); base += ws_xsorted_bytes(L, c.M); }
-  if (write_planes) planes = reinterpret_cast<uint16_t*>(base);
-  dim3 grid((unsigned)((L->Kp / 8 + 255) / 256), (unsigned)(c.M < 65535 ? c.M : 65535));
-  hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, c.stream, reinterpret_cast<const uint16_t*>(c.x),
-                     write_xsorted ? L->perm : nullptr, xs, planes, (int)c.M, L->K, L->Kp, seg_k(L),
-                     n_segments_padded(L), c.x_bf16, -bias_of(L->bits, c.x_bf16));
+  uint16_t* xs = reinterpret_cast<uint16_t*>(base);
+  int32_t* rowexp = to_f16 ? reinterpret_cast<int32_t*>(base + ws_xsorted_bytes(L, c.M)) : nullptr;
+  const unsigned blocks = (unsigned)(c.M < 65535 ? c.M : 65535);
+  hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, c.stream, reinterpret_cast<const uint16_t*>(c.x),
+                     L->has_perm ? L->perm : nullptr, xs, rowexp, (int)c.M, L->K, L->Kp, to_f16 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -138,12 +125,11 @@ struct TiledArgs {
   const uint32_t* meta;     // per (tile, group, column): scale bits | stored zero << 16
   const uint32_t* scale32;  // f32 scale bits (scale_kind == 2 only)
   const uint16_t* x;     // [M, ld] sorted-order activations
-  const uint16_t* planes;  // bias correction: [M][3][nsp] bf16 (bf16 activations only)
+  const int32_t* rowexp;   // per-row power of two of the fp16 copy (bf16 activations only)
   uint16_t* y;
   int ld;
   int M, K, N, KC, CT, G, scale_kind, MB, NB;
   int gdiv, gshift;      // segment -> group map (see segment_divisor)
-  int nseg, nsp;         // segments of the sorted K, padded to a multiple of 32
 };
 
 // x tile of one chunk in LDS: BM rows x 16 pieces of 16 bytes, no padding, piece c of row r at
@@ -151,7 +137,7 @@ struct TiledArgs {
 // rows (an A operand) then hit sixteen different 16-byte bank groups.  The tile is filled with
 // buffer_load ... lds (lane i of a load writes slot i of its 1 KB destination), so each lane
 // simply fetches the global piece that belongs in its slot.
-template <int BITS, int XT, int WM, int WN, int SEG, int NW>
+template <int BITS, int OB, int WM, int WN, int SEG, int NW>
 __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   constexpr int BM = 16 * WM;
   constexpr int NSEG = 4 / SEG;
@@ -162,7 +148,6 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   constexpr int A_INST = BM / (4 * NW);        // 1 KB LDS loads per wave per chunk
   constexpr int NT = 64 * NW;                  // threads per workgroup
   static_assert(A_INST * NW * 64 == BM * 16, "x tile must split evenly over the waves");
-  constexpr bool BIAS = Bias<BITS, XT>::any;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2][A_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -253,7 +238,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        b[j][t] = build_b<BITS, XT>(st.w[j], t, zero_term<BITS, XT>(stored_zero_of(st.rec[j][t / SEG])));
+        b[j][t] = build_b<BITS, 0>(st.w[j], t, zero_term<BITS, 0>(stored_zero_of(st.rec[j][t / SEG])));
     float sc[WN][NSEG];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
@@ -273,7 +258,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
           for (int s = 0; s < NSEG; ++s) {
             f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(af[t], b[j][t], tmp);
+            for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<0>(af[t], b[j][t], tmp);
             acc[i][j] += sc[j][s] * tmp;
           }
       }
@@ -298,7 +283,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
         for (int s = 0; s < NSEG; ++s) {
           f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(afc[t], b[j][t], tmp);
+          for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<0>(afc[t], b[j][t], tmp);
           part[j][s] = tmp;
         }
       if (i > 0) {
@@ -335,56 +320,6 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     cur = nxt;
   }
 
-  // ---- bf16: add the bias correction, a GEMM over segments on the matrix cores -------------
-  // acc[m, n] += sum_seg (-144 sum_{k in seg} x[m, k]) * scale[g(seg), n].  A: the three bf16
-  // planes of prep_kernel (rows past M read 0); B: this lane's column scale for 8 consecutive
-  // segments split as bf16 hi + lo (0 past the last segment).  All products are exact in fp32.
-  if constexpr (BIAS) {
-    const rsrc_t rp = make_rsrc(a.planes, (uint32_t)((int64_t)3 * a.M * a.nsp * 2));
-    const uint32_t plane_bytes = (uint32_t)a.nsp * 2u;
-    for (int step = 0; step < a.nsp / 32; ++step) {
-      u32x4 bh[WN], bl[WN];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          uint32_t hv[2], lv[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int sg = step * 32 + 8 * q + 2 * e2 + h;
-            float sv = 0.f;
-            if (sg < a.nseg) {
-              const int g = segment_group(sg, a.gdiv, a.gshift, a.G);
-              sv = scale_of(load_b32(rm[j], voff_m, (uint32_t)g * 64u), load_b32(rs[j], voff_m, (uint32_t)g * 64u),
-                            a.scale_kind);
-            }
-            const uint16_t shi = bf16_rne(sv);
-            hv[h] = shi;
-            lv[h] = bf16_rne(sv - bf16_val(shi));
-          }
-          bh[j][e2] = hv[0] | (hv[1] << 16);
-          bl[j][e2] = lv[0] | (lv[1] << 16);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        const int row = m0 + i * 16 + col;
-        const uint32_t vo = row < a.M ? (uint32_t)(row * 3 * a.nsp + step * 32 + 8 * q) * 2u : kOob;
-        const u32x4 ph = load_b128(rp, vo, 0u), pm = load_b128(rp, vo, plane_bytes), pl = load_b128(rp, vo, 2u * plane_bytes);
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          f32x4 c2 = f32x4{0.f, 0.f, 0.f, 0.f};
-          c2 = mfma16<1>(ph, bh[j], c2);
-          c2 = mfma16<1>(ph, bl[j], c2);
-          c2 = mfma16<1>(pm, bh[j], c2);
-          c2 = mfma16<1>(pm, bl[j], c2);
-          c2 = mfma16<1>(pl, bh[j], c2);
-          acc[i][j] += c2;
-        }
-      }
-    }
-  }
-
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     if (ct0 + j >= a.CT) continue;
@@ -394,17 +329,20 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + i * 16 + 4 * q + r;
-        if (m < a.M) a.y[(int64_t)m * a.N + n] = to_out<XT>(acc[i][j][r]);
+        if (m < a.M) {
+          if constexpr (OB) a.y[(int64_t)m * a.N + n] = to_out<1>(ldexpf(acc[i][j][r], a.rowexp[m]));
+          else a.y[(int64_t)m * a.N + n] = to_out<0>(acc[i][j][r]);
+        }
       }
   }
 }
 
-template <int BITS, int XT, int WM, int WN, int SEG, int NW>
+template <int BITS, int OB, int WM, int WN, int SEG, int NW>
 static hipError_t run_tiled(const TiledArgs& a0, hipStream_t s) {
   TiledArgs a = a0;
   a.MB = (a.M + 16 * WM - 1) / (16 * WM);
   a.NB = (a.CT + NW * WN - 1) / (NW * WN);
-  hipLaunchKernelGGL((tiled_kernel<BITS, XT, WM, WN, SEG, NW>), dim3((unsigned)(a.MB * a.NB)), dim3(64 * NW), 0, s,
+  hipLaunchKernelGGL((tiled_kernel<BITS, OB, WM, WN, SEG, NW>), dim3((unsigned)(a.MB * a.NB)), dim3(64 * NW), 0, s,
                      a);
   return hipGetLastError();
 }
@@ -412,59 +350,53 @@ static hipError_t run_tiled(const TiledArgs& a0, hipStream_t s) {
 // M > 128: wave tile 256 x 32, eight waves (workgroup tile 256 x 256, two waves per SIMD).
 // Smaller M, and 32-input segments (group sizes that are not a multiple of 128, whose four scales
 // per chunk do not fit the larger tile's registers): wave tile 128 x 16, eight waves (128 x 128).
-template <int BITS, int XT>
+template <int BITS, int OB>
 static hipError_t run_tiled_m(const TiledArgs& a, int seg, hipStream_t s) {
-  if (seg != 4) return run_tiled<BITS, XT, 8, 1, 1, 8>(a, s);
-  if (a.M > 128) return run_tiled<BITS, XT, 16, 2, 4, 8>(a, s);
-  return run_tiled<BITS, XT, 8, 1, 4, 8>(a, s);
+  if (seg != 4) return run_tiled<BITS, OB, 8, 1, 1, 8>(a, s);
+  if (a.M > 128) return run_tiled<BITS, OB, 16, 2, 4, 8>(a, s);
+  return run_tiled<BITS, OB, 8, 1, 4, 8>(a, s);
 }
 
-template <int XT>
+template <int OB>
 static hipError_t run_tiled_bits(const TiledArgs& a, int bits, int seg, hipStream_t s) {
   switch (bits) {
-    case 2: return run_tiled_m<2, XT>(a, seg, s);
-    case 3: return run_tiled_m<3, XT>(a, seg, s);
-    case 4: return run_tiled_m<4, XT>(a, seg, s);
-    default: return run_tiled_m<8, XT>(a, seg, s);
+    case 2: return run_tiled_m<2, OB>(a, seg, s);
+    case 3: return run_tiled_m<3, OB>(a, seg, s);
+    case 4: return run_tiled_m<4, OB>(a, seg, s);
+    default: return run_tiled_m<8, OB>(a, seg, s);
   }
 }
 
-// Rows are processed in slices small enough that every byte offset inside a slice (x rows of
-// up to 2^20 inputs, bias planes, y) fits the 32-bit buffer offsets the kernel uses.
+// Rows are processed in slices small enough that every byte offset inside a slice (x rows of up
+// to 2^20 inputs, y) fits the 32-bit buffer offsets the kernel uses.
 hipError_t launch_tiled(const GemmCall& c) {
   const gptq_layer* L = c.L;
-  const bool planes = needs_bias_planes(L, c.x_bf16);
-  if (L->has_perm || planes) {
-    hipError_t e = launch_prep(c, L->has_perm != 0, planes);
-    if (e != hipSuccess) return e;
-  }
   TiledArgs a;
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(c.ws);
   const uint16_t* x;
-  if (L->has_perm) {
+  const int32_t* rowexp = nullptr;
+  if (tiled_needs_xsorted(L, c.x_bf16)) {
+    hipError_t e = launch_prep(c, c.x_bf16 != 0);
+    if (e != hipSuccess) return e;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(c.ws);
     x = reinterpret_cast<const uint16_t*>(base);
+    if (c.x_bf16) rowexp = reinterpret_cast<const int32_t*>(base + ws_xsorted_bytes(L, c.M));
     a.ld = L->Kp;
-    base += ws_xsorted_bytes(L, c.M);
   } else {
     x = reinterpret_cast<const uint16_t*>(c.x);
     a.ld = L->K;
   }
-  const uint16_t* pl = planes ? reinterpret_cast<const uint16_t*>(base) : nullptr;
   a.wq = L->wq;
   a.meta = L->meta;
   a.scale32 = L->scale32;
   a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
   segment_divisor(L, &a.gdiv, &a.gshift);
-  a.nseg = n_segments(L);
-  a.nsp = n_segments_padded(L);
   a.scale_kind = L->scales_dtype;
   a.MB = a.NB = 0;
-  const int64_t row_bytes = 2 * (int64_t)(a.ld > 3 * a.nsp ? a.ld : 3 * a.nsp);
-  const int64_t slice = ((int64_t(1) << 31) - 1) / row_bytes / 256 * 256;   // >= 1024 for K <= 2^20
+  const int64_t slice = ((int64_t(1) << 31) - 1) / (2 * (int64_t)a.ld) / 256 * 256;   // >= 1024 for K <= 2^20
   for (int64_t m0 = 0; m0 < c.M; m0 += slice) {
     a.M = (int)(c.M - m0 < slice ? c.M - m0 : slice);
     a.x = x + m0 * a.ld;
-    a.planes = pl ? pl + m0 * 3 * a.nsp : nullptr;
+    a.rowexp = rowexp ? rowexp + m0 : nullptr;
     a.y = reinterpret_cast<uint16_t*>(c.y) + m0 * a.N;
     const hipError_t e = c.x_bf16 ? run_tiled_bits<1>(a, L->bits, L->seg_steps, c.stream)
                                   : run_tiled_bits<0>(a, L->bits, L->seg_steps, c.stream);
