@@ -107,8 +107,9 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
 
 /* Device bytes of workspace gptq_gemm needs for this handle, M, activation dtype and path
  * (0 when none).  The size depends only on (handle, M, x_dtype, path): act-order layers need a
- * sorted copy of x, and the TILED family with BF16 activations an fp16 copy of x (exactly
- * rescaled per row by a power of two) plus one exponent per row. */
+ * sorted copy of x; the TILED family also copies x when in_features is not a multiple of 128
+ * (rows zero-padded) and, for BF16 activations, makes that copy fp16 (exactly rescaled per row
+ * by a power of two) with one exponent per row. */
 gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int32_t path,
                                 size_t* bytes);
 

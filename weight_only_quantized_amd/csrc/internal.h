@@ -48,7 +48,8 @@ struct GemmCall {
 // Workspace layout helpers (tiled.hip): sizes in bytes, 256-B aligned parts.
 size_t ws_xsorted_bytes(const gptq_layer* L, int64_t M);
 size_t ws_rowexp_bytes(int64_t M);
-// the tiled family reads a prepared copy of x: act-order layers, and bf16 activations (fp16 copy)
+// the tiled family reads a prepared copy of x: act-order layers, bf16 activations (fp16 copy), and
+// K not a multiple of 128 (zero-padded rows)
 bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16);
 
 // True when the skinny family needs a sorted copy of x in the workspace (act-order with x too

@@ -40,7 +40,11 @@ namespace gq {
 static inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 size_t ws_xsorted_bytes(const gptq_layer* L, int64_t M) { return align256((size_t)M * L->Kp * 2); }
 size_t ws_rowexp_bytes(int64_t M) { return align256((size_t)M * 4); }
-bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16) { return L->has_perm || x_bf16; }
+// The tiled kernel reads x in whole 128-input chunks, so it takes a zero-padded copy whenever x
+// itself is not in that form: act-order (sorted copy), bf16 (fp16 copy), K not a multiple of 128.
+bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16) {
+  return L->has_perm || x_bf16 || (L->K % kChunkK) != 0;
+}
 
 // ---------------------------------------------------------------------------------------------
 // prep: one workgroup per row m.  xs[m, j] = x[m, perm[j]] (perm may be the identity), 0 for
@@ -146,7 +150,6 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
   constexpr int A_BYTES = BM * 256;            // one chunk of x for the tile
   constexpr int A_INST = BM / (4 * NW);        // 1 KB LDS loads per wave per chunk
-  constexpr int NT = 64 * NW;                  // threads per workgroup
   static_assert(A_INST * NW * 64 == BM * 16, "x tile must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2][A_BYTES];
 
@@ -171,16 +174,14 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
 
   // ---- resources and fixed per-lane offsets -------------------------------------------------
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.ld * 2));
+  // x rows hold whole chunks (ld is a multiple of 128: a padded copy is made otherwise)
   uint32_t voff_a[A_INST];
-  int kpiece_a[A_INST];                        // input offset of the lane's piece within a chunk
 #pragma unroll
   for (int j = 0; j < A_INST; ++j) {
     const int slot = (wave * A_INST + j) * 64 + lane;
     const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
-    kpiece_a[j] = c * 8;
     voff_a[j] = (m0 + r < a.M) ? (uint32_t)((m0 + r) * a.ld + c * 8) * 2u : kOob;
   }
-  const bool ktail = (a.K & (kChunkK - 1)) != 0;
   rsrc_t rw[WN], rm[WN], rs[WN];
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
@@ -221,11 +222,11 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
         st.s32[j][s] = load_b32(rs[j], voff_m, (uint32_t)g * 64u);
       }
     }
-    const bool tail = ktail && kc == a.KC - 1;
 #pragma unroll
     for (int j = 0; j < A_INST; ++j) {
-      uint32_t vo = voff_a[j];
-      if (tail && kc * kChunkK + kpiece_a[j] >= a.K) vo = kOob;
+      // (the offset goes through a local: passed straight from the array, the host pass of this
+      // compiler drops the kernel's launch stub)
+      const uint32_t vo = voff_a[j];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx, (__attribute__((address_space(3))) void*)(&xs[buf][(wave * A_INST + j) * 1024]), 16, vo,
           (uint32_t)kc * 256u, 0, 0);
