@@ -3,6 +3,7 @@ libgptq_mi355x.so for gfx950 (hipcc cross-compiles, no GPU needed)."""
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -11,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
 SOURCES = ["api.cpp", "repack.hip", "skinny.hip", "skinny_b2.hip", "skinny_b3.hip", "skinny_b4.hip",
-           "skinny_b8.hip", "tiled.hip"]
+           "skinny_b8.hip", "mid.hip", "mid_b2.hip", "mid_b3.hip", "mid_b4.hip", "mid_b8.hip", "tiled.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -22,6 +23,20 @@ def hipcc_flags():
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-Wno-unused-result",
     ]
+
+
+def spilled_kernels(remarks: str) -> list:
+    """Kernels whose resource-usage remarks report VGPR or SGPR spills.  Every kernel here is
+    sized to stay in registers; a spill means a configuration outgrew its budget."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"[SV]GPRs Spill: (\d+)", line)
+        if m and int(m.group(1)) > 0 and name and name not in out:
+            out.append(name)
+    return out
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
@@ -37,13 +52,16 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         src = os.path.join(CSRC, s)
         obj = os.path.join(objdir, s + ".o")
         # api.cpp holds host code only but calls the HIP runtime: compile it as HIP too
-        cmd = [HIPCC] + flags + ["-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC] + flags + ["-x", "hip", "-c", src, "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             sys.stderr.write(r.stdout + r.stderr)
             raise RuntimeError(f"hipcc failed on {s} ({r.returncode})")
+        spills = spilled_kernels(r.stderr)
+        if spills:
+            raise RuntimeError(f"{s}: kernels spill registers to scratch (not allowed): {spills}")
         return obj
 
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:

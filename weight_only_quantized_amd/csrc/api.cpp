@@ -230,8 +230,9 @@ gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int
     if (path == GPTQ_PATH_TILED) {
       if (tiled_needs_xsorted(h, bf16)) b += ws_xsorted_bytes(h, M);
       if (bf16) b += ws_rowexp_bytes(M);
-    } else if (skinny_needs_xsorted(h, M)) {
-      b += ws_xsorted_bytes(h, M);
+    } else {
+      if (skinny_needs_xsorted(h, M)) b += ws_xsorted_bytes(h, M);
+      b += ws_mid_part_bytes(h, M);
     }
   }
   *bytes = b;

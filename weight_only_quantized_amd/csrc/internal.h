@@ -56,8 +56,14 @@ bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16);
 // large to gather into LDS).
 bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
 
-// Family launchers.  Both assume the call was validated.
+// The SKINNY path (M <= 64) runs the skinny kernel when x fits one workgroup's LDS whole and the
+// mid kernel (split K, mid.hip) otherwise; the mid kernel's partial sums need workspace.
+bool uses_mid(const gptq_layer* L, int64_t M);
+size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M);
+
+// Family launchers.  All assume the call was validated.
 hipError_t launch_skinny(const GemmCall& c);
+hipError_t launch_mid(const GemmCall& c);
 hipError_t launch_tiled(const GemmCall& c);
 // x -> workspace copy in the sorted input order (identity without act-order); with to_f16, a bf16
 // x becomes fp16 after a per-row power-of-two scaling whose exponents follow the copy.

@@ -9,6 +9,7 @@ bool skinny_needs_xsorted(const gptq_layer* L, int64_t M) { return L->has_perm &
 
 hipError_t launch_skinny(const GemmCall& c) {
   const gptq_layer* L = c.L;
+  if (uses_mid(L, c.M)) return launch_mid(c);
   SkinnyArgs a;
   a.wq = L->wq;
   a.meta = L->meta;

@@ -314,6 +314,10 @@ inline bool x_fits_lds(int64_t M, int Kp) {
   return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && M * (int64_t)(Kp + 8) * 2 + 16 <= kXLdsMax;
 }
 
+// The other case the skinny kernel keeps: M <= 16 over at most 32 chunks of K, with x read from
+// L2 per chunk (on MI355X faster there than the mid family's split K, slower for longer K).
+inline bool skinny_reads_x_from_l2(int64_t M, int KC) { return M <= 16 && KC <= 32; }
+
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH>
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   constexpr int CGS = 4 / KSPLIT;
@@ -328,23 +332,21 @@ static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
 
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH>
 static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
-  // Straight-line variants for the LDS-staged (small M), whole-chunk-segment case; ring depths
-  // measured best on MI355X for 4-bit M=1 (2 for 8 chunks per wave, 4 for 16).
-  if constexpr (XLDS != 0) {
-    if (seg == 4 && a.KC == 8 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 8>(a, seg, s);
-    if (seg == 4 && a.KC == 16 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 16>(a, seg, s);
-  }
+  // Straight-line variants for the whole-chunk-segment case; ring depths measured best on
+  // MI355X for 4-bit M=1 (2 for 8 chunks per wave, 4 for 16).
+  if (seg == 4 && a.KC == 8 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 8>(a, seg, s);
+  if (seg == 4 && a.KC == 16 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 16>(a, seg, s);
   return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 0>(a, seg, s);
 }
 
-// Tiles per wave grow with M so that x traffic (from L2) stays near the weight traffic.
+// x staged in LDS whole, or (M <= 16, see skinny_reads_x_from_l2) read from L2 per chunk, two
+// column tiles per wave so that x traffic stays near the weight traffic.
 template <int BITS, int XT>
 static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
   if (x_fits_lds(a.M, a.Kp))
     return a.iperm ? run<BITS, XT, 1, 1, 4, 2, 4>(a, seg, s) : run<BITS, XT, 1, 1, 4, 1, 4>(a, seg, s);
   if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
-  if (a.M <= 32) return run<BITS, XT, 2, 2, 4, 0, 2>(a, seg, s);
-  return run<BITS, XT, 4, 2, 4, 0, 2>(a, seg, s);
+  return hipErrorInvalidValue;   // larger M goes to the mid family
 }
 
 template <int BITS>

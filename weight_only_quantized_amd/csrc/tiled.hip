@@ -47,7 +47,9 @@ bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// prep: one workgroup per row m.  xs[m, j] = x[m, perm[j]] (perm may be the identity), 0 for
+// prep: workgroup (m, stripe) handles row m, sorted inputs [stripe * span, (stripe + 1) * span)
+// (one stripe of the whole row when a row maximum is needed).  xs[m, j] = x[m, perm[j]] (perm may
+// be the identity), 0 for
 // K <= j < Kp.  With to_f16 (bf16 input): e_m = ilogb(max_k |x[m, k]|) - 14 (0 for an all-zero or
 // non-finite maximum), xs holds fp16(x * 2^-e_m) and rowexp[m] = e_m.  The conversion is exact
 // except for magnitudes below 2^-17 after scaling (more than 2^31 below the row maximum), which
@@ -55,7 +57,7 @@ bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16) {
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) prep_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
                                                    uint16_t* __restrict__ xs, int32_t* __restrict__ rowexp, int M,
-                                                   int K, int Kp, int to_f16) {
+                                                   int K, int Kp, int to_f16, int span) {
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int m = blockIdx.x; m < M; m += gridDim.x) {
@@ -79,7 +81,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const uint16_t* __restrict__ 
       if (mx > 0.f && mx <= 3.4028235e38f) e = ilogbf(mx) - 14;
       if (tid == 0) rowexp[m] = e;
     }
-    for (int j0 = tid * 8; j0 < Kp; j0 += 2048) {
+    const int jend = min(Kp, (int)blockIdx.y * span + span);
+    for (int j0 = (int)blockIdx.y * span + tid * 8; j0 < jend; j0 += 2048) {
       uint16_t v[8];
       if (perm) {
 #pragma unroll
@@ -115,9 +118,11 @@ hipError_t launch_prep(const GemmCall& c, bool to_f16) {
   uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
   uint16_t* xs = reinterpret_cast<uint16_t*>(base);
   int32_t* rowexp = to_f16 ? reinterpret_cast<int32_t*>(base + ws_xsorted_bytes(L, c.M)) : nullptr;
-  const unsigned blocks = (unsigned)(c.M < 65535 ? c.M : 65535);
-  hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, c.stream, reinterpret_cast<const uint16_t*>(c.x),
-                     L->has_perm ? L->perm : nullptr, xs, rowexp, (int)c.M, L->K, L->Kp, to_f16 ? 1 : 0);
+  const unsigned rows = (unsigned)(c.M < 65535 ? c.M : 65535);
+  const int span = to_f16 ? L->Kp : 2048;     // multiple of 2048 or the whole row
+  const unsigned stripes = (unsigned)((L->Kp + span - 1) / span);
+  hipLaunchKernelGGL(prep_kernel, dim3(rows, stripes), dim3(256), 0, c.stream, reinterpret_cast<const uint16_t*>(c.x),
+                     L->has_perm ? L->perm : nullptr, xs, rowexp, (int)c.M, L->K, L->Kp, to_f16 ? 1 : 0, span);
   return hipGetLastError();
 }
 
