@@ -45,18 +45,26 @@ def algorithmic_bytes(K, N, M, bits, gs, desc_act, scale_bytes=2, act_bytes=2):
     return b
 
 
-def csrc_digest():
+# Sources that make up each measured kernel family (its own files plus the shared headers).
+SHARED_SOURCES = ["bufmem.h", "dequant.h", "internal.h", "layout.h"]
+FAMILY_SOURCES = {"skinny": ["skinny_impl.h", "skinny.hip", "skinny_b4.hip"],
+                  "tiled": ["tiled.hip"]}
+
+
+def csrc_digest(family):
+    """Digest of the sources of one kernel family; stored counter readings are used only while it
+    is unchanged."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "weight_only_quantized_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(FAMILY_SOURCES[family] + SHARED_SOURCES):
         h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, only if the kernel sources
-    are unchanged since they were taken."""
+    """HBM bytes per launch from the committed rocprofv3 counter runs (profiles/traffic.json), only
+    if the sources of the kernel's family are unchanged since they were taken."""
     p = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(p):
         return None
@@ -65,7 +73,7 @@ def stored_traffic(kernel_key):
     except Exception:
         return None
     e = t.get(kernel_key)
-    if not e or e.get("csrc_sha") != csrc_digest():
+    if not e or e.get("csrc_sha") != csrc_digest(kernel_key.split("_")[0]):
         return None
     return e.get("bytes_per_launch")
 
@@ -259,8 +267,14 @@ def main():
             rec["frac_hbm"] = round(b / (eus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
             if e.M >= 1024:
                 fl = 2.0 * e.M * e.N * e.K
-                rec["TFLOP_per_s"] = round(fl / (eus * 1e-6) / 1e12, 1)
-                rec["frac_mfma_bf16"] = round(fl / (eus * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
+                tf = fl / (eus * 1e-6) / 1e12
+                rec["TFLOP_per_s"] = round(tf, 1)
+                rec["frac_mfma_bf16"] = round(tf / BF16_PEAK_TFLOPS, 4)
+                # whole call (the fp16 copy of x plus the GEMM), against the dense 16-bit MFMA peak
+                rec["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                   "traffic": stored_traffic("tiled_" + e.label()),
+                                   "kernel": "gq::tiled_kernel<4,1,16,2,4,8>", "algorithmic_flops_per_launch": fl}
             extra.append(rec)
             print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_oracle_baseline(w)

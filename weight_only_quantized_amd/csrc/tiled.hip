@@ -23,11 +23,10 @@
 //     B operands would need the +144 bias of dequant.h, whose eight busy mantissa bits measured
 //     about 10% slower on the matrix cores than exact small fp16 integers, plus a correction.)
 //   * workgroup ids are remapped so that the 32 workgroups resident on one XCD share an x row
-//     block (L2) while all XCDs walk the same weight column blocks (MALL);
-//   * each workgroup starts its K loop at a different chunk (the loop wraps around), so the
-//     weight loads in flight at one moment spread over all chunk offsets instead of sitting at
-//     one stride of the tile-major layout; the packed units and metadata of the next chunk are
-//     requested before its x tile.
+//     block (L2) while all XCDs walk the same weight column blocks (MALL); workgroups sharing a
+//     row block walk K in step, so each x chunk is fetched into L2 about once per XCD (a
+//     staggered K start per column block measured 2-3 % slower and doubled the fabric reads);
+//   * the packed units and metadata of the next chunk are requested before its x tile.
 #include <hip/hip_runtime.h>
 
 #include "bufmem.h"
@@ -169,7 +168,6 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   const int mb = lid / a.NB, nb = lid % a.NB;
   const int m0 = mb * BM;
   const int ct0 = nb * (NW * WN) + wave * WN;
-  const int kshift = (nb * 13) % a.KC;          // first chunk of this workgroup's K loop
 
   f32x4 acc[WM][WN];
 #pragma unroll
@@ -208,11 +206,8 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     uint32_t s32[WN][NSEG];
   };
 
-  // Step it of the K loop works on chunk kc = (it + kshift) mod KC: packed units and metadata ->
-  // registers, then the x chunk -> xs[buf] by LDS DMA.
-  auto issue = [&](int it, int buf, Stage& st) {
-    int kc = it + kshift;
-    if (kc >= a.KC) kc -= a.KC;
+  // Chunk kc: packed units and metadata -> registers, then the x chunk -> xs[buf] by LDS DMA.
+  auto issue = [&](int kc, int buf, Stage& st) {
 #pragma unroll
     for (int j = 0; j < WN; ++j)
 #pragma unroll
