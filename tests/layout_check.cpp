@@ -1,6 +1,7 @@
 // Host check of the runtime layout map (weight_only_quantized_amd/csrc/layout.h): for every bit
 // width, the 32 codes of a lane must cover every bit of the lane's words exactly once, and every
-// lane word must land at a distinct offset inside its unit.  Built with g++ by
+// lane word must land at a distinct offset inside its unit; the division-free segment -> group map
+// must equal integer division for every divisor and segment a layer can have.  Built with g++ by
 // tests/test_boundary_cpu.py; prints "ok" on success.
 #include <cstdio>
 #include <set>
@@ -36,6 +37,23 @@ int main() {
     for (int lane = 0; lane < 64; ++lane)
       for (int i = 0; i < 32; ++i) kn.insert(gq::code_k_in_chunk(lane, i) * 16 + gq::lane_col(lane));
     if ((int)kn.size() != 2048) { printf("k/n cover %d\n", bits); return 1; }
+  }
+  // segment -> group map: d = segments per group (1 .. 4096, and 2^30 for one group), segments
+  // below 2^15 (K <= 2^20 in 32-input steps), G groups
+  for (long long d = 1; d <= 4096; ++d) {
+    const int sh = gq::segment_shift(d);
+    const unsigned mg = gq::segment_magic(d);
+    const int G = (int)((32768 + d - 1) / d);
+    for (int si = 0; si < 32768; ++si) {
+      const long long want = si / d < G - 1 ? si / d : G - 1;
+      if (gq::group_of_segment(si, mg, sh, G) != want) { printf("group map d=%lld si=%d\n", d, si); return 1; }
+    }
+  }
+  {
+    const long long d = 1LL << 30;
+    if (gq::segment_shift(d) != 30) { printf("shift 2^30\n"); return 1; }
+    for (int si = 0; si < 32768; ++si)
+      if (gq::group_of_segment(si, gq::segment_magic(d), gq::segment_shift(d), 1) != 0) { printf("one group\n"); return 1; }
   }
   printf("ok\n");
   return 0;

@@ -71,15 +71,13 @@ hipError_t launch_prep(const GemmCall& c, bool to_f16);
 
 constexpr int64_t kSkinnyMaxM = 64;
 
-// Segment -> group map: group = min(segment / div, G - 1), shift = log2(div) when div is a power
-// of two, else -1.  A segment is a 128-input chunk (seg_steps 4) or a 32-input step (seg_steps 1).
-inline void segment_divisor(const gptq_layer* L, int* div, int* shift) {
-  int d = L->group_size == -1 ? (1 << 30) : L->gs_eff / (32 * L->seg_steps);
-  int sh = -1;
-  for (int b = 0; b < 31; ++b)
-    if (d == (1 << b)) sh = b;
-  *div = d;
-  *shift = sh;
+// Segment -> group map of a layer (layout.h, group_of_segment): d = segments per group, 2^30 for
+// one group.  A segment is a 128-input chunk (seg_steps 4) or a 32-input step (seg_steps 1); a layer
+// has fewer than 2^15 segments, so the magic-number division is exact.
+inline void segment_divisor(const gptq_layer* L, uint32_t* magic, int* shift) {
+  const int64_t d = L->group_size == -1 ? (int64_t(1) << 30) : L->gs_eff / (32 * L->seg_steps);
+  *shift = segment_shift(d);
+  *magic = segment_magic(d);
 }
 
 }  // namespace gq

@@ -79,6 +79,23 @@ GQ_HD int code_pieces(int bits, int i, Piece* p) {
   p[0] = {1, 8 * b + 7, 1, 0}; p[1] = {2, 8 * b + 6, 2, 1}; return 2;
 }
 
+// Segment -> group map (a segment is a 128-input chunk or a 32-input step; d = segments per group):
+// group = min(segment / d, G - 1), computed without a divide instruction.  shift = log2(d) when d is
+// a power of two, else -1 with magic = ceil(2^32 / d); then segment / d = (segment * magic) >> 32,
+// exact whenever segment * (magic * d - 2^32) < 2^32, which holds for segment < 2^32 / d.
+GQ_HD int segment_shift(int64_t d) {
+  for (int b = 0; b < 31; ++b)
+    if (d == (int64_t(1) << b)) return b;
+  return -1;
+}
+GQ_HD uint32_t segment_magic(int64_t d) {
+  return segment_shift(d) >= 0 ? 0u : (uint32_t)(((int64_t(1) << 32) + d - 1) / d);
+}
+GQ_HD int group_of_segment(int si, uint32_t magic, int shift, int G) {
+  const int g = shift >= 0 ? (si >> shift) : (int)(((uint64_t)(uint32_t)si * magic) >> 32);
+  return g < G - 1 ? g : G - 1;
+}
+
 // Sorted-K offset within the chunk, and column within the tile, of lane code i.
 GQ_HD int code_k_in_chunk(int lane, int i) { return 32 * (i >> 3) + 8 * (lane >> 4) + (i & 7); }
 GQ_HD int lane_col(int lane) { return lane & 15; }

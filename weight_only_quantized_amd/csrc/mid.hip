@@ -56,7 +56,7 @@ static hipError_t mid_pass(const GemmCall& c, const uint16_t* x, int ld, float* 
   a.y = reinterpret_cast<uint16_t*>(c.y) + r0 * L->N;
   a.M = (int)rows; a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
   a.scale_kind = L->scales_dtype;
-  segment_divisor(L, &a.gdiv, &a.gshift);
+  segment_divisor(L, &a.gmagic, &a.gshift);
   a.cpw = p.cpw;
   hipError_t e;
   switch (L->bits) {

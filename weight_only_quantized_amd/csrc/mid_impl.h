@@ -36,14 +36,14 @@ struct MidArgs {
   uint16_t* y;            // [M, N] (KS == 1)
   int ld;
   int M, K, N, KC, CT, G, scale_kind;
-  int gdiv, gshift;
+  uint32_t gmagic;       // segment -> group map (segment_divisor)
+  int gshift;
   int cpw;                // chunks per K slice (TCH)
 };
 
 // Group of segment `si` (a chunk, or a 32-input step); wave-uniform.
-__device__ __forceinline__ int mid_segment_group(int si, int gdiv, int gshift, int G) {
-  const int g = gshift >= 0 ? (si >> gshift) : si / gdiv;
-  return g < G - 1 ? g : G - 1;
+__device__ __forceinline__ int mid_segment_group(int si, uint32_t gmagic, int gshift, int G) {
+  return group_of_segment(si, gmagic, gshift, G);
 }
 
 template <int BITS, int XT, int MT, int WN, int NW, int SEG, int DEPTH, int TCH>
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
         load_words<PW, kAuxStream>(rw[j], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &c.w[j][4 * p]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      const int g = mid_segment_group(SEG == 4 ? kc : kc * 4 + s, a.gdiv, a.gshift, a.G);
+      const int g = mid_segment_group(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         c.rec[j][s] = load_b32(rm[j], voff_m, (uint32_t)g * 64u);

@@ -33,14 +33,14 @@ struct SkinnyArgs {
   uint16_t* y;            // [M, N]
   int64_t ld;             // row stride of x in elements
   int M, K, Kp, N, KC, CT, G, scale_kind;
-  int gdiv, gshift;       // group of a segment = min(seg_index / gdiv, G - 1); gshift >= 0 when gdiv = 1 << gshift
+  uint32_t gmagic;        // segment -> group map (segment_divisor): min(segment / d, G - 1)
+  int gshift;
 };
 
 // Group of segment `si` (a chunk index when segments are chunks, a 32-input step index when they
 // are steps).  Every operand is wave-uniform, so this runs on the scalar unit.
-__device__ __forceinline__ int segment_group(int si, int gdiv, int gshift, int G) {
-  const int g = gshift >= 0 ? (si >> gshift) : si / gdiv;
-  return g < G - 1 ? g : G - 1;
+__device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift, int G) {
+  return group_of_segment(si, gmagic, gshift, G);
 }
 
 // XLDS = 1: the workgroup first copies x[0:M, sorted 0:Kp] (gathering through perm when set) into
@@ -56,13 +56,15 @@ __device__ __forceinline__ int segment_group(int si, int gdiv, int gshift, int G
 // (a loop back-edge would make the compiler wait for every load in flight).
 // XLDS == 2: as XLDS == 1 for an act-order layer (x is scattered into sorted order).
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH>
-__global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
-  constexpr int CGS = 4 / KSPLIT;               // column groups per workgroup
+__global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) skinny_kernel(const SkinnyArgs a) {
+  constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;  // waves per workgroup
+  constexpr int NT = 64 * NWV;
+  constexpr int CGS = NWV / KSPLIT;             // column groups per workgroup
   constexpr int NSEG = 4 / SEG;                 // fixup segments per chunk
   constexpr int PARTS = BITS == 8 ? 2 : 1;      // loads per lane per unit
   constexpr int PW = BITS == 8 ? 4 : BITS;      // words per load
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
-  __shared__ float red[4][MT * TW * 4][64];
+  __shared__ float red[NWV][MT * TW * 4][64];
   extern __shared__ __attribute__((aligned(16))) uint16_t xlds[];
 
   // Chunk and tile bookkeeping is wave-uniform (scalar registers).
@@ -110,7 +112,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
         load_words<PW, kAuxStream>(rw[i], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &c.w[i][4 * p]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gdiv, a.gshift, a.G);
+      const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
         c.rec[i][s] = load_b32(rm[i], voff_m, (uint32_t)g * 64u);
@@ -139,19 +141,18 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
         c.xa[m][t] = load_b128(rx, vo, (uint32_t)kc * 256u);
       }
   };
-  // rows >= M read a 16-byte zero slot placed after the staged rows (a broadcast read)
-  const int zero_slot = a.M * xrow;
+  // rows >= M read a zero row placed after the staged rows, so every lane's address is its fixed
+  // base plus the chunk offset (an immediate in the straight-line variants)
+  const int zero_row = a.M * xrow;
   int xbase[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) xbase[m] = (m * 16 + col < a.M) ? (m * 16 + col) * xrow + 8 * q : -1;
+  for (int m = 0; m < MT; ++m) xbase[m] = ((m * 16 + col < a.M) ? (m * 16 + col) * xrow : zero_row) + 8 * q;
   auto load_x_lds = [&](int kc, XChunk& c) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int off = xbase[m] >= 0 ? xbase[m] + kc * kChunkK + 32 * t : zero_slot;
-        c.xa[m][t] = *reinterpret_cast<const u32x4*>(&xlds[off]);
-      }
+      for (int t = 0; t < 4; ++t)
+        c.xa[m][t] = *reinterpret_cast<const u32x4*>(&xlds[xbase[m] + kc * kChunkK + 32 * t]);
   };
 
   auto compute = [&](const WChunk& c, const XChunk& xc) {
@@ -188,7 +189,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
   // x staging loads go out before the weight ring (loads complete in issue order).  Act-order
   // layers scatter x into sorted order in LDS through the inverse permutation: both global reads
   // stay coalesced and independent, and the scatter is eight 2-byte LDS writes per piece.
-  constexpr int XPT = 4;                          // 16-byte x pieces per thread held in registers
+  constexpr int XPT = 4 * 256 / NT;               // 16-byte x pieces per thread held in registers
   constexpr bool PERMUTE = XLDS == 2;
   u32x4 xreg[XPT];
   u32x4 ipreg[PERMUTE ? XPT : 1][2];
@@ -197,7 +198,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
   if constexpr (XLDS) {
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
-      const int idx = threadIdx.x + 256 * r;
+      const int idx = threadIdx.x + NT * r;
       const int m = idx / per_row, j0 = (idx % per_row) * 8;
       const bool real = idx < n8 && j0 < a.K;
       xreg[r] = load_b128(rx, real ? (uint32_t)(m * a.ld + j0) * 2u : kOob, 0u);
@@ -216,7 +217,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
   if constexpr (XLDS) {
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
-      const int idx = threadIdx.x + 256 * r;
+      const int idx = threadIdx.x + NT * r;
       if (idx < n8) {
         const int m = idx / per_row, j0 = (idx % per_row) * 8;
         if (PERMUTE && j0 < a.K) {
@@ -230,7 +231,8 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyArgs a) {
         }
       }
     }
-    if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(&xlds[zero_slot]) = u32x4{0u, 0u, 0u, 0u};
+    for (int j = threadIdx.x * 8; j < a.Kp; j += NT * 8)
+      *reinterpret_cast<u32x4*>(&xlds[zero_row + j]) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
 
@@ -311,7 +313,7 @@ constexpr int kXLdsMax = 64 * 1024;   // dynamic LDS budget for staged x
 // True when x for this call can be staged in LDS (small M): the call then needs no workspace.
 // The staging holds at most 4 pieces of 8 inputs per thread (M * Kp <= 8192).
 inline bool x_fits_lds(int64_t M, int Kp) {
-  return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && M * (int64_t)(Kp + 8) * 2 + 16 <= kXLdsMax;
+  return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && (M + 1) * (int64_t)(Kp + 8) * 2 <= kXLdsMax;
 }
 
 // The other case the skinny kernel keeps: M <= 16 over at most 32 chunks of K, with x read from
@@ -320,13 +322,14 @@ inline bool skinny_reads_x_from_l2(int64_t M, int KC) { return M <= 16 && KC <= 
 
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH>
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
-  constexpr int CGS = 4 / KSPLIT;
+  constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;
+  constexpr int CGS = NWV / KSPLIT;
   const int blocks = (a.CT + TW * CGS - 1) / (TW * CGS);
-  const size_t lds = XLDS ? (size_t)a.M * (a.Kp + 8) * 2 + 16 : 0;
+  const size_t lds = XLDS ? (size_t)(a.M + 1) * (a.Kp + 8) * 2 : 0;   // staged rows + the zero row
   if (seg == 4)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH>), dim3(blocks), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH>), dim3(blocks), dim3(64 * NWV), lds, s, a);
   else if constexpr (TCH == 0)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0>), dim3(blocks), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0>), dim3(blocks), dim3(64 * NWV), lds, s, a);
   return hipGetLastError();
 }
 
@@ -334,6 +337,7 @@ template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH>
 static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
   // Straight-line variants for the whole-chunk-segment case; ring depths measured best on
   // MI355X for 4-bit M=1 (2 for 8 chunks per wave, 4 for 16).
+  if (seg == 4 && a.KC == 4 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 4>(a, seg, s);
   if (seg == 4 && a.KC == 8 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 8>(a, seg, s);
   if (seg == 4 && a.KC == 16 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 16>(a, seg, s);
   return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 0>(a, seg, s);

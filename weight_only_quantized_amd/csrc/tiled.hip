@@ -137,7 +137,8 @@ struct TiledArgs {
   uint16_t* y;
   int ld;
   int M, K, N, KC, CT, G, scale_kind, MB, NB;
-  int gdiv, gshift;      // segment -> group map (see segment_divisor)
+  uint32_t gmagic;       // segment -> group map (see segment_divisor)
+  int gshift;
 };
 
 // x tile of one chunk in LDS: BM rows x 16 pieces of 16 bytes, no padding, piece c of row r at
@@ -215,7 +216,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
         load_words<PW, 0>(rw[j], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &st.w[j][4 * p]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gdiv, a.gshift, a.G);
+      const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         st.rec[j][s] = load_b32(rm[j], voff_m, (uint32_t)g * 64u);
@@ -390,7 +391,7 @@ hipError_t launch_tiled(const GemmCall& c) {
   a.meta = L->meta;
   a.scale32 = L->scale32;
   a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
-  segment_divisor(L, &a.gdiv, &a.gshift);
+  segment_divisor(L, &a.gmagic, &a.gshift);
   a.scale_kind = L->scales_dtype;
   a.MB = a.NB = 0;
   const int64_t slice = ((int64_t(1) << 31) - 1) / (2 * (int64_t)a.ld) / 256 * 256;   // >= 1024 for K <= 2^20
