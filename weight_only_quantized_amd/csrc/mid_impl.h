@@ -10,7 +10,7 @@
 //     all); it copies x[0:M, its slice] into LDS once (buffer_load ... lds, rows XOR-swizzled as
 //     in the tiled family), and every wave reads its A operands from there;
 //   * each wave streams the packed units of its WN column tiles through a register ring DEPTH
-//     chunks deep; every workgroup handles exactly TCH chunks, emitted as straight-line code with
+//     (2) chunks deep; every workgroup handles exactly TCH chunks, emitted as straight-line code with
 //     unconditional loads (chunk indices clamped; x past K is zero), so each chunk waits only for
 //     its own loads -- a loop back-edge or a conditional load would make the compiler wait for
 //     every load in flight;
@@ -212,7 +212,9 @@ struct MidPlan {
 constexpr int kMidNW = 4, kMidWN = 2;          // four waves of two column tiles: 128 columns
 
 // Slices of 16, 8 or 4 chunks (x of one slice: cpw * MT * 4 KB <= 64 KB of LDS), the longest that
-// still gives about four workgroups per compute unit.
+// still gives two workgroups per compute unit (longer slices stream behind a 2-chunk ring; at four
+// workgroups per compute unit the 4-chunk slices loaded everything before computing, 13-16 %
+// slower on the act-order 8192 x 8192, M = 32 layer).
 // Rows per pass: all of M, except 32 for 32-input segments (whose four-row-block variant would
 // not fit in registers).
 inline int64_t mid_rows_per_pass(const gptq_layer* L) { return L->seg_steps == 4 ? 64 : 32; }
@@ -223,7 +225,7 @@ inline MidPlan mid_plan(const gptq_layer* L, int64_t M) {
   p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int nbk = (L->CT + kMidNW * kMidWN - 1) / (kMidNW * kMidWN);
   int cpw = L->seg_steps == 4 ? 16 / p.MT : 4;
-  while (cpw > 4 && (int64_t)nbk * ((L->KC + cpw - 1) / cpw) < 4 * 256) cpw /= 2;
+  while (cpw > 4 && (int64_t)nbk * ((L->KC + cpw - 1) / cpw) < 2 * 256) cpw /= 2;
   p.cpw = cpw;
   p.KS = (L->KC + cpw - 1) / cpw;
   return p;
@@ -231,7 +233,7 @@ inline MidPlan mid_plan(const gptq_layer* L, int64_t M) {
 
 template <int BITS, int XT, int MT, int SEG, int TCH>
 static hipError_t run_mid_cfg(const MidArgs& a, int KS, hipStream_t s) {
-  constexpr int DEPTH = 4;
+  constexpr int DEPTH = 2;
   const int nbk = (a.CT + kMidNW * kMidWN - 1) / (kMidNW * kMidWN);
   const size_t lds = (size_t)TCH * 16 * MT * 256;
   hipLaunchKernelGGL((mid_kernel<BITS, XT, MT, kMidWN, kMidNW, SEG, DEPTH, TCH>), dim3(nbk, KS), dim3(64 * kMidNW), lds,
