@@ -43,8 +43,8 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
   return group_of_segment(si, gmagic, gshift, G);
 }
 
-// XLDS = 1: the workgroup first copies x[0:M, sorted 0:Kp] (gathering through perm when set) into
-// LDS, rows padded by 16 bytes; A operands then come from LDS.  XLDS = 0: each chunk's A
+// XLDS = 1: each wave first copies the part of x[0:M, 0:Kp] that its own K range multiplies into
+// LDS (rows padded by 16 bytes) and reads its A operands from there, with no workgroup barrier.  XLDS = 0: each chunk's A
 // operands are loaded from global memory (L2-resident) one chunk ahead.
 // DEPTH chunks of packed weights (and their group metadata) are kept in flight per wave in a
 // register ring, so a wave never waits on HBM latency more than once per DEPTH chunks.
@@ -54,7 +54,8 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // TCH > 0: every wave owns exactly TCH chunks (the dispatcher guarantees KC == KSPLIT * TCH) and
 // its whole K range is emitted as straight-line code, so each chunk waits only for its own loads
 // (a loop back-edge would make the compiler wait for every load in flight).
-// XLDS == 2: as XLDS == 1 for an act-order layer (x is scattered into sorted order).
+// XLDS == 2: an act-order layer; the workgroup scatters all of x into sorted order in LDS through
+// the inverse permutation, then meets at a barrier.
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH>
 __global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) skinny_kernel(const SkinnyArgs a) {
   constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;  // waves per workgroup
@@ -191,11 +192,31 @@ __global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) skinny_kernel(
   // stay coalesced and independent, and the scatter is eight 2-byte LDS writes per piece.
   constexpr int XPT = 4 * 256 / NT;               // 16-byte x pieces per thread held in registers
   constexpr bool PERMUTE = XLDS == 2;
-  u32x4 xreg[XPT];
+  u32x4 xreg[PERMUTE ? XPT : 1];
   u32x4 ipreg[PERMUTE ? XPT : 1][2];
   const int per_row = a.Kp / 8;
   const int n8 = XLDS ? a.M * per_row : 0;        // 16-byte pieces of x (original order if iperm)
-  if constexpr (XLDS) {
+  // Without act-order each wave stages only the inputs of its own K range (rows 0..M-1, then its
+  // part of the zero row), so no wave waits for another before its first chunk.  x_fits_lds bounds
+  // a wave's M * wpr row pieces by 64 * XLW (a fixed count of loads: a load under a branch would
+  // make the compiler wait for it at once) and its (M + 1) * wpr pieces by 64 * XSW.  With TCH > 0
+  // every wave owns exactly TCH chunks, so the piece -> (row, input) split is a shift.
+  constexpr int XLW = XLDS == 1 ? (TCH > 0 ? 4 : 8) : 1;
+  constexpr int XSW = 8;
+  const int wpr = TCH > 0 ? TCH * (kChunkK / 8) : max(kc1 - kc0, 0) * (kChunkK / 8);
+  const int wrows = a.M * wpr;                          // pieces loaded from x
+  const int wn8 = wrows + wpr;                          // ... plus the zero row
+  u32x4 xw[XLW];
+  if constexpr (XLDS == 1) {
+#pragma unroll
+    for (int r = 0; r < XLW; ++r) {
+      const int idx = lane + 64 * r;
+      const int m = idx / wpr, j0 = kc0 * kChunkK + (idx - m * wpr) * 8;
+      const bool real = idx < wrows && j0 < a.K;
+      xw[r] = load_b128(rx, real ? (uint32_t)(m * a.ld + j0) * 2u : kOob, 0u);
+    }
+  }
+  if constexpr (XLDS == 2) {
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
       const int idx = threadIdx.x + NT * r;
@@ -214,7 +235,24 @@ __global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) skinny_kernel(
   for (int j = 0; j < DEPTH; ++j)
     if (TCH > 0 || kc0 + j < kc1) load_w(kc0 + j, ring[j]);
 
-  if constexpr (XLDS) {
+  if constexpr (XLDS == 1) {
+#pragma unroll
+    for (int r = 0; r < XSW; ++r) {
+      if (64 * r < wn8) {                               // wave-uniform
+        const int idx = lane + 64 * r;
+        if (idx < wn8) {
+          const int m = idx / wpr, j0 = kc0 * kChunkK + (idx - m * wpr) * 8;
+          const u32x4 v = (r < XLW && idx < wrows) ? xw[r < XLW ? r : 0] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&xlds[m * xrow + j0]) = v;   // row M: the zero row
+        }
+      }
+    }
+    // the wave reads back only what it wrote: LDS keeps one wave's accesses in order, the fence
+    // keeps the compiler from moving reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  if constexpr (XLDS == 2) {
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
       const int idx = threadIdx.x + NT * r;
@@ -313,7 +351,9 @@ constexpr int kXLdsMax = 64 * 1024;   // dynamic LDS budget for staged x
 // True when x for this call can be staged in LDS (small M): the call then needs no workspace.
 // The staging holds at most 4 pieces of 8 inputs per thread (M * Kp <= 8192).
 inline bool x_fits_lds(int64_t M, int Kp) {
-  return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && (M + 1) * (int64_t)(Kp + 8) * 2 <= kXLdsMax;
+  // (with M * Kp <= 8192, a wave's share (M + 1) * 16 * ceil(Kp / 512) is at most 512 pieces)
+  return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && (M + 1) * (int64_t)(Kp + 8) * 2 <= kXLdsMax &&
+         (M + 1) * 16 * ((Kp / 128 + 3) / 4) <= 512;
 }
 
 // The other case the skinny kernel keeps: M <= 16 over at most 32 chunks of K, with x read from
