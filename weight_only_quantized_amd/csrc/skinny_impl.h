@@ -56,8 +56,11 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // (a loop back-edge would make the compiler wait for every load in flight).
 // XLDS == 2: an act-order layer; the workgroup scatters all of x into sorted order in LDS through
 // the inverse permutation, then meets at a barrier.
+// At least two waves per SIMD: the kernel needs about 60-130 VGPRs, and without the hint the
+// compiler spreads a one-wave-per-SIMD schedule over all 512, so a compute unit held one workgroup.
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH>
-__global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) skinny_kernel(const SkinnyArgs a) {
+__global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) __attribute__((amdgpu_waves_per_eu(2)))
+skinny_kernel(const SkinnyArgs a) {
   constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;  // waves per workgroup
   constexpr int NT = 64 * NWV;
   constexpr int CGS = NWV / KSPLIT;             // column groups per workgroup
