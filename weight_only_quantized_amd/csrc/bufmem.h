@@ -48,5 +48,9 @@ __device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t voff, uint32_t sof
 __device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// Stores past the resource's byte size are dropped, like loads there return zero.
+__device__ __forceinline__ void store_b16(rsrc_t r, uint16_t v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, 0u, 0);
+}
 
 }  // namespace gq

@@ -141,6 +141,36 @@ struct TiledArgs {
   int gshift;
 };
 
+// Writes a wave's WM x WN accumulator tiles (rows m0 + 16 i + 4 q + r, column tile ct0 + j, lane
+// column col) to y.  bf16 outputs (OB) are first multiplied back by 2^rowexp[m]: the exponents of
+// a row block come in one 16-byte load per lane, all issued before the first store.  Rows past M
+// are dropped by the y resource (their offsets lie past its end), so the stores need no branches.
+template <int OB, int WM, int WN>
+__device__ __forceinline__ void store_tiles(const TiledArgs& a, const f32x4 (&acc)[WM][WN], int m0, int ct0, int col,
+                                            int q) {
+  const rsrc_t ry = make_rsrc(a.y, (uint32_t)((int64_t)a.M * a.N * 2));
+  u32x4 ex[WM];
+  if constexpr (OB) {
+    const rsrc_t re = make_rsrc(a.rowexp, (uint32_t)a.M * 4u);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) ex[i] = load_b128(re, (uint32_t)(m0 + i * 16 + 4 * q) * 4u, 0u);
+  }
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    if (ct0 + j >= a.CT) continue;
+    const int n = (ct0 + j) * 16 + col;
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + i * 16 + 4 * q + r;
+        const uint32_t off = m < a.M ? (uint32_t)(m * a.N + n) * 2u : kOob;
+        if constexpr (OB) store_b16(ry, to_out<1>(ldexpf(acc[i][j][r], (int)ex[i][r])), off);
+        else store_b16(ry, to_out<0>(acc[i][j][r]), off);
+      }
+  }
+}
+
 // x tile of one chunk in LDS: BM rows x 16 pieces of 16 bytes, no padding, piece c of row r at
 // slot r * 16 + (c ^ (r & 15)).  Sixteen lanes reading the same piece of sixteen consecutive
 // rows (an A operand) then hit sixteen different 16-byte bank groups.  The tile is filled with
@@ -322,21 +352,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     cur = nxt;
   }
 
-#pragma unroll
-  for (int j = 0; j < WN; ++j) {
-    if (ct0 + j >= a.CT) continue;
-    const int n = (ct0 + j) * 16 + col;
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + i * 16 + 4 * q + r;
-        if (m < a.M) {
-          if constexpr (OB) a.y[(int64_t)m * a.N + n] = to_out<1>(ldexpf(acc[i][j][r], a.rowexp[m]));
-          else a.y[(int64_t)m * a.N + n] = to_out<0>(acc[i][j][r]);
-        }
-      }
-  }
+  store_tiles<OB, WM, WN>(a, acc, m0, ct0, col, q);
 }
 
 template <int BITS, int OB, int WM, int WN, int SEG, int NW>
@@ -370,7 +386,7 @@ static hipError_t run_tiled_bits(const TiledArgs& a, int bits, int seg, hipStrea
 }
 
 // Rows are processed in slices small enough that every byte offset inside a slice (x rows of up
-// to 2^20 inputs, y) fits the 32-bit buffer offsets the kernel uses.
+// to 2^20 inputs, y rows of up to 2^20 outputs) fits the 32-bit buffer offsets the kernels use.
 hipError_t launch_tiled(const GemmCall& c) {
   const gptq_layer* L = c.L;
   TiledArgs a;
@@ -394,7 +410,10 @@ hipError_t launch_tiled(const GemmCall& c) {
   segment_divisor(L, &a.gmagic, &a.gshift);
   a.scale_kind = L->scales_dtype;
   a.MB = a.NB = 0;
-  const int64_t slice = ((int64_t(1) << 31) - 1) / (2 * (int64_t)a.ld) / 256 * 256;   // >= 1024 for K <= 2^20
+  // rows per slice: x and y byte offsets inside a slice stay below 2^31 (at least 768 rows, as
+  // K, N <= 2^20)
+  const int64_t lim = ((int64_t(1) << 31) - 1) / (2 * (int64_t)(a.ld > a.N ? a.ld : a.N));
+  const int64_t slice = lim / 256 * 256;
   for (int64_t m0 = 0; m0 < c.M; m0 += slice) {
     a.M = (int)(c.M - m0 < slice ? c.M - m0 : slice);
     a.x = x + m0 * a.ld;
