@@ -238,7 +238,16 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   };
 
   // Chunk kc: packed units and metadata -> registers, then the x chunk -> xs[buf] by LDS DMA.
-  auto issue = [&](int kc, int buf, Stage& st) {
+  // One 1 KB piece (j) of chunk kc's x tile -> xs[buf] by LDS DMA.
+  auto issue_x = [&](int kc, int buf, int j) {
+    // (the offset goes through a local: passed straight from the array, the host pass of this
+    // compiler drops the kernel's launch stub)
+    const uint32_t vo = voff_a[j];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rx, (__attribute__((address_space(3))) void*)(&xs[buf][(wave * A_INST + j) * 1024]), 16, vo,
+        (uint32_t)kc * 256u, 0, 0);
+  };
+  auto issue = [&](int kc, int buf, Stage& st, bool with_x) {
 #pragma unroll
     for (int j = 0; j < WN; ++j)
 #pragma unroll
@@ -253,18 +262,13 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
         st.s32[j][s] = load_b32(rs[j], voff_m, (uint32_t)g * 64u);
       }
     }
+    if (with_x) {
 #pragma unroll
-    for (int j = 0; j < A_INST; ++j) {
-      // (the offset goes through a local: passed straight from the array, the host pass of this
-      // compiler drops the kernel's launch stub)
-      const uint32_t vo = voff_a[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void*)(&xs[buf][(wave * A_INST + j) * 1024]), 16, vo,
-          (uint32_t)kc * 256u, 0, 0);
+      for (int j = 0; j < A_INST; ++j) issue_x(kc, buf, j);
     }
   };
 
-  auto compute = [&](int buf, const Stage& st) {
+  auto compute = [&](int buf, const Stage& st, auto&& hook) {
     u32x4 b[WN][4];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
@@ -281,6 +285,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
       // four scales per chunk: the plain order keeps the wave within four waves per SIMD
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
+        hook(i);
         u32x4 af[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) af[t] = *reinterpret_cast<const u32x4*>(xb + a_off[t] + i * 4096);
@@ -304,6 +309,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     for (int t = 0; t < 4; ++t) afc[t] = *reinterpret_cast<const u32x4*>(xb + a_off[t]);
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
+      hook(i);
       if (i + 1 < WM) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) afn[t] = *reinterpret_cast<const u32x4*>(xb + a_off[t] + (i + 1) * 4096);
@@ -338,14 +344,19 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   };
 
   Stage cur, nxt;
-  issue(0, 0, cur);
+  issue(0, 0, cur, true);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < a.KC; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < a.KC;
-    if (more) issue(it + 1, buf ^ 1, nxt);
-    compute(buf, cur);
+    // the next chunk's units and metadata first; its x tile one 1 KB piece per row block, so the
+    // workgroup's DMA requests do not all queue up at once behind the barrier
+    const int kn = more ? it + 1 : it;
+    issue(kn, buf ^ 1, nxt, false);
+    compute(buf, cur, [&](int i) {
+      if (i < A_INST) issue_x(kn, buf ^ 1, i);
+    });
     // the next chunk's x tile, units and metadata were issued before this chunk's compute
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
