@@ -112,12 +112,67 @@ __global__ void __launch_bounds__(256) prep_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// prep for bf16 activations without a permutation, rows of at most 2048 * PR inputs: workgroup m
+// reads its row once into registers (PR pieces of 8 per thread, all loads in flight together),
+// reduces the row maximum, and writes the rescaled fp16 copy from the registers -- the same
+// values as prep_kernel with to_f16, in one pass over x instead of two.
+template <int PR>
+__global__ void __launch_bounds__(256) prep_f16_row_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xs,
+                                                           int32_t* __restrict__ rowexp, int M, int K, int Kp) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int m = blockIdx.x; m < M; m += gridDim.x) {
+    const uint16_t* xr = x + (int64_t)m * K;
+    u32x4 v[PR];
+#pragma unroll
+    for (int r = 0; r < PR; ++r) {
+      const int j0 = tid * 8 + r * 2048;
+      v[r] = j0 < K ? *reinterpret_cast<const u32x4*>(xr + j0) : u32x4{0u, 0u, 0u, 0u};   // K % 8 == 0
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int r = 0; r < PR; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, v[r][q] << 16)));
+        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, v[r][q] & 0xFFFF0000u)));
+      }
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const int e = (mx > 0.f && mx <= 3.4028235e38f) ? ilogbf(mx) - 14 : 0;
+    if (tid == 0) rowexp[m] = e;
+#pragma unroll
+    for (int r = 0; r < PR; ++r) {
+      const int j0 = tid * 8 + r * 2048;
+      if (j0 < Kp) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = ldexpf(__builtin_bit_cast(float, v[r][q] << 16), -e);
+          const float hi = ldexpf(__builtin_bit_cast(float, v[r][q] & 0xFFFF0000u), -e);
+          w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+        }
+        *reinterpret_cast<u32x4*>(xs + (int64_t)m * Kp + j0) = w;
+      }
+    }
+  }
+}
+
 hipError_t launch_prep(const GemmCall& c, bool to_f16) {
   const gptq_layer* L = c.L;
   uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
   uint16_t* xs = reinterpret_cast<uint16_t*>(base);
   int32_t* rowexp = to_f16 ? reinterpret_cast<int32_t*>(base + ws_xsorted_bytes(L, c.M)) : nullptr;
   const unsigned rows = (unsigned)(c.M < 65535 ? c.M : 65535);
+  if (to_f16 && !L->has_perm && L->Kp <= 2048 * 8) {
+    hipLaunchKernelGGL(prep_f16_row_kernel<8>, dim3(rows), dim3(256), 0, c.stream,
+                       reinterpret_cast<const uint16_t*>(c.x), xs, rowexp, (int)c.M, L->K, L->Kp);
+    return hipGetLastError();
+  }
   const int span = to_f16 ? L->Kp : 2048;     // multiple of 2048 or the whole row
   const unsigned stripes = (unsigned)((L->Kp + span - 1) / span);
   hipLaunchKernelGGL(prep_kernel, dim3(rows, stripes), dim3(256), 0, c.stream, reinterpret_cast<const uint16_t*>(c.x),
