@@ -390,8 +390,13 @@ static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
 // column tiles per wave so that x traffic stays near the weight traffic.
 template <int BITS, int XT>
 static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
-  if (x_fits_lds(a.M, a.Kp))
-    return a.iperm ? run<BITS, XT, 1, 1, 4, 2, 4>(a, seg, s) : run<BITS, XT, 1, 1, 4, 1, 4>(a, seg, s);
+  if (x_fits_lds(a.M, a.Kp)) {
+    if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, 4>(a, seg, s);
+    // M = 1 over 32 chunks: two waves per column tile, each a straight-line 16-chunk range with a
+    // 4-deep ring, measured 3 % faster on MI355X than four waves of 8 chunks (4096-input layers)
+    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16>(a, seg, s);
+    return run<BITS, XT, 1, 1, 4, 1, 4>(a, seg, s);
+  }
   if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
   return hipErrorInvalidValue;   // larger M goes to the mid family
 }
