@@ -233,10 +233,14 @@ skinny_kernel(const SkinnyArgs a) {
       }
     }
   }
+  // With TCH > 0 the waves of neighbouring column tiles walk their K ranges from different
+  // starting chunks, so at any moment they read different offsets within their units.
+  const int rot = TCH > 0 ? (ct0 * 5) & (TCH - 1) : 0;
+  auto chunk_at = [&](int j) { return kc0 + ((j + rot) & (TCH > 0 ? TCH - 1 : 0)); };
   WChunk ring[DEPTH];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j)
-    if (TCH > 0 || kc0 + j < kc1) load_w(kc0 + j, ring[j]);
+    if (TCH > 0 || kc0 + j < kc1) load_w(TCH > 0 ? chunk_at(j) : kc0 + j, ring[j]);
 
   if constexpr (XLDS == 1) {
 #pragma unroll
@@ -280,19 +284,19 @@ skinny_kernel(const SkinnyArgs a) {
   // ---- main loop: compute chunk kc from the ring slot, then refill the slot with kc + DEPTH ---
   XChunk xcur, xnxt;
   if constexpr (!XLDS) {
-    if (kc0 < kc1) load_x_global(kc0, xcur);
+    if (kc0 < kc1) load_x_global(TCH > 0 ? chunk_at(0) : kc0, xcur);
   }
   if constexpr (TCH > 0) {
 #pragma unroll
     for (int j = 0; j < TCH; ++j) {
-      const int kc = kc0 + j;
+      const int kc = chunk_at(j);
       if constexpr (XLDS) {
         load_x_lds(kc, xcur);
       } else {
-        if (j + 1 < TCH) load_x_global(kc + 1, xnxt);
+        if (j + 1 < TCH) load_x_global(chunk_at(j + 1), xnxt);
       }
       compute(ring[j % DEPTH], xcur);
-      if (j + DEPTH < TCH) load_w(kc + DEPTH, ring[j % DEPTH]);
+      if (j + DEPTH < TCH) load_w(chunk_at(j + DEPTH), ring[j % DEPTH]);
       if constexpr (!XLDS) xcur = xnxt;
     }
   } else
