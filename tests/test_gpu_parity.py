@@ -93,6 +93,50 @@ def test_gemm_small_shapes_both_paths(K, N, bits, gs, desc, sdt, xdt):
     h.close()
 
 
+# ---- the kernel variants the dispatcher picks at long K ----------------------------------------
+# 16, 32 and 64 chunks of K select the straight-line skinny variants (four or two waves per column
+# tile, x staged per wave), the x-from-L2 skinny kernel, the split-K mid kernel and both tiled
+# tiles; N = 96 leaves a partial 256-column block on the tiled path.
+
+DISPATCH_MS = [1, 2, 3, 4, 5, 16, 17, 33, 64, 130, 257]
+
+
+@pytest.mark.parametrize("K,bits,desc,xdt", [(2048, 4, False, "f16"), (4096, 4, False, "f16"),
+                                             (4096, 4, False, "bf16"), (4096, 2, False, "f16"),
+                                             (4096, 3, False, "bf16"), (4096, 8, False, "f16"),
+                                             (8192, 4, False, "f16"), (8192, 4, False, "bf16"),
+                                             (4096, 4, True, "f16"), (8192, 3, True, "bf16")])
+def test_gemm_dispatch_variants(K, bits, desc, xdt):
+    import weight_only_quantized_amd as wq
+    N = 96
+    say("dispatch-variants", K, bits, desc, xdt)
+    L = gi.make_layer(K, N, bits, 128, desc_act=desc, scales_dtype="f16", seed=K + 10 * bits + desc)
+    h = repack_layer(L)
+    x = gi.make_x(max(DISPATCH_MS), K, xdt, seed=K * 3 + bits)
+    y_ref_all = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, "f16", L.g_idx, bits)
+    for M in DISPATCH_MS:
+        paths = [wq.PATH_AUTO] + ([wq.PATH_SKINNY] if M <= 64 else [])
+        for p in paths:
+            y = run_gemm(h, x[:M], xdt, path=p)
+            check(y, xdt, y_ref_all[:M], label=(K, bits, desc, xdt, M, p))
+    h.close()
+
+
+def test_bf16_rows_longer_than_the_one_pass_prep():
+    """bf16 rows of more than 16384 inputs take the two-pass prep; 129 chunks is an odd count."""
+    import weight_only_quantized_amd as wq
+    K, N = 16512, 256
+    say("bf16-long-rows", K, N)
+    L = gi.make_layer(K, N, 4, 128, scales_dtype="bf16", seed=5)
+    h = repack_layer(L)
+    x = gi.make_x(257, K, "bf16", seed=6)
+    y_ref_all = o.gemm(x, "bf16", L.qweight, L.qzeros, L.scales, "bf16", L.g_idx, 4)
+    for M in (1, 130, 257):
+        y = run_gemm(h, x[:M], "bf16", path=wq.PATH_TILED)
+        check(y, "bf16", y_ref_all[:M], label=("long-rows", M))
+    h.close()
+
+
 # ---- closed-form special cases: bit-exact ------------------------------------------------------
 
 @pytest.mark.parametrize("bits,xdt", [(4, "f16"), (4, "bf16"), (2, "f16"), (3, "bf16"), (8, "f16"), (8, "bf16")])
