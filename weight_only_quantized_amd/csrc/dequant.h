@@ -111,6 +111,29 @@ __device__ __forceinline__ u32x4 build_b(const uint32_t* w, int t, uint32_t zt) 
   return r;
 }
 
+// B operand of MFMA step t without the zero: 1024 + code (fp16) or 128 + code (bf16, 2/3/4-bit
+// codes), exact; the caller removes (offset + zero) * sum_k x[k] in fp32.
+template <int BITS, int XT>
+__device__ __forceinline__ u32x4 build_b_offset(const uint32_t* w, int t) {
+  u32x4 r;
+  if constexpr (BITS <= 4) {
+    constexpr uint32_t hi = XT == 0 ? 0x64646464u : 0x43434343u;
+    const uint32_t b0 = byte_vector<BITS>(w, 2 * t), b1 = byte_vector<BITS>(w, 2 * t + 1);
+    r[0] = __builtin_amdgcn_perm(hi, b0, 0x04010400u);
+    r[1] = __builtin_amdgcn_perm(hi, b0, 0x04030402u);
+    r[2] = __builtin_amdgcn_perm(hi, b1, 0x04010400u);
+    r[3] = __builtin_amdgcn_perm(hi, b1, 0x04030402u);
+  } else {
+    static_assert(XT == 0, "8-bit codes plus 128 do not fit bf16's significand");
+    const uint32_t w0 = w[2 * t], w1 = w[2 * t + 1];
+    r[0] = (w0 & 0x00FF00FFu) | 0x64006400u;
+    r[1] = ((w0 >> 8) & 0x00FF00FFu) | 0x64006400u;
+    r[2] = (w1 & 0x00FF00FFu) | 0x64006400u;
+    r[3] = ((w1 >> 8) & 0x00FF00FFu) | 0x64006400u;
+  }
+  return r;
+}
+
 // Group scale of a metadata record (see layout.h); s32 holds the f32 bits when kind == 2.
 // (Computed branch-free: a branch here would split the straight-line chunk code.)
 __device__ __forceinline__ float scale_of(uint32_t rec, uint32_t s32, int kind) {

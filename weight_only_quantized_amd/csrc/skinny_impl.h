@@ -58,9 +58,15 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // the inverse permutation, then meets at a barrier.
 // At least two waves per SIMD: the kernel needs about 60-130 VGPRs, and without the hint the
 // compiler spreads a one-wave-per-SIMD schedule over all 512, so a compute unit held one workgroup.
-template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH>
+// ONE (M = 1, whole-chunk segments, x staged per wave, straight-line ranges): the B operand is
+// bias + code with no zero subtraction (build_b_offset), and the term -(bias + zero) * sum_k x[k]
+// of each chunk is applied to the fp32 partial instead; each wave sums its chunks of x once while
+// staging them and keeps the sums in LDS.  Only row 0 of the accumulators is carried.
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH, int ONE = 0>
 __global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) __attribute__((amdgpu_waves_per_eu(2)))
 skinny_kernel(const SkinnyArgs a) {
+  static_assert(!ONE || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
+                "the M = 1 form needs whole-chunk segments, per-wave staging and an exact offset operand");
   constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;  // waves per workgroup
   constexpr int NT = 64 * NWV;
   constexpr int CGS = NWV / KSPLIT;             // column groups per workgroup
@@ -159,6 +165,21 @@ skinny_kernel(const SkinnyArgs a) {
         c.xa[m][t] = *reinterpret_cast<const u32x4*>(&xlds[xbase[m] + kc * kChunkK + 32 * t]);
   };
 
+  // per-chunk sums of x (ONE): TCH floats per wave after the staged rows
+  float* const xsum = reinterpret_cast<float*>(xlds + (XLDS ? (a.M + 1) * xrow : 0)) + wave * TCH;
+  auto compute_one = [&](const WChunk& c, const XChunk& xc, int kc) {
+    if constexpr (ONE) {
+      const float sx = xsum[kc - kc0];
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) tmp = mfma16<XT>(xc.xa[0][t], build_b_offset<BITS, XT>(c.w[i], t), tmp);
+        const float off = (XT == 0 ? 1024.f : 128.f) + (float)(stored_zero_of(c.rec[i][0]) + 1u);
+        acc[0][i][0] += scale_of(c.rec[i][0], c.s32[i][0], a.scale_kind) * (tmp[0] - off * sx);
+      }
+    }
+  };
   auto compute = [&](const WChunk& c, const XChunk& xc) {
     f32x4 c0[MT][NSEG];
 #pragma unroll
@@ -254,6 +275,28 @@ skinny_kernel(const SkinnyArgs a) {
         }
       }
     }
+    if constexpr (ONE) {
+      // piece r of a lane is 8 inputs of chunk kc0 + lane / 16 + 4 r; its 16 lanes add up
+#pragma unroll
+      for (int r = 0; r < XLW; ++r) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = xw[r][e];
+          if constexpr (XT == 0) {
+            p += (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+            p += (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+          } else {
+            p += __builtin_bit_cast(float, w << 16);
+            p += __builtin_bit_cast(float, w & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o);
+        const int ch = lane / 16 + 4 * r;
+        if ((lane & 15) == 0 && ch < TCH) xsum[ch] = p;
+      }
+    }
     // the wave reads back only what it wrote: LDS keeps one wave's accesses in order, the fence
     // keeps the compiler from moving reads above the writes
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -295,7 +338,8 @@ skinny_kernel(const SkinnyArgs a) {
       } else {
         if (j + 1 < TCH) load_x_global(chunk_at(j + 1), xnxt);
       }
-      compute(ring[j % DEPTH], xcur);
+      if constexpr (ONE) compute_one(ring[j % DEPTH], xcur, kc);
+      else compute(ring[j % DEPTH], xcur);
       if (j + DEPTH < TCH) load_w(chunk_at(j + DEPTH), ring[j % DEPTH]);
       if constexpr (!XLDS) xcur = xnxt;
     }
@@ -367,14 +411,15 @@ inline bool x_fits_lds(int64_t M, int Kp) {
 // L2 per chunk (on MI355X faster there than the mid family's split K, slower for longer K).
 inline bool skinny_reads_x_from_l2(int64_t M, int KC) { return M <= 16 && KC <= 32; }
 
-template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH>
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE = 0>
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;
   constexpr int CGS = NWV / KSPLIT;
   const int blocks = (a.CT + TW * CGS - 1) / (TW * CGS);
-  const size_t lds = XLDS ? (size_t)(a.M + 1) * (a.Kp + 8) * 2 : 0;   // staged rows + the zero row
+  // staged rows + the zero row (+ the per-chunk sums of x of every wave, ONE)
+  const size_t lds = (XLDS ? (size_t)(a.M + 1) * (a.Kp + 8) * 2 : 0) + (ONE ? (size_t)NWV * TCH * 4 : 0);
   if (seg == 4)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH>), dim3(blocks), dim3(64 * NWV), lds, s, a);
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE>), dim3(blocks), dim3(64 * NWV), lds, s, a);
   else if constexpr (TCH == 0)
     hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0>), dim3(blocks), dim3(64 * NWV), lds, s, a);
   return hipGetLastError();
@@ -398,7 +443,11 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, 4>(a, seg, s);
     // M = 1 over 32 chunks: two waves per column tile, each a straight-line 16-chunk range with a
     // 4-deep ring, measured 3 % faster on MI355X than four waves of 8 chunks (4096-input layers)
-    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16>(a, seg, s);
+    // the offset operand for bf16 activations (it replaces the bias MFMAs: 4 % on MI355X for the
+    // 8192-input layer); fp16 keeps its exact operands (no gain measured)
+    constexpr int ONE = XT == 1 && BITS <= 4;
+    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16, ONE>(a, seg, s);
+    if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE>(a, seg, s);
     return run<BITS, XT, 1, 1, 4, 1, 4>(a, seg, s);
   }
   if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
