@@ -105,6 +105,7 @@ DISPATCH_MS = [1, 2, 3, 4, 5, 16, 17, 33, 64, 130, 257]
                                              (4096, 4, False, "bf16"), (4096, 2, False, "f16"),
                                              (4096, 3, False, "bf16"), (4096, 8, False, "f16"),
                                              (8192, 4, False, "f16"), (8192, 4, False, "bf16"),
+                                             (4096, 8, False, "bf16"), (8192, 2, False, "bf16"),
                                              (4096, 4, True, "f16"), (8192, 3, True, "bf16")])
 def test_gemm_dispatch_variants(K, bits, desc, xdt):
     import weight_only_quantized_amd as wq
