@@ -17,7 +17,7 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Layer", "make_layer", "make_x", "to_f16_bits", "to_bf16_bits", "WORKLOADS", "seed_for"]
+__all__ = ["Layer", "make_layer", "make_x", "make_bias", "to_f16_bits", "to_bf16_bits", "WORKLOADS", "seed_for"]
 
 
 def to_f16_bits(v) -> np.ndarray:
@@ -86,6 +86,12 @@ def make_x(M, K, dtype="f16", seed=0) -> np.ndarray:
     """Activations x[M, K] ~ N(0, 1), rounded to the activation dtype (bit patterns)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return _round(rng.standard_normal(size=(M, K)), dtype)
+
+
+def make_bias(N, dtype="f16", seed=0) -> np.ndarray:
+    """A layer's bias[N] ~ N(0, 1), rounded to the scales' dtype (bit patterns, or float32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _round(rng.standard_normal(size=N), dtype)
 
 
 def seed_for(workload: int, variant: int = 0) -> int:

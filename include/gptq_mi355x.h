@@ -126,6 +126,17 @@ gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int
 gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, void* y,
                       void* workspace, size_t workspace_bytes, int32_t path, void* stream);
 
+/* y = x . W^T + bias: gptq_gemm with the layer's optional bias vector added ("GPTQ packed
+ * checkpoint (safetensors / torch)", section "GptqLayer": an [out_features] tensor in the same
+ * dtype as the scales, applied at the layer's output).
+ *   bias  [N] device vector in the handle's scales dtype (F16 or BF16: 2-byte aligned; F32:
+ *         4-byte aligned), read only, must not overlap y; NULL makes the call identical to
+ *         gptq_gemm.
+ * The bias is added in fp32 to each output's accumulated sum, before the one rounding to x_dtype.
+ * Everything else (arguments, workspace, errors, graph capture) is as for gptq_gemm. */
+gptq_status gptq_gemm_bias(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, const void* bias, void* y,
+                           void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
 /* Frees the handle's device memory (after synchronising the device).  NULL is accepted. */
 gptq_status gptq_destroy(gptq_handle_t h);
 

@@ -10,7 +10,8 @@ Sources (page title, then section):
          its pack / unpack / as_int32 helpers (the writer and the two's-complement
          wrap).
   [SPEC] "GPTQ packed checkpoint (safetensors / torch)", sections "GptqLayer"
-         (shapes, ceil(in/group) groups), "QuantizeConfig" (bits 2/3/4/8,
+         (shapes, ceil(in/group) groups, the optional [out_features] bias in the
+         scales' dtype), "QuantizeConfig" (bits 2/3/4/8,
          group_size -1 = one group), "Reader" (low bits first along the input
          dimension, the "10 / split / 10" 3-bit loop, +1 on unpacked zeros,
          W = (code - zero) * scale with g = g_idx[k]) and "Reject the file when"
@@ -43,7 +44,7 @@ __all__ = [
     "unpack_along_rows", "unpack_along_cols", "pack_along_rows", "pack_along_cols",
     "unpack_codes", "unpack_zeros", "pack_codes", "pack_zeros",
     "decode_float_bits", "round_to_dtype_bits", "validate_layer",
-    "dequant", "gemm", "gemm_entries", "runtime_perm", "compare", "effective_bits",
+    "dequant", "gemm", "gemm_bias", "gemm_entries", "runtime_perm", "compare", "effective_bits",
 ]
 
 SUPPORTED_BITS = (2, 3, 4, 8)          # [SPEC] QuantizeConfig / GPTQ-001
@@ -274,6 +275,14 @@ def gemm(x_bits, x_dtype: str, qweight, qzeros, scales, scales_dtype: str, g_idx
         W = _dequant_cols(qweight[:, n0:n1], qzeros, scales, scales_dtype, g_idx, bits, zero_cols)
         y[:, n0:n1] = x @ W.T
     return y
+
+
+def gemm_bias(x_bits, x_dtype: str, qweight, qzeros, scales, scales_dtype: str, g_idx, bits: int,
+              bias_bits) -> np.ndarray:
+    """y_ref[m, n] = sum_k x[m, k] * W[n, k] + bias[n] in float64: the layer with its optional
+    bias ([SPEC] GptqLayer: an [out_features] tensor in the same dtype as the scales)."""
+    b = decode_float_bits(bias_bits, scales_dtype)             # [N]
+    return gemm(x_bits, x_dtype, qweight, qzeros, scales, scales_dtype, g_idx, bits) + b[None, :]
 
 
 def _dequant_cols(qweight_cols, qzeros, scales, scales_dtype, g_idx, bits, cols):

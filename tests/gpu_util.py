@@ -38,9 +38,11 @@ def repack_layer(L: gi.Layer, use_gidx=True):
     return h
 
 
-def run_gemm(h, x_bits, x_tag, path=0):
+def run_gemm(h, x_bits, x_tag, path=0, bias=None, bias_tag=None):
+    """One gemm call (gptq_gemm_bias when `bias`, bit patterns in `bias_tag`, is given)."""
     x = bits_to_device(x_bits, x_tag)
-    y = h.gemm(x, path=path)
+    b = bits_to_device(bias, bias_tag) if bias is not None else None
+    y = h.gemm(x, path=path, bias=b)
     import torch
     torch.cuda.synchronize()
     return device_to_bits(y)

@@ -138,6 +138,84 @@ def test_bf16_rows_longer_than_the_one_pass_prep():
     h.close()
 
 
+# ---- the layer's optional bias (gptq_gemm_bias) ---------------------------------------------------
+# Every family adds the bias in its own epilogue: the skinny kernel (x in LDS, the bf16 M = 1 form,
+# x from L2), the mid kernel without and with split K (in-kernel store, reduction kernel), and both
+# tiled tiles.
+
+BIAS_MS = [1, 3, 8, 17, 33, 130, 257]
+
+
+@pytest.mark.parametrize("K,sdt,xdt", [(512, "f16", "f16"), (512, "bf16", "bf16"), (4096, "f16", "bf16"),
+                                       (4096, "bf16", "bf16"), (4096, "f32", "f16"), (8192, "f16", "bf16")])
+def test_gemm_bias_all_families(K, sdt, xdt):
+    import weight_only_quantized_amd as wq
+    N = 96
+    say("gemm-bias", K, sdt, xdt)
+    L = gi.make_layer(K, N, 4, 128, scales_dtype=sdt, seed=K + 3)
+    h = repack_layer(L)
+    bias = gi.make_bias(N, sdt, seed=K + 4)
+    x = gi.make_x(max(BIAS_MS), K, xdt, seed=K + 5)
+    y_ref_all = o.gemm_bias(x, xdt, L.qweight, L.qzeros, L.scales, sdt, L.g_idx, 4, bias)
+    for M in BIAS_MS:
+        paths = [wq.PATH_AUTO] + ([wq.PATH_SKINNY] if M <= 64 else [])
+        for p in paths:
+            y = run_gemm(h, x[:M], xdt, path=p, bias=bias, bias_tag=sdt)
+            check(y, xdt, y_ref_all[:M], label=("bias", K, sdt, xdt, M, p))
+    h.close()
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_bias_on_a_zero_weight(xdt):
+    """W = 0: every output is the bias rounded once to x's dtype.  Bit-exact wherever the operands
+    are exact; the bf16 skinny and mid kernels carry an operand offset removed in fp32, so there the
+    bar is the bf16 tolerance around the same values."""
+    import weight_only_quantized_amd as wq
+    K, N, bits, gs = 4096, 64, 4, 128
+    rng = np.random.default_rng(3)
+    zeros = rng.integers(1, 2 ** bits, size=(K // gs, N))
+    codes = zeros[np.arange(K) // gs]
+    scales = gi.to_f16_bits(np.full((K // gs, N), 0.01))
+    L = gi.Layer(K, N, bits, gs, False, o.pack_codes(codes, bits), o.pack_zeros(zeros, bits), scales, "f16",
+                 (np.arange(K) // gs).astype(np.int32))
+    h = repack_layer(L)
+    bias = gi.make_bias(N, "f16", seed=9)
+    x = gi.make_x(130, K, xdt, seed=10)
+    want = o.round_to_dtype_bits(np.broadcast_to(o.decode_float_bits(bias, "f16"), (130, N)), xdt)
+    for M, p in [(1, wq.PATH_SKINNY), (17, wq.PATH_SKINNY), (64, wq.PATH_SKINNY), (1, wq.PATH_TILED),
+                 (130, wq.PATH_TILED)]:
+        y = run_gemm(h, x[:M], xdt, path=p, bias=bias, bias_tag="f16")
+        if xdt == "f16" or p == wq.PATH_TILED:
+            assert np.array_equal(y, want[:M]), (M, p)
+        else:
+            check(y, xdt, np.broadcast_to(o.decode_float_bits(bias, "f16"), (M, N)), label=(M, p))
+    h.close()
+
+
+def test_bias_null_is_gemm_and_bad_bias_is_rejected():
+    import torch
+    import weight_only_quantized_amd as wq
+    from gpu_util import torch_dtype
+    K, N = 512, 64
+    L = gi.make_layer(K, N, 4, 128, scales_dtype="f16", seed=21)
+    h = repack_layer(L)
+    lib = wq.load_library()
+    x = bits_to_device(gi.make_x(5, K, "f16", seed=22), "f16")
+    y0 = h.gemm(x)
+    y1 = torch.empty_like(y0)
+    st = lib.gptq_gemm_bias(h.ptr, x.data_ptr(), 5, 0, None, y1.data_ptr(), None, 0, 0, None)
+    torch.cuda.synchronize()
+    assert st == 0 and torch.equal(y0, y1)
+    b = torch.zeros(N + 1, dtype=torch.float16, device="cuda")
+    odd = b.data_ptr() + 1                                   # not 2-byte aligned
+    assert lib.gptq_gemm_bias(h.ptr, x.data_ptr(), 5, 0, odd, y1.data_ptr(), None, 0, 0, None) == 1
+    assert lib.gptq_gemm_bias(h.ptr, x.data_ptr(), 5, 0, y1.data_ptr(), y1.data_ptr(), None, 0, 0, None) == 1
+    with pytest.raises(TypeError):
+        h.gemm(x, bias=torch.zeros(N, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    h.close()
+
+
 # ---- closed-form special cases: bit-exact ------------------------------------------------------
 
 @pytest.mark.parametrize("bits,xdt", [(4, "f16"), (4, "bf16"), (2, "f16"), (3, "bf16"), (8, "f16"), (8, "bf16")])

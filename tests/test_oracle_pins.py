@@ -216,6 +216,47 @@ def test_code_equal_zero_gives_zero_output(bits):
     assert np.all(y == 0.0)
 
 
+@pytest.mark.parametrize("sdt", ["f16", "bf16", "f32"])
+def test_bias_on_a_zero_weight_is_the_output(sdt):
+    """code == zero everywhere: W = 0, so every output row is the bias itself, decoded from the
+    scales' dtype ([SPEC] GptqLayer bias)."""
+    rng = np.random.default_rng(11)
+    K, N, gs, bits = 128, 64, 64, 4
+    G = K // gs
+    zeros = rng.integers(1, 2 ** bits, size=(G, N))
+    codes = zeros[np.arange(K) // gs]
+    L = gi.make_layer(K, N, bits, gs, scales_dtype=sdt, seed=4)
+    bias = gi.make_bias(N, sdt, seed=5)
+    y = o.gemm_bias(gi.make_x(3, K, "bf16", seed=6), "bf16", o.pack_codes(codes, bits), o.pack_zeros(zeros, bits),
+                    L.scales, sdt, L.g_idx, bits, bias)
+    want = o.decode_float_bits(bias, sdt)
+    assert np.all(np.isfinite(want)) and np.any(want != 0)
+    assert np.array_equal(y, np.broadcast_to(want, y.shape))
+
+
+@pytest.mark.parametrize("bits,sdt,xdt", [(4, "f16", "f16"), (3, "bf16", "bf16"), (8, "f32", "f16")])
+def test_gemm_bias_matches_exact_rationals(bits, sdt, xdt):
+    rng = np.random.default_rng(17 + bits)
+    K, N, M, gs = 64, 32, 3, 32
+    G = o.num_groups(K, gs)
+    codes = rng.integers(0, 2 ** bits, size=(K, N))
+    zeros = rng.integers(1, 2 ** bits + 1, size=(G, N))
+    scales = gi.make_layer(K, N, bits, gs, scales_dtype=sdt, seed=3).scales
+    g_idx = np.arange(K) // gs
+    x = gi.make_x(M, K, xdt, seed=5)
+    bias = gi.make_bias(N, sdt, seed=8)
+    qw, qz = o.pack_codes(codes, bits), o.pack_zeros(zeros, bits)
+    y = o.gemm_bias(x, xdt, qw, qz, scales, sdt, g_idx, bits, bias)
+    ye = _exact_y(x, xdt, codes, zeros, scales, sdt, g_idx)
+    b = o.decode_float_bits(bias, sdt)
+    W = o.dequant(qw, qz, scales, sdt, g_idx, bits)
+    bound = 1e-13 * (np.abs(o.decode_float_bits(x, xdt)) @ np.abs(W.T) + np.abs(b)[None, :])
+    for m in range(M):
+        for n in range(N):
+            exact = ye[m][n] + Fraction(float(b[n]))
+            assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(float(bound[m, n])) + Fraction(1, 10 ** 30)
+
+
 @pytest.mark.parametrize("bits,p", [(2, 3), (4, 5), (8, 1), (3, 0)])
 def test_identity_weight_gives_scaled_x(bits, p):
     K = N = 64

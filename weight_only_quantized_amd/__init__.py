@@ -25,7 +25,7 @@ FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2}
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
 # Every symbol include/gptq_mi355x.h declares.
-symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_destroy",
+symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
            "gptq_info", "gptq_decode_runtime", "gptq_status_str", "gptq_last_hip_error"]
 
 
@@ -73,14 +73,15 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_repack.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, ctypes.POINTER(P)]
     lib.gptq_workspace_size.argtypes = [P, I64, I32, I32, ctypes.POINTER(SZ)]
     lib.gptq_gemm.argtypes = [P, P, I64, I32, P, P, SZ, I32, P]
+    lib.gptq_gemm_bias.argtypes = [P, P, I64, I32, P, P, P, SZ, I32, P]
     lib.gptq_destroy.argtypes = [P]
     lib.gptq_info.argtypes = [P, ctypes.POINTER(Info)]
     lib.gptq_decode_runtime.argtypes = [P, P, P, P, P]
     lib.gptq_status_str.argtypes = [I32]
     lib.gptq_status_str.restype = ctypes.c_char_p
     lib.gptq_last_hip_error.argtypes = []
-    for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_destroy", "gptq_info",
-              "gptq_decode_runtime", "gptq_last_hip_error"):
+    for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
+              "gptq_info", "gptq_decode_runtime", "gptq_last_hip_error"):
         getattr(lib, f).restype = I32
     _lib = lib
     return lib
@@ -157,9 +158,10 @@ class Handle:
             raise GPTQError(st, "gptq_workspace_size", self._lib)
         return n.value
 
-    def gemm(self, x, out=None, workspace=None, path=PATH_AUTO, stream=None):
-        """y = x . W^T; x [M, K] fp16/bf16 on this handle's GPU.  `workspace` (uint8 tensor) is
-        allocated from torch's caching allocator when not given."""
+    def gemm(self, x, out=None, workspace=None, path=PATH_AUTO, stream=None, bias=None):
+        """y = x . W^T (+ bias); x [M, K] fp16/bf16 on this handle's GPU; bias, when given, an [N]
+        tensor in the scales' dtype (gptq_gemm_bias).  `workspace` (uint8 tensor) is allocated from
+        torch's caching allocator when not given."""
         import torch
         if x.dim() != 2 or x.shape[1] != self.K:
             raise ValueError(f"x must be [M, {self.K}]")
@@ -174,10 +176,20 @@ class Handle:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        st = self._lib.gptq_gemm(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), out.data_ptr(), ws_ptr, ws_n,
-                                 path, _stream_ptr(stream))
+        if bias is None:
+            st = self._lib.gptq_gemm(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), out.data_ptr(), ws_ptr, ws_n,
+                                     path, _stream_ptr(stream))
+            if st:
+                raise GPTQError(st, "gptq_gemm", self._lib)
+            return out
+        if bias.dim() != 1 or bias.shape[0] != self.N or not bias.is_contiguous():
+            raise ValueError(f"bias must be a contiguous [{self.N}] tensor")
+        if _dtype_code(bias.dtype) != self.info()["scales_dtype"]:
+            raise TypeError("bias must have the scales' dtype")
+        st = self._lib.gptq_gemm_bias(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), bias.data_ptr(), out.data_ptr(),
+                                      ws_ptr, ws_n, path, _stream_ptr(stream))
         if st:
-            raise GPTQError(st, "gptq_gemm", self._lib)
+            raise GPTQError(st, "gptq_gemm_bias", self._lib)
         return out
 
     def decode(self) -> dict:

@@ -245,8 +245,8 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, void* y,
-                      void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+static gptq_status gemm_impl(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, const void* bias, void* y,
+                             void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
   gptq_status st = check_handle(h);
   if (st != GPTQ_OK) return st;
   if (M < 0 || M > (int64_t(1) << 24)) return GPTQ_E_INVALID_ARG;
@@ -258,6 +258,10 @@ gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype
   if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return GPTQ_E_INVALID_ARG;
   const size_t xb = (size_t)M * h->K * 2, yb = (size_t)M * h->N * 2;
   if (overlaps(x, xb, y, yb)) return GPTQ_E_INVALID_ARG;
+  if (bias) {
+    const size_t be = h->scales_dtype == GPTQ_F32 ? 4 : 2;
+    if (!aligned(bias, be) || overlaps(bias, (size_t)h->N * be, y, yb)) return GPTQ_E_INVALID_ARG;
+  }
   size_t need = 0;
   st = gptq_workspace_size(h, M, x_dtype, path, &need);
   if (st != GPTQ_OK) return st;
@@ -270,10 +274,20 @@ gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype
   if (e != hipSuccess) return hip_fail(e);
   if (dev != h->device) return GPTQ_E_DEVICE;
 
-  GemmCall c{h, x, M, x_dtype == GPTQ_BF16 ? 1 : 0, y, workspace, workspace_bytes, (hipStream_t)stream};
+  GemmCall c{h, x, M, x_dtype == GPTQ_BF16 ? 1 : 0, y, workspace, workspace_bytes, (hipStream_t)stream, bias};
   e = path == GPTQ_PATH_SKINNY ? launch_skinny(c) : launch_tiled(c);
   if (e != hipSuccess) return hip_fail(e);
   return GPTQ_OK;
+}
+
+gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, void* y,
+                      void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  return gemm_impl(h, x, M, x_dtype, nullptr, y, workspace, workspace_bytes, path, stream);
+}
+
+gptq_status gptq_gemm_bias(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, const void* bias, void* y,
+                           void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  return gemm_impl(h, x, M, x_dtype, bias, y, workspace, workspace_bytes, path, stream);
 }
 
 gptq_status gptq_destroy(gptq_handle_t h) {

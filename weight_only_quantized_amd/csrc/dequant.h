@@ -144,6 +144,15 @@ __device__ __forceinline__ float scale_of(uint32_t rec, uint32_t s32, int kind) 
 }
 __device__ __forceinline__ uint32_t stored_zero_of(uint32_t rec) { return rec >> 16; }
 
+// Element n of an optional bias vector ("GPTQ packed checkpoint (safetensors / torch)", section
+// "GptqLayer": same dtype as the scales), as fp32; 0 without one.  kind: 0 fp16, 1 bf16, 2 f32.
+__device__ __forceinline__ float bias_at(const void* bias, int kind, int n) {
+  if (!bias) return 0.f;
+  if (kind == 2) return reinterpret_cast<const float*>(bias)[n];
+  const uint16_t h = reinterpret_cast<const uint16_t*>(bias)[n];
+  return kind == 0 ? (float)__builtin_bit_cast(_Float16, h) : __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
 template <int XT>
 __device__ __forceinline__ uint16_t to_out(float v) {
   if constexpr (XT == 0) return __builtin_bit_cast(uint16_t, (_Float16)v);

@@ -43,6 +43,7 @@ struct GemmCall {
   void* ws;           // workspace base (256-B aligned) or NULL
   size_t ws_bytes;
   hipStream_t stream;
+  const void* bias;   // [N] in the scales' dtype, or NULL
 };
 
 // Workspace layout helpers (tiled.hip): sizes in bytes, 256-B aligned parts.

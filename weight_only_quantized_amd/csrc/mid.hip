@@ -20,15 +20,21 @@ size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M) {
   return p.KS > 1 ? align256m((size_t)p.KS * rows * L->N * 4) : 0;
 }
 
-// y[m, n] = round(sum over slices s in order of part[s, m, n]); four outputs per thread.  Slices
-// are read eight at a time, all eight loads in flight together (indices past KS re-read the
-// last slice and are masked out of the sum).
+// y[m, n] = round(sum over slices s in order of part[s, m, n] + bias[n]); four outputs per
+// thread.  Slices are read eight at a time, all eight loads in flight together (indices past KS
+// re-read the last slice and are masked out of the sum).
 template <int XT>
 __global__ void __launch_bounds__(256) mid_reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ y,
-                                                         int64_t mn4, int64_t mn, int KS) {
+                                                         int64_t mn4, int64_t mn, int KS, int N, const void* bias,
+                                                         int bias_kind) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= mn4) return;
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (bias) {
+    const int n0 = (int)((4 * i) % N);          // N % 4 == 0: the four outputs share a row
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = bias_at(bias, bias_kind, n0 + e);
+  }
   for (int k0 = 0; k0 < KS; k0 += 8) {
     f32x4 v[8];
 #pragma unroll
@@ -58,6 +64,7 @@ static hipError_t mid_pass(const GemmCall& c, const uint16_t* x, int ld, float* 
   a.scale_kind = L->scales_dtype;
   segment_divisor(L, &a.gmagic, &a.gshift);
   a.cpw = p.cpw;
+  a.bias = c.bias;
   hipError_t e;
   switch (L->bits) {
     case 2: e = mid_b2(a, p, c.x_bf16, L->seg_steps, c.stream); break;
@@ -69,9 +76,11 @@ static hipError_t mid_pass(const GemmCall& c, const uint16_t* x, int ld, float* 
   const int64_t mn = rows * (int64_t)L->N, mn4 = mn / 4;     // N is a multiple of 32
   const unsigned blocks = (unsigned)((mn4 + 255) / 256);
   if (c.x_bf16)
-    hipLaunchKernelGGL(mid_reduce_kernel<1>, dim3(blocks), dim3(256), 0, c.stream, a.part, a.y, mn4, mn, p.KS);
+    hipLaunchKernelGGL(mid_reduce_kernel<1>, dim3(blocks), dim3(256), 0, c.stream, a.part, a.y, mn4, mn, p.KS,
+                       L->N, c.bias, L->scales_dtype);
   else
-    hipLaunchKernelGGL(mid_reduce_kernel<0>, dim3(blocks), dim3(256), 0, c.stream, a.part, a.y, mn4, mn, p.KS);
+    hipLaunchKernelGGL(mid_reduce_kernel<0>, dim3(blocks), dim3(256), 0, c.stream, a.part, a.y, mn4, mn, p.KS,
+                       L->N, c.bias, L->scales_dtype);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ struct MidArgs {
   uint32_t gmagic;       // segment -> group map (segment_divisor)
   int gshift;
   int cpw;                // chunks per K slice (TCH)
+  const void* bias;       // [N] in the scales' dtype (scale_kind), or NULL; added when KS == 1
 };
 
 // Group of segment `si` (a chunk, or a 32-input step); wave-uniform.
@@ -191,13 +192,14 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   for (int j = 0; j < WN; ++j) {
     if (ct0 + j >= a.CT) continue;
     const int n = (ct0 + j) * 16 + col;
+    const float bn = whole ? bias_at(a.bias, a.scale_kind, n) : 0.f;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m * 16 + 4 * q + r;
         if (row >= a.M) continue;
-        if (whole) a.y[(int64_t)row * a.N + n] = to_out<XT>(acc[m][j][r]);
+        if (whole) a.y[(int64_t)row * a.N + n] = to_out<XT>(acc[m][j][r] + bn);
         else a.part[((int64_t)ks * a.M + row) * a.N + n] = acc[m][j][r];
       }
   }

@@ -18,6 +18,7 @@ hipError_t launch_skinny(const GemmCall& c) {
   a.M = (int)c.M; a.K = L->K; a.Kp = L->Kp; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
   segment_divisor(L, &a.gmagic, &a.gshift);
   a.scale_kind = L->scales_dtype;
+  a.bias = c.bias;
   a.iperm = nullptr;
   if (skinny_needs_xsorted(L, c.M)) {
     hipError_t e = launch_prep(c, false);

@@ -35,6 +35,7 @@ struct SkinnyArgs {
   int M, K, Kp, N, KC, CT, G, scale_kind;
   uint32_t gmagic;        // segment -> group map (segment_divisor): min(segment / d, G - 1)
   int gshift;
+  const void* bias;       // [N] in the scales' dtype (scale_kind), or NULL
 };
 
 // Group of segment `si` (a chunk index when segments are chunks, a 32-input step index when they
@@ -384,12 +385,13 @@ skinny_kernel(const SkinnyArgs a) {
   for (int i = 0; i < TW; ++i) {
     if (ct0 + i >= a.CT) continue;
     const int n = (ct0 + i) * 16 + col;
+    const float bn = bias_at(a.bias, a.scale_kind, n);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m * 16 + 4 * q + r;
-        if (row < a.M) a.y[(int64_t)row * a.N + n] = to_out<XT>(acc[m][i][r]);
+        if (row < a.M) a.y[(int64_t)row * a.N + n] = to_out<XT>(acc[m][i][r] + bn);
       }
   }
 }

@@ -194,6 +194,7 @@ struct TiledArgs {
   int M, K, N, KC, CT, G, scale_kind, MB, NB;
   uint32_t gmagic;       // segment -> group map (see segment_divisor)
   int gshift;
+  const void* bias;      // [N] in the scales' dtype (scale_kind), or NULL
 };
 
 // Writes a wave's WM x WN accumulator tiles (rows m0 + 16 i + 4 q + r, column tile ct0 + j, lane
@@ -214,14 +215,15 @@ __device__ __forceinline__ void store_tiles(const TiledArgs& a, const f32x4 (&ac
   for (int j = 0; j < WN; ++j) {
     if (ct0 + j >= a.CT) continue;
     const int n = (ct0 + j) * 16 + col;
+    const float bn = bias_at(a.bias, a.scale_kind, n);
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + i * 16 + 4 * q + r;
         const uint32_t off = m < a.M ? (uint32_t)(m * a.N + n) * 2u : kOob;
-        if constexpr (OB) store_b16(ry, to_out<1>(ldexpf(acc[i][j][r], (int)ex[i][r])), off);
-        else store_b16(ry, to_out<0>(acc[i][j][r]), off);
+        if constexpr (OB) store_b16(ry, to_out<1>(ldexpf(acc[i][j][r], (int)ex[i][r]) + bn), off);
+        else store_b16(ry, to_out<0>(acc[i][j][r] + bn), off);
       }
   }
 }
@@ -477,6 +479,7 @@ hipError_t launch_tiled(const GemmCall& c) {
   a.K = L->K; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
   segment_divisor(L, &a.gmagic, &a.gshift);
   a.scale_kind = L->scales_dtype;
+  a.bias = c.bias;
   a.MB = a.NB = 0;
   // rows per slice: x and y byte offsets inside a slice stay below 2^31 (at least 768 rows, as
   // K, N <= 2^20)
