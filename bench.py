@@ -79,9 +79,9 @@ def stored_traffic(kernel_key):
 
 
 class Workload:
-    def __init__(self, name, K, N, M, bits, gs, desc_act, sdt, xdt, seed):
+    def __init__(self, name, K, N, M, bits, gs, desc_act, sdt, xdt, seed, bias=False):
         self.name, self.K, self.N, self.M, self.bits, self.gs = name, K, N, M, bits, gs
-        self.desc_act, self.sdt, self.xdt, self.seed = desc_act, sdt, xdt, seed
+        self.desc_act, self.sdt, self.xdt, self.seed, self.bias = desc_act, sdt, xdt, seed, bias
 
     def label(self):
         g = "g-1" if self.gs == -1 else f"g{self.gs}"
@@ -127,10 +127,18 @@ def time_calls(w: Workload, steps: int, warmup: int, copies=None, graph=False):
     sp = stream.cuda_stream
     xcode = 0 if w.xdt == "f16" else 1
     args = [(hs[i % R].ptr, xs[i % len(xs)].data_ptr(), ys[i % len(ys)].data_ptr()) for i in range(R * len(xs))]
+    bias = None
+    if w.bias:   # the layer's [N] bias in the scales' dtype, through gptq_gemm_bias
+        bb = gi.make_bias(w.N, w.sdt, seed=w.seed + 2)
+        bias = (torch.from_numpy(np.ascontiguousarray(bb, dtype=np.float32)) if w.sdt == "f32" else
+                torch.from_numpy(bb.view(np.int16).copy())).to(dev)
 
     def call(i):
         h, x, y = args[i % len(args)]
-        st = lib.gptq_gemm(h, x, w.M, xcode, y, ws.data_ptr(), ws.numel(), 0, sp)
+        if bias is None:
+            st = lib.gptq_gemm(h, x, w.M, xcode, y, ws.data_ptr(), ws.numel(), 0, sp)
+        else:
+            st = lib.gptq_gemm_bias(h, x, w.M, xcode, bias.data_ptr(), y, ws.data_ptr(), ws.numel(), 0, sp)
         if st:
             raise wq.GPTQError(st, "gptq_gemm", lib)
 
@@ -208,6 +216,11 @@ def extra_workloads():
                                     gi.seed_for(3, bits)))
     out.append(Workload("prefill_4096x8192x28672", 8192, 28672, 4096, 4, 128, False, "bf16", "bf16",
                         gi.seed_for(4)))
+    # the same layers with their bias (gptq_gemm_bias)
+    out.append(Workload("bias_llama3_8b_up_proj", 4096, 14336, 1, 4, 128, False, "f16", "f16", gi.seed_for(1),
+                        bias=True))
+    out.append(Workload("bias_prefill_4096x8192x28672", 8192, 28672, 4096, 4, 128, False, "bf16", "bf16",
+                        gi.seed_for(4), bias=True))
     return out
 
 
@@ -261,7 +274,7 @@ def main():
             steps = args.steps if e.M < 1024 else max(3, args.steps // 200)
             eus, eR = time_calls(e, steps, min(args.warmup, steps), graph=args.graph)
             rec = {"workload": e.label(), "us_per_call": round(eus, 3), "copies": eR}
-            b = algorithmic_bytes(e.K, e.N, e.M, e.bits, e.gs, e.desc_act, scale_bytes=2)
+            b = algorithmic_bytes(e.K, e.N, e.M, e.bits, e.gs, e.desc_act, scale_bytes=2) + (2 * e.N if e.bias else 0)
             rec["algorithmic_bytes"] = b
             rec["TB_per_s"] = round(b / (eus * 1e-6) / 1e12, 3)
             rec["frac_hbm"] = round(b / (eus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
