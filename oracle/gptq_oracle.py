@@ -22,6 +22,11 @@ Sources (page title, then section):
          error from output-rounding error).
   [FK]   "Formats and kernels: FP8, INT8, INT4, Marlin, Machete", opening section
          (effective bits b_eff = bits + 16 / group_size with fp16 scales).
+  [AWQ]  "39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes", section
+         "AWQ", its checkpoint part: AutoAWQ GEMM tensors qweight [in, out / 8] and
+         qzeros [groups, out / 8] pack eight 4-bit fields along the OUTPUT dimension in
+         the interleaved order 0 2 4 6 1 3 5 7 (output 1's field in bits 16-19), zeros
+         are stored as they are (offset = -zero * scale), scales [groups, out].
 
 Readings where the pages are silent or ambiguous (each is listed in the design doc):
   * v1 zeros: the writer stores (z - 1) & mask, the reader adds 1 with no mask,
@@ -45,6 +50,7 @@ __all__ = [
     "unpack_codes", "unpack_zeros", "pack_codes", "pack_zeros",
     "decode_float_bits", "round_to_dtype_bits", "validate_layer",
     "dequant", "gemm", "gemm_bias", "gemm_entries", "runtime_perm", "compare", "effective_bits",
+    "AWQ_ORDER", "unpack_awq", "pack_awq", "dequant_awq", "gemm_awq",
 ]
 
 SUPPORTED_BITS = (2, 3, 4, 8)          # [SPEC] QuantizeConfig / GPTQ-001
@@ -304,6 +310,58 @@ def gemm_entries(x_bits, x_dtype, qweight, qzeros, scales, scales_dtype, g_idx, 
         W[n] = _dequant_cols(np.asarray(qweight)[:, n:n + 1], qzeros, scales, scales_dtype,
                              g_idx, bits, slice(n, n + 1))[0]
     return np.array([x[row_pos[r]] @ W[c] for r, c in zip(rows, cols)], dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# AWQ GEMM checkpoints: the same W = (code - zero) * scale from another packing
+# ----------------------------------------------------------------------------------------------
+
+AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)   # [AWQ] field j of a word holds output 8 w + AWQ_ORDER[j]
+
+
+def _awq_shifts() -> np.ndarray:
+    """Bit offset of output column c % 8 inside its word: 4 * (position of c % 8 in AWQ_ORDER)."""
+    pos = np.empty(8, dtype=np.uint32)
+    pos[list(AWQ_ORDER)] = np.arange(8, dtype=np.uint32)
+    return 4 * pos
+
+
+def unpack_awq(words) -> np.ndarray:
+    """int32 [rows, cols / 8] -> uint8 codes [rows, cols]: column c is the 4-bit field at bit
+    4 * pos(c % 8) of word c // 8 ([AWQ])."""
+    u = to_u32(words)
+    cols = u.shape[1] * 8
+    sh = np.tile(_awq_shifts(), u.shape[1])                   # [cols]
+    return ((u[:, np.arange(cols) // 8] >> sh[None, :]) & 0xF).astype(np.uint8)
+
+
+def pack_awq(codes) -> np.ndarray:
+    """Inverse of unpack_awq (used by the generators and pins only)."""
+    c = np.asarray(codes, dtype=np.uint32)
+    rows, cols = c.shape
+    assert cols % 8 == 0 and c.max(initial=0) < 16
+    sh = np.tile(_awq_shifts(), cols // 8)
+    words = np.zeros((rows, cols // 8), dtype=np.uint32)
+    for c8 in range(8):                                        # one field position at a time
+        words |= c[:, c8::8] << sh[c8]
+    return to_i32(words)
+
+
+def dequant_awq(qweight, qzeros, scales, scales_dtype: str, group_size: int) -> np.ndarray:
+    """W[n, k] = (code[k, n] - zero[g, n]) * scale[g, n], g = k // group_size, zeros used as
+    stored ([AWQ]: offset = -zero * scale), in float64 (exact)."""
+    code = unpack_awq(qweight).astype(np.float64)              # [K, N]
+    zero = unpack_awq(qzeros).astype(np.float64)               # [G, N]
+    s = decode_float_bits(scales, scales_dtype)                # [G, N]
+    K = code.shape[0]
+    g = np.arange(K) // (K if group_size == -1 else group_size)
+    return ((code - zero[g]) * s[g]).T.copy()                  # [N, K]
+
+
+def gemm_awq(x_bits, x_dtype: str, qweight, qzeros, scales, scales_dtype: str, group_size: int) -> np.ndarray:
+    """y_ref = x . W^T for an AWQ GEMM layer, float64."""
+    x = decode_float_bits(x_bits, x_dtype)
+    return x @ dequant_awq(qweight, qzeros, scales, scales_dtype, group_size).T
 
 
 def runtime_perm(g_idx) -> np.ndarray:

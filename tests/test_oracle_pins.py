@@ -355,3 +355,59 @@ def test_compare_metrics():
     y = o.round_to_dtype_bits(ref * 1.0009765625, "f16")          # each value off by one part in 1024
     m = o.compare(y, "f16", ref)
     assert abs(m["rel_l2"] - 2.0 ** -10) < 1e-12 and abs(m["max_abs"] - 4.0 * 2.0 ** -10) < 1e-12
+
+
+# ---- AWQ GEMM checkpoints (a second packing of the same W) ---------------------------------------
+
+def test_awq_words_unpack_to_stated_codes():
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "awq_words.json")))
+    for case in g["cases"]:
+        w = np.array([[int(case["word_hex"], 16)]], dtype=np.uint64)
+        assert o.unpack_awq(o.to_i32(w)).tolist() == [case["codes"]], case
+        assert o.to_u32(o.pack_awq(np.array([case["codes"]]))).tolist() == [[int(case["word_hex"], 16)]]
+
+
+def test_awq_single_hot_and_round_trip():
+    for col in range(16):
+        for v in (1, 7, 15):
+            c = np.zeros((1, 16), dtype=np.uint8)
+            c[0, col] = v
+            w = o.to_u32(o.pack_awq(c))
+            assert np.count_nonzero(w) == 1 and w[0, col // 8] == v << int(4 * o.AWQ_ORDER.index(col % 8))
+    rng = np.random.default_rng(2)
+    words = rng.integers(0, 2 ** 32, size=(5, 6), dtype=np.uint64)
+    assert np.array_equal(o.to_u32(o.pack_awq(o.unpack_awq(o.to_i32(words)))), words.astype(np.uint32))
+
+
+def test_awq_dequant_matches_exact_rationals_and_zero_is_representable():
+    rng = np.random.default_rng(3)
+    K, N, gs = 64, 16, 32
+    codes = rng.integers(0, 16, size=(K, N))
+    zeros = rng.integers(0, 16, size=(K // gs, N))
+    zeros[0, :4] = 0                                            # AWQ stores zeros as they are
+    scales = gi.to_f16_bits(rng.uniform(0.005, 0.02, size=(K // gs, N)))
+    W = o.dequant_awq(o.pack_awq(codes), o.pack_awq(zeros), scales, "f16", gs)
+    s = o.decode_float_bits(scales, "f16")
+    for n in range(N):
+        for k in range(0, K, 3):
+            g = k // gs
+            assert Fraction(float(W[n, k])) == (int(codes[k, n]) - int(zeros[g, n])) * Fraction(float(s[g, n]))
+    assert np.array_equal(W[:4, :gs], (codes[:gs, :4] * s[0, :4]).T)
+
+
+def test_awq_layer_equals_the_gptq_layer_of_the_same_codes():
+    """Logical codes and zeros (1..15) packed both ways give the same W and y."""
+    rng = np.random.default_rng(4)
+    K, N, gs = 256, 32, 64
+    codes = rng.integers(0, 16, size=(K, N))
+    zeros = rng.integers(1, 16, size=(K // gs, N))
+    scales = gi.to_f16_bits(rng.uniform(0.005, 0.02, size=(K // gs, N)))
+    g_idx = (np.arange(K) // gs).astype(np.int32)
+    Wa = o.dequant_awq(o.pack_awq(codes), o.pack_awq(zeros), scales, "f16", gs)
+    Wg = o.dequant(o.pack_codes(codes, 4), o.pack_zeros(zeros, 4), scales, "f16", g_idx, 4)
+    assert np.array_equal(Wa, Wg)
+    x = gi.make_x(3, K, "bf16", seed=5)
+    ya = o.gemm_awq(x, "bf16", o.pack_awq(codes), o.pack_awq(zeros), scales, "f16", gs)
+    yg = o.gemm(x, "bf16", o.pack_codes(codes, 4), o.pack_zeros(zeros, 4), scales, "f16", g_idx, 4)
+    assert np.allclose(ya, yg, rtol=1e-13, atol=1e-13)
