@@ -17,7 +17,8 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Layer", "make_layer", "make_x", "make_bias", "to_f16_bits", "to_bf16_bits", "WORKLOADS", "seed_for"]
+__all__ = ["Layer", "AwqLayer", "make_layer", "make_awq_layer", "make_x", "make_bias", "to_f16_bits",
+           "to_bf16_bits", "WORKLOADS", "seed_for"]
 
 
 def to_f16_bits(v) -> np.ndarray:
@@ -80,6 +81,35 @@ def make_layer(K, N, bits, group_size, desc_act=False, scales_dtype="f16", seed=
     else:
         g_idx = (np.arange(K) // gs).astype(np.int32)
     return Layer(K, N, bits, group_size, bool(desc_act), qweight, qzeros, scales, scales_dtype, g_idx)
+
+
+@dataclasses.dataclass
+class AwqLayer:
+    K: int
+    N: int
+    group_size: int
+    qweight: np.ndarray      # int32 [K, N/8]  (AutoAWQ GEMM: eight 4-bit fields along the outputs)
+    qzeros: np.ndarray       # int32 [G, N/8]
+    scales: np.ndarray       # uint16 bits (f16/bf16) or float32, [G, N]
+    scales_dtype: str
+    bits: int = 4
+
+    @property
+    def G(self) -> int:
+        return self.scales.shape[0]
+
+
+def make_awq_layer(K, N, group_size, scales_dtype="f16", seed=0, scale_lo=0.005, scale_hi=0.02) -> AwqLayer:
+    """Draw one 4-bit AutoAWQ GEMM layer: uniform qweight words [K, N/8], uniform qzeros words
+    [G, N/8] (so every code and zero is uniform over [0, 15] whatever the field order), then
+    scales ~ U[scale_lo, scale_hi) rounded to scales_dtype."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    gs = K if group_size == -1 else group_size
+    G = -(-K // gs)
+    qweight = rng.integers(0, 2 ** 32, size=(K, N // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    qzeros = rng.integers(0, 2 ** 32, size=(G, N // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    scales = _round(rng.uniform(scale_lo, scale_hi, size=(G, N)), scales_dtype)
+    return AwqLayer(K, N, group_size, qweight, qzeros, scales, scales_dtype)
 
 
 def make_x(M, K, dtype="f16", seed=0) -> np.ndarray:

@@ -44,7 +44,8 @@ typedef enum {
                              in_features or out_features not a multiple of 32 */
   GPTQ_E_GIDX = 3,        /* rule GPTQ-004: g_idx length wrong or an index outside [0, G) */
   GPTQ_E_UNSUPPORTED = 4, /* rule GPTQ-001 (bits not 2/3/4/8), GPTQ-005 (a private layout such as
-                             marlin), group_size not -1 and not a positive multiple of 32, or a
+                             marlin), an AWQ_GEMM layer that is not 4-bit or sets desc_act,
+                             group_size not -1 and not a positive multiple of 32, or a
                              g_idx whose groups are not whole (its stable sort is not j // gs) */
   GPTQ_E_HIP = 5,         /* a HIP runtime call failed (see gptq_last_hip_error) */
   GPTQ_E_OOM = 6,         /* device allocation for the runtime layout failed */
@@ -54,10 +55,21 @@ typedef enum {
 
 typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype;
 
-/* Checkpoint formats.  Only GPTQ_FORMAT_GPTQ (AutoGPTQ "cuda" pack, v1 stored-minus-one zeros)
- * is accepted; the others are named so that callers can pass what the checkpoint declares and be
- * refused with GPTQ_E_UNSUPPORTED (rule GPTQ-005). */
-typedef enum { GPTQ_FORMAT_GPTQ = 0, GPTQ_FORMAT_MARLIN = 1, GPTQ_FORMAT_GPTQ_V2 = 2 } gptq_format;
+/* Checkpoint formats.  GPTQ_FORMAT_GPTQ (AutoGPTQ "cuda" pack, v1 stored-minus-one zeros) and
+ * GPTQ_FORMAT_AWQ_GEMM are accepted and repack into the same runtime layout; MARLIN and GPTQ_V2
+ * are named so that callers can pass what the checkpoint declares and be refused with
+ * GPTQ_E_UNSUPPORTED (rule GPTQ-005). */
+typedef enum {
+  GPTQ_FORMAT_GPTQ = 0,
+  GPTQ_FORMAT_MARLIN = 1,
+  GPTQ_FORMAT_GPTQ_V2 = 2,
+  /* AutoAWQ GEMM tensors ("39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes",
+   * section "AWQ"): 4-bit only; qweight int32 [K, N/8] and qzeros int32 [G, N/8] hold eight
+   * fields along the OUTPUT dimension in the order 0 2 4 6 1 3 5 7 (field j of word w is output
+   * 8w + order[j]); zeros are stored as they are (no "minus one"); scales [G, N]; sequential
+   * groups g = k / group_size, so no g_idx.  Same W = (code - zero) * scale, same runtime layout. */
+  GPTQ_FORMAT_AWQ_GEMM = 3
+} gptq_format;
 
 /* Kernel family for gptq_gemm.  AUTO picks SKINNY for M <= 64 and TILED otherwise.  Forcing a
  * family is for tests; a forced family that cannot run the given M returns GPTQ_E_INVALID_ARG. */
@@ -70,14 +82,17 @@ typedef struct {
   int32_t out_features;      /* N                                                              */
   int32_t bits;              /* 2, 3, 4 or 8 (GPTQ-001)                                        */
   int32_t group_size;        /* -1 = one group over all K, else a positive multiple of 32      */
-  int32_t desc_act;          /* informational; act-order is taken from g_idx itself            */
+  int32_t desc_act;          /* informational; act-order is taken from g_idx itself (must be 0
+                                for AWQ_GEMM, which has no g_idx)                              */
   int32_t checkpoint_format; /* gptq_format                                                    */
   int32_t scales_dtype;      /* gptq_dtype of `scales`: F16, BF16 or F32                        */
   int32_t reserved;          /* must be 0                                                      */
-  int64_t qweight_shape[2];  /* must be [K / 32 * bits, N]                                     */
-  int64_t qzeros_shape[2];   /* must be [G, N / 32 * bits], G = ceil(K / group_size)           */
+  int64_t qweight_shape[2];  /* must be [K / 32 * bits, N] ([K, N / 8] for AWQ_GEMM)           */
+  int64_t qzeros_shape[2];   /* must be [G, N / 32 * bits], G = ceil(K / group_size)
+                                ([G, N / 8] for AWQ_GEMM)                                      */
   int64_t scales_shape[2];   /* must be [G, N]                                                 */
-  int64_t g_idx_len;         /* K, or 0 when no g_idx is passed (then g = k / group_size)      */
+  int64_t g_idx_len;         /* K, or 0 when no g_idx is passed (then g = k / group_size); 0
+                                for AWQ_GEMM                                                   */
 } gptq_layer_desc;
 
 typedef struct {
@@ -146,7 +161,7 @@ gptq_status gptq_info(gptq_handle_t h, gptq_handle_info* info);
 /* Test hook: reads the runtime layout back and decodes it on the host into the checkpoint's
  * logical values, in ORIGINAL input order:
  *   codes_kn_host  uint8 [K * N]  code[k, n] at k * N + n
- *   zeros_gn_host  int32 [G * N]  zero[g, n] = stored + 1
+ *   zeros_gn_host  int32 [G * N]  zero[g, n] (GPTQ: stored + 1; AWQ_GEMM: as stored)
  *   scales_gn_host uint32 [G * N] raw scale bits (16-bit patterns zero-extended, or f32 bits)
  *   perm_host      int32 [K]      input index at each sorted position
  * Any output pointer may be NULL to skip it.  Synchronises the device.  The runtime layout is

@@ -38,6 +38,15 @@ def repack_layer(L: gi.Layer, use_gidx=True):
     return h
 
 
+def repack_awq_layer(L: gi.AwqLayer):
+    import torch
+    import weight_only_quantized_amd as wq
+    qw = torch.from_numpy(np.ascontiguousarray(L.qweight)).cuda()
+    qz = torch.from_numpy(np.ascontiguousarray(L.qzeros)).cuda()
+    sc = bits_to_device(L.scales, L.scales_dtype)
+    return wq.repack(qw, qz, sc, None, bits=4, group_size=L.group_size, checkpoint_format="awq_gemm")
+
+
 def run_gemm(h, x_bits, x_tag, path=0, bias=None, bias_tag=None):
     """One gemm call (gptq_gemm_bias when `bias`, bit patterns in `bias_tag`, is given)."""
     x = bits_to_device(x_bits, x_tag)

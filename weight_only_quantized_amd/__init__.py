@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi3
 STATUS = {0: "OK", 1: "E_INVALID_ARG", 2: "E_SHAPE", 3: "E_GIDX", 4: "E_UNSUPPORTED", 5: "E_HIP",
           6: "E_OOM", 7: "E_WORKSPACE", 8: "E_DEVICE"}
 F16, BF16, F32 = 0, 1, 2
-FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2}
+FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2, "awq_gemm": 3}
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
 # Every symbol include/gptq_mi355x.h declares.
@@ -224,7 +224,9 @@ class Handle:
 def repack(qweight, qzeros, scales, g_idx=None, *, bits, group_size, desc_act=False, checkpoint_format="gptq",
            stream=None) -> Handle:
     """Build the runtime layout from checkpoint tensors on the current GPU (int32 qweight/qzeros,
-    fp16/bf16/fp32 scales, optional int32 g_idx).  The inputs may be freed afterwards."""
+    fp16/bf16/fp32 scales, optional int32 g_idx).  The inputs may be freed afterwards.
+    checkpoint_format "awq_gemm" reads AutoAWQ GEMM tensors instead (4-bit, qweight [K, N/8],
+    qzeros [G, N/8], zeros as stored, no g_idx)."""
     import torch
     lib = load_library()
     for name, t in (("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
@@ -232,12 +234,16 @@ def repack(qweight, qzeros, scales, g_idx=None, *, bits, group_size, desc_act=Fa
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
         raise TypeError("qweight and qzeros must be int32")
-    K = qweight.shape[0] * 32 // bits if bits in (2, 3, 4, 8) else 0
+    awq = FORMATS.get(checkpoint_format, checkpoint_format) == FORMATS["awq_gemm"]
+    if awq:  # AutoAWQ GEMM: qweight [K, N / 8], eight 4-bit fields per word along the outputs
+        K, N = qweight.shape[0], qweight.shape[1] * 8
+    else:
+        K = qweight.shape[0] * 32 // bits if bits in (2, 3, 4, 8) else 0
+        N = qweight.shape[1]
     if g_idx is not None:
         if g_idx.dtype != torch.int32 or not g_idx.is_cuda or not g_idx.is_contiguous():
             raise TypeError("g_idx must be a contiguous int32 GPU tensor")
         K = g_idx.shape[0]
-    N = qweight.shape[1]
     d = make_desc(K, N, bits, group_size, _dtype_code(scales.dtype), qweight.shape, qzeros.shape, scales.shape,
                   0 if g_idx is None else g_idx.shape[0], desc_act, checkpoint_format)
     out = ctypes.c_void_p()

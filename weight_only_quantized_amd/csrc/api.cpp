@@ -55,19 +55,27 @@ static gptq_status validate_desc(const gptq_layer_desc* d) {
   if (!d || d->reserved != 0) return GPTQ_E_INVALID_ARG;
   const int b = d->bits;
   if (b != 2 && b != 3 && b != 4 && b != 8) return GPTQ_E_UNSUPPORTED;           // GPTQ-001
-  if (d->checkpoint_format != GPTQ_FORMAT_GPTQ) return GPTQ_E_UNSUPPORTED;        // GPTQ-005
+  const bool awq = d->checkpoint_format == GPTQ_FORMAT_AWQ_GEMM;
+  if (d->checkpoint_format != GPTQ_FORMAT_GPTQ && !awq) return GPTQ_E_UNSUPPORTED;  // GPTQ-005
+  if (awq && (b != 4 || d->desc_act)) return GPTQ_E_UNSUPPORTED;                // 4-bit, sequential groups
   if (d->scales_dtype != GPTQ_F16 && d->scales_dtype != GPTQ_BF16 && d->scales_dtype != GPTQ_F32)
     return GPTQ_E_INVALID_ARG;
   const int gs = d->group_size;
   if (gs != -1 && (gs <= 0 || gs % 32 != 0)) return GPTQ_E_UNSUPPORTED;
   const int64_t K = d->in_features, N = d->out_features;
   if (K <= 0 || K % 32 != 0 || K > (1 << 20)) return GPTQ_E_SHAPE;               // GPTQ-002
-  if (d->qweight_shape[0] != K / 32 * b || d->qweight_shape[1] != N) return GPTQ_E_SHAPE;
   if (N <= 0 || N % 32 != 0 || N > (1 << 20) || K * N > (int64_t(1) << 36)) return GPTQ_E_SHAPE;
   const int64_t G = groups_of((int)K, gs);
-  if (d->qzeros_shape[0] != G || d->qzeros_shape[1] != N / 32 * b) return GPTQ_E_SHAPE;  // GPTQ-003
+  if (awq) {
+    if (d->qweight_shape[0] != K || d->qweight_shape[1] != N / 8) return GPTQ_E_SHAPE;
+    if (d->qzeros_shape[0] != G || d->qzeros_shape[1] != N / 8) return GPTQ_E_SHAPE;
+    if (d->g_idx_len != 0) return GPTQ_E_GIDX;                                   // no g_idx in AWQ
+  } else {
+    if (d->qweight_shape[0] != K / 32 * b || d->qweight_shape[1] != N) return GPTQ_E_SHAPE;
+    if (d->qzeros_shape[0] != G || d->qzeros_shape[1] != N / 32 * b) return GPTQ_E_SHAPE;  // GPTQ-003
+    if (d->g_idx_len != 0 && d->g_idx_len != K) return GPTQ_E_GIDX;               // GPTQ-004
+  }
   if (d->scales_shape[0] != G || d->scales_shape[1] != N) return GPTQ_E_SHAPE;
-  if (d->g_idx_len != 0 && d->g_idx_len != K) return GPTQ_E_GIDX;                 // GPTQ-004
   return GPTQ_OK;
 }
 
@@ -188,7 +196,8 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
   }
   L->bytes = (int64_t)(wq_bytes + meta_n * 4 + s32_bytes + (has_perm ? perm_bytes : 0));
   e = hipMemcpyAsync(L->perm, perm_host.data(), perm_bytes, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = launch_repack(L, qweight, qzeros, scales, s);
+  if (e == hipSuccess)
+    e = launch_repack(L, qweight, qzeros, scales, desc->checkpoint_format == GPTQ_FORMAT_AWQ_GEMM ? 1 : 0, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     free_layer(L);
@@ -369,7 +378,7 @@ gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t
       for (int g = 0; g < G; ++g)
         for (int j = 0; j < kTileN; ++j) {
           const size_t src = ((size_t)ct * G + g) * kTileN + j, dst = (size_t)g * N + ct * kTileN + j;
-          if (zeros_gn_host) zeros_gn_host[dst] = (int32_t)((meta[src] >> 16) & 0xFFFF) + 1;
+          if (zeros_gn_host) zeros_gn_host[dst] = (int32_t)(((meta[src] >> 16) + 1) & 0xFFFF);
           if (scales_gn_host) scales_gn_host[dst] = f32 ? s32[src] : (meta[src] & 0xFFFF);
         }
   }

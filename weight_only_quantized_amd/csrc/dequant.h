@@ -47,12 +47,12 @@ template <> struct Bias<4, 1> { static constexpr bool any = true; static constex
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Per-lane, per-segment zero term from the stored zero s (= zero - 1).
+// Per-lane, per-segment zero term from the zero (0 .. 2^bits; zero_of).
 template <int BITS, int XT>
-__device__ __forceinline__ uint32_t zero_term(uint32_t stored) {
-  if constexpr (XT == 0) return (0xE400u + stored + 1u) * 0x00010001u;     // fp16 -(1024 + zero), both halves
-  else if constexpr (BITS <= 4) return (15u - stored) * 0x01010101u;       // + 16 - zero per byte
-  else return stored + 1u;                                                 // the zero itself
+__device__ __forceinline__ uint32_t zero_term(uint32_t zero) {
+  if constexpr (XT == 0) return (0xE400u + zero) * 0x00010001u;            // fp16 -(1024 + zero), both halves
+  else if constexpr (BITS <= 4) return (16u - zero) * 0x01010101u;         // + 16 - zero per byte
+  else return zero;                                                        // the zero itself
 }
 
 // Byte vector j (codes 4j .. 4j+3 of the lane, see layout.h) from the lane's words.
@@ -142,7 +142,9 @@ __device__ __forceinline__ float scale_of(uint32_t rec, uint32_t s32, int kind) 
   const float f32v = __builtin_bit_cast(float, s32);
   return kind == 0 ? f16v : (kind == 1 ? bf16v : f32v);
 }
-__device__ __forceinline__ uint32_t stored_zero_of(uint32_t rec) { return rec >> 16; }
+// The zero of a metadata record: its high half holds zero - 1 mod 2^16 (layout.h), which is the
+// GPTQ v1 stored field as it is and 0xFFFF for an AWQ zero of 0.
+__device__ __forceinline__ uint32_t zero_of(uint32_t rec) { return ((rec >> 16) + 1u) & 0xFFFFu; }
 
 // Element n of an optional bias vector ("GPTQ packed checkpoint (safetensors / torch)", section
 // "GptqLayer": same dtype as the scales), as fp32; 0 without one.  kind: 0 fp16, 1 bf16, 2 f32.

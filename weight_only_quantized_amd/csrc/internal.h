@@ -30,8 +30,9 @@ namespace gq {
 gptq_status hip_fail(hipError_t e);
 
 // Repack kernels (repack.hip).
+// awq: the tensors are AutoAWQ GEMM packed (fields along the output dimension, zeros as stored).
 hipError_t launch_repack(const gptq_layer* L, const int32_t* qweight, const int32_t* qzeros,
-                         const void* scales, hipStream_t s);
+                         const void* scales, int awq, hipStream_t s);
 
 // Parameters of one gptq_gemm call as the launchers see them.
 struct GemmCall {

@@ -32,7 +32,8 @@
 //
 // Group metadata is re-tiled the same way, one 32-bit record per (tile, group, column):
 //   meta[(ct * G + g) * 16 + j] = scale bits (fp16/bf16, bits 0-15; 0 for f32 scales)
-//                                 | stored zero (z - 1) << 16
+//                                 | (zero - 1 mod 2^16) << 16
+// (the GPTQ v1 stored field; an AWQ zero is stored as it is, so its 0 becomes 0xFFFF)
 // plus, for f32 scales only, scale32[(ct * G + g) * 16 + j] = the f32 bits.  One record per lane
 // per segment keeps the kernels' metadata loads unconditional and width-uniform.
 #pragma once

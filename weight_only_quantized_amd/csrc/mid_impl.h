@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        b[j][t] = build_b<BITS, XT>(wc.w[j], t, zero_term<BITS, XT>(stored_zero_of(wc.rec[j][t / SEG])));
+        b[j][t] = build_b<BITS, XT>(wc.w[j], t, zero_term<BITS, XT>(zero_of(wc.rec[j][t / SEG])));
     float sc[WN][NSEG];
 #pragma unroll
     for (int j = 0; j < WN; ++j)

@@ -28,6 +28,15 @@ __device__ __forceinline__ uint32_t packed_field(const uint32_t* __restrict__ w,
   return (v >> (bits * (int)(k % pack))) & ((1u << bits) - 1u);
 }
 
+// AutoAWQ GEMM pack ("39. Quantized checkpoints ...", section "AWQ"): row r, output n is the
+// 4-bit field at bit 4 * pos(n % 8) of word n / 8, where pos inverts the order 0 2 4 6 1 3 5 7:
+// pos(c) = 4 (c & 1) + c / 2.
+__device__ __forceinline__ uint32_t awq_field(const uint32_t* __restrict__ w, int64_t ld, int64_t r, int64_t n) {
+  const int c = (int)(n & 7);
+  const int pos = ((c & 1) << 2) | (c >> 1);
+  return (w[r * ld + (n >> 3)] >> (4 * pos)) & 0xFu;
+}
+
 // Same rule along the row (qzeros: group row g, output column n).
 __device__ __forceinline__ uint32_t packed_field_cols(const uint32_t* __restrict__ w, int64_t ld, int bits,
                                                       int64_t g, int64_t n) {
@@ -48,7 +57,7 @@ __device__ __forceinline__ uint32_t packed_field_cols(const uint32_t* __restrict
 // One thread per (unit, lane): gathers the lane's 32 codes and writes its `bits` words.
 __global__ void __launch_bounds__(256) repack_words_kernel(
     const uint32_t* __restrict__ qweight, const int32_t* __restrict__ perm, uint32_t* __restrict__ out,
-    int K, int N, int bits, int KC, int64_t n_lanes) {
+    int K, int N, int bits, int KC, int64_t n_lanes, int awq) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_lanes) return;
   const int lane = (int)(gid & 63);
@@ -62,7 +71,7 @@ __global__ void __launch_bounds__(256) repack_words_kernel(
     uint32_t code = 0;
     if (ks < K) {
       const int k = perm[ks];
-      code = packed_field(qweight, N, bits, k, n);
+      code = awq ? awq_field(qweight, N / 8, k, n) : packed_field(qweight, N, bits, k, n);
     }
     Piece p[2];
     const int np = code_pieces(bits, i, p);
@@ -75,10 +84,10 @@ __global__ void __launch_bounds__(256) repack_words_kernel(
   for (int w = 0; w < bits; ++w) u[unit_word_offset(bits, lane, w)] = words[w];
 }
 
-// One thread per (tile, group, column-in-tile): scale bits and stored zero.
+// One thread per (tile, group, column-in-tile): scale bits and zero - 1 (mod 2^16; layout.h).
 __global__ void __launch_bounds__(256) repack_meta_kernel(
     const uint32_t* __restrict__ qzeros, const void* __restrict__ scales, int scale_bytes,
-    uint32_t* __restrict__ meta, uint32_t* __restrict__ scale32, int N, int G, int bits, int64_t total) {
+    uint32_t* __restrict__ meta, uint32_t* __restrict__ scale32, int N, int G, int bits, int64_t total, int awq) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int j = (int)(gid & 15);
@@ -87,7 +96,8 @@ __global__ void __launch_bounds__(256) repack_meta_kernel(
   const int64_t ct = cg / G;
   const int64_t n = ct * kTileN + j;
   const int64_t zld = (int64_t)N / 32 * bits;
-  const uint32_t z = packed_field_cols(qzeros, zld, bits, g, n);
+  // GPTQ v1 stores zero - 1 already; an AWQ zero is stored as it is
+  const uint32_t z = awq ? ((awq_field(qzeros, N / 8, g, n) - 1u) & 0xFFFFu) : packed_field_cols(qzeros, zld, bits, g, n);
   if (scale_bytes == 4) {
     meta[gid] = z << 16;
     scale32[gid] = reinterpret_cast<const uint32_t*>(scales)[(int64_t)g * N + n];
@@ -97,18 +107,18 @@ __global__ void __launch_bounds__(256) repack_meta_kernel(
 }
 
 hipError_t launch_repack(const gptq_layer* L, const int32_t* qweight, const int32_t* qzeros,
-                         const void* scales, hipStream_t s) {
+                         const void* scales, int awq, hipStream_t s) {
   const int64_t n_lanes = (int64_t)L->CT * L->KC * kLanes;
   const int64_t blocks = (n_lanes + 255) / 256;
   hipLaunchKernelGGL(repack_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(qweight), L->perm, L->wq, L->K, L->N, L->bits,
-                     L->KC, n_lanes);
+                     L->KC, n_lanes, awq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = (int64_t)L->CT * L->G * kTileN;
   hipLaunchKernelGGL(repack_meta_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(qzeros), scales, L->scales_dtype == GPTQ_F32 ? 4 : 2,
-                     L->meta, L->scale32, L->N, L->G, L->bits, total);
+                     L->meta, L->scale32, L->N, L->G, L->bits, total, awq);
   return hipGetLastError();
 }
 

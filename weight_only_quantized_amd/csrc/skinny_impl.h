@@ -176,7 +176,7 @@ skinny_kernel(const SkinnyArgs a) {
         f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) tmp = mfma16<XT>(xc.xa[0][t], build_b_offset<BITS, XT>(c.w[i], t), tmp);
-        const float off = (XT == 0 ? 1024.f : 128.f) + (float)(stored_zero_of(c.rec[i][0]) + 1u);
+        const float off = (XT == 0 ? 1024.f : 128.f) + (float)zero_of(c.rec[i][0]);
         acc[0][i][0] += scale_of(c.rec[i][0], c.s32[i][0], a.scale_kind) * (tmp[0] - off * sx);
       }
     }
@@ -198,7 +198,7 @@ skinny_kernel(const SkinnyArgs a) {
     for (int i = 0; i < TW; ++i) {
       u32x4 b[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[t] = build_b<BITS, XT>(c.w[i], t, zero_term<BITS, XT>(stored_zero_of(c.rec[i][t / SEG])));
+      for (int t = 0; t < 4; ++t) b[t] = build_b<BITS, XT>(c.w[i], t, zero_term<BITS, XT>(zero_of(c.rec[i][t / SEG])));
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll

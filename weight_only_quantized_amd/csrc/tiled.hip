@@ -332,7 +332,7 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        b[j][t] = build_b<BITS, 0>(st.w[j], t, zero_term<BITS, 0>(stored_zero_of(st.rec[j][t / SEG])));
+        b[j][t] = build_b<BITS, 0>(st.w[j], t, zero_term<BITS, 0>(zero_of(st.rec[j][t / SEG])));
     float sc[WN][NSEG];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
