@@ -79,9 +79,10 @@ def stored_traffic(kernel_key):
 
 
 class Workload:
-    def __init__(self, name, K, N, M, bits, gs, desc_act, sdt, xdt, seed, bias=False):
+    def __init__(self, name, K, N, M, bits, gs, desc_act, sdt, xdt, seed, bias=False, fmt="gptq"):
         self.name, self.K, self.N, self.M, self.bits, self.gs = name, K, N, M, bits, gs
         self.desc_act, self.sdt, self.xdt, self.seed, self.bias = desc_act, sdt, xdt, seed, bias
+        self.fmt = fmt   # checkpoint the layer is repacked from: "gptq" or "awq_gemm"
 
     def label(self):
         g = "g-1" if self.gs == -1 else f"g{self.gs}"
@@ -93,14 +94,19 @@ def build_handles(w: Workload, copies: int):
     import torch
     import gptq_inputs as gi
     import weight_only_quantized_amd as wq
-    L = gi.make_layer(w.K, w.N, w.bits, w.gs, desc_act=w.desc_act, scales_dtype=w.sdt, seed=w.seed)
     dev = torch.device("cuda:0")
+    if w.fmt == "awq_gemm":
+        L = gi.make_awq_layer(w.K, w.N, w.gs, scales_dtype=w.sdt, seed=w.seed)
+        g = None
+    else:
+        L = gi.make_layer(w.K, w.N, w.bits, w.gs, desc_act=w.desc_act, scales_dtype=w.sdt, seed=w.seed)
+        g = torch.from_numpy(L.g_idx).to(dev)
     qw = torch.from_numpy(L.qweight).to(dev)
     qz = torch.from_numpy(L.qzeros).to(dev)
     sc = torch.from_numpy(L.scales.view(np.int16).copy()).to(dev).view(
         torch.float16 if w.sdt == "f16" else torch.bfloat16)
-    g = torch.from_numpy(L.g_idx).to(dev)
-    hs = [wq.repack(qw, qz, sc, g, bits=w.bits, group_size=w.gs, desc_act=w.desc_act) for _ in range(copies)]
+    hs = [wq.repack(qw, qz, sc, g, bits=w.bits, group_size=w.gs, desc_act=w.desc_act, checkpoint_format=w.fmt)
+          for _ in range(copies)]
     del qw, qz, sc, g
     return L, hs
 
@@ -221,6 +227,11 @@ def extra_workloads():
                         bias=True))
     out.append(Workload("bias_prefill_4096x8192x28672", 8192, 28672, 4096, 4, 128, False, "bf16", "bf16",
                         gi.seed_for(4), bias=True))
+    # the same shapes repacked from AutoAWQ GEMM tensors (same runtime layout and kernels)
+    out.append(Workload("awq_llama3_8b_up_proj", 4096, 14336, 1, 4, 128, False, "f16", "f16", gi.seed_for(5),
+                        fmt="awq_gemm"))
+    out.append(Workload("awq_prefill_4096x8192x28672", 8192, 28672, 4096, 4, 128, False, "bf16", "bf16",
+                        gi.seed_for(5), fmt="awq_gemm"))
     return out
 
 
