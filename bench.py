@@ -211,9 +211,9 @@ HEADLINE = Workload("llama3_8b_up_proj", 4096, 14336, 1, 4, 128, False, "f16", "
 def extra_workloads():
     import gptq_inputs as gi
     out = []
-    for M in (4, 16):
+    for M in (4, 16, 64, 128, 256):
         out.append(Workload("llama3_8b_up_proj", 4096, 14336, M, 4, 128, False, "f16", "f16", gi.seed_for(1)))
-    for M in (1, 8, 16):
+    for M in (1, 8, 16, 32, 64, 128, 256):
         out.append(Workload("llama3_70b_gate_proj", 8192, 28672, M, 4, 128, False, "f16", "bf16", gi.seed_for(2)))
     for bits in (2, 3, 4, 8):
         for gs in (128, -1):

@@ -71,8 +71,9 @@ typedef enum {
   GPTQ_FORMAT_AWQ_GEMM = 3
 } gptq_format;
 
-/* Kernel family for gptq_gemm.  AUTO picks SKINNY for M <= 64 and TILED otherwise.  Forcing a
- * family is for tests; a forced family that cannot run the given M returns GPTQ_E_INVALID_ARG. */
+/* Kernel family for gptq_gemm.  AUTO picks SKINNY for M <= 16 (M <= 32 when K spans more than
+ * 4096 inputs) and TILED otherwise.  Forcing a family is for tests; SKINNY runs M <= 64 only
+ * (GPTQ_E_INVALID_ARG above), TILED any M. */
 typedef enum { GPTQ_PATH_AUTO = 0, GPTQ_PATH_SKINNY = 1, GPTQ_PATH_TILED = 2 } gptq_path;
 
 /* Description of one checkpoint layer.  The *_shape fields are the shapes of the tensors the

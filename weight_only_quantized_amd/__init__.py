@@ -67,6 +67,9 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
                            "or `python weight_only_quantized_amd/build.py`")
+    # torch first: the library then binds to the HIP runtime torch has loaded, so both share one
+    # runtime (a library loaded before torch would bring up a second runtime in the process)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.gptq_validate.argtypes = [ctypes.POINTER(Desc), P]

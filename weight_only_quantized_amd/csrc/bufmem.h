@@ -52,5 +52,8 @@ __device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t voff, uint32_t s
 __device__ __forceinline__ void store_b16(rsrc_t r, uint16_t v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, 0u, 0);
 }
+__device__ __forceinline__ void store_b32(rsrc_t r, uint32_t v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0u, 0);
+}
 
 }  // namespace gq

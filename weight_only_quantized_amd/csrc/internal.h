@@ -62,6 +62,13 @@ bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
 // mid kernel (split K, mid.hip) otherwise; the mid kernel's partial sums need workspace.
 bool uses_mid(const gptq_layer* L, int64_t M);
 size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M);
+// Split-K partial sums of the tiled family ([KS][M][N] fp32 after the x copy and row exponents).
+size_t ws_tiled_part_bytes(const gptq_layer* L, int64_t M);
+
+// y[m, n] = round(sum over s = 0 .. KS-1 in order of part[s][m][n] + bias[n]) for rows*N outputs
+// (N a multiple of 4): the second launch of every split-K call (mid.hip).
+hipError_t launch_part_reduce(const float* part, uint16_t* y, int64_t rows, int N, int KS, const void* bias,
+                              int bias_kind, int x_bf16, hipStream_t s);
 
 // Family launchers.  All assume the call was validated.
 hipError_t launch_skinny(const GemmCall& c);

@@ -73,14 +73,17 @@ static hipError_t mid_pass(const GemmCall& c, const uint16_t* x, int ld, float* 
     default: e = mid_b8(a, p, c.x_bf16, L->seg_steps, c.stream); break;
   }
   if (e != hipSuccess || p.KS == 1) return e;
-  const int64_t mn = rows * (int64_t)L->N, mn4 = mn / 4;     // N is a multiple of 32
+  return launch_part_reduce(a.part, a.y, rows, L->N, p.KS, c.bias, L->scales_dtype, c.x_bf16, c.stream);
+}
+
+hipError_t launch_part_reduce(const float* part, uint16_t* y, int64_t rows, int N, int KS, const void* bias,
+                              int bias_kind, int x_bf16, hipStream_t s) {
+  const int64_t mn = rows * (int64_t)N, mn4 = mn / 4;     // N is a multiple of 32
   const unsigned blocks = (unsigned)((mn4 + 255) / 256);
-  if (c.x_bf16)
-    hipLaunchKernelGGL(mid_reduce_kernel<1>, dim3(blocks), dim3(256), 0, c.stream, a.part, a.y, mn4, mn, p.KS,
-                       L->N, c.bias, L->scales_dtype);
+  if (x_bf16)
+    hipLaunchKernelGGL(mid_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, part, y, mn4, mn, KS, N, bias, bias_kind);
   else
-    hipLaunchKernelGGL(mid_reduce_kernel<0>, dim3(blocks), dim3(256), 0, c.stream, a.part, a.y, mn4, mn, p.KS,
-                       L->N, c.bias, L->scales_dtype);
+    hipLaunchKernelGGL(mid_reduce_kernel<0>, dim3(blocks), dim3(256), 0, s, part, y, mn4, mn, KS, N, bias, bias_kind);
   return hipGetLastError();
 }
 

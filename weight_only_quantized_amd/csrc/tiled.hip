@@ -1,4 +1,6 @@
-// Tiled family (M > 64): an MFMA-bound GEMM with the weight operand dequantised in registers.
+// Tiled family (M > 16, or > 32 on long K): an MFMA GEMM with the weight operand dequantised in
+// registers, from a table of workgroup tiles, with K split over workgroups when the tiles alone
+// would leave compute units idle (tiled_plan).
 //
 // "Formats and kernels: FP8, INT8, INT4, Marlin, Machete" (the batch-size crossover and the
 // software-pipelining discussion) places large M on the matrix cores: the packed weight must stay
@@ -26,8 +28,17 @@
 //     block (L2) while all XCDs walk the same weight column blocks (MALL); workgroups sharing a
 //     row block walk K in step, so each x chunk is fetched into L2 about once per XCD (a
 //     staggered K start per column block measured 2-3 % slower and doubled the fabric reads);
-//   * the packed units and metadata of the next chunk are requested before its x tile.
+//   * the packed units and metadata of the next chunk are requested before its x tile;
+//   * split K for the few-tile calls of the mid-batch range that "Formats and kernels ...", section
+//     "Tile tables, and what happens when your shape does not fit", buckets: slice ks of KS runs chunks
+//     [ks kcs, (ks + 1) kcs) and writes fp32 partial sums; a second launch adds the slices in
+//     order with the bias and rounds once (deterministic, no atomics, no counters to clear).
 #include <hip/hip_runtime.h>
+
+#ifdef GQ_TUNE
+#include <cstdio>
+#include <cstdlib>
+#endif
 
 #include "bufmem.h"
 #include "dequant.h"
@@ -190,8 +201,10 @@ struct TiledArgs {
   const uint16_t* x;     // [M, ld] sorted-order activations
   const int32_t* rowexp;   // per-row power of two of the fp16 copy (bf16 activations only)
   uint16_t* y;
+  float* part;           // split K: [KS][M][N] fp32 partial sums (KS > 1), else NULL
   int ld;
   int M, K, N, KC, CT, G, scale_kind, MB, NB;
+  int KS, kcs;           // K slices and chunks per slice (KS = ceil(KC / kcs))
   uint32_t gmagic;       // segment -> group map (see segment_divisor)
   int gshift;
   const void* bias;      // [N] in the scales' dtype (scale_kind), or NULL
@@ -228,6 +241,35 @@ __device__ __forceinline__ void store_tiles(const TiledArgs& a, const f32x4 (&ac
   }
 }
 
+// Split K: the same tiles as fp32 partial sums of slice ks (bf16 rows already multiplied back by
+// 2^rowexp), no bias; launch_part_reduce adds the slices in order.
+template <int OB, int WM, int WN>
+__device__ __forceinline__ void store_part(const TiledArgs& a, const f32x4 (&acc)[WM][WN], int ks, int m0, int ct0,
+                                           int col, int q) {
+  const int64_t mn = (int64_t)a.M * a.N;
+  const rsrc_t rp = make_rsrc(a.part + ks * mn, (uint32_t)(mn * 4));
+  u32x4 ex[WM];
+  if constexpr (OB) {
+    const rsrc_t re = make_rsrc(a.rowexp, (uint32_t)a.M * 4u);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) ex[i] = load_b128(re, (uint32_t)(m0 + i * 16 + 4 * q) * 4u, 0u);
+  }
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    if (ct0 + j >= a.CT) continue;
+    const int n = (ct0 + j) * 16 + col;
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + i * 16 + 4 * q + r;
+        const uint32_t off = m < a.M ? (uint32_t)(m * a.N + n) * 4u : kOob;
+        const float v = OB ? ldexpf(acc[i][j][r], (int)ex[i][r]) : acc[i][j][r];
+        store_b32(rp, __builtin_bit_cast(uint32_t, v), off);
+      }
+  }
+}
+
 // x tile of one chunk in LDS: BM rows x 16 pieces of 16 bytes, no padding, piece c of row r at
 // slot r * 16 + (c ^ (r & 15)).  Sixteen lanes reading the same piece of sixteen consecutive
 // rows (an A operand) then hit sixteen different 16-byte bank groups.  The tile is filled with
@@ -250,11 +292,16 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, q = lane >> 4;
 
-  // XCD-aware remap of the linear workgroup id (see the file comment).
-  const int total = a.MB * a.NB;
+  // XCD-aware remap of the linear workgroup id (see the file comment); with split K the slice is
+  // the outermost index, so an XCD's workgroups share one slice of x.
+  const int tiles = a.MB * a.NB;
+  const int total = tiles * a.KS;
   int lid = blockIdx.x;
   if ((total & 7) == 0) lid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int mb = lid / a.NB, nb = lid % a.NB;
+  const int ks = lid / tiles;
+  const int mb = (lid - ks * tiles) / a.NB, nb = (lid - ks * tiles) % a.NB;
+  const int kc_lo = ks * a.kcs;
+  const int kc_hi = min(a.KC, kc_lo + a.kcs);     // never empty: KS = ceil(KC / kcs)
   const int m0 = mb * BM;
   const int ct0 = nb * (NW * WN) + wave * WN;
 
@@ -402,12 +449,12 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   };
 
   Stage cur, nxt;
-  issue(0, 0, cur, true);
+  issue(kc_lo, 0, cur, true);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int it = 0; it < a.KC; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < a.KC;
+  for (int it = kc_lo; it < kc_hi; ++it) {
+    const int buf = (it - kc_lo) & 1;
+    const bool more = it + 1 < kc_hi;
     // The next chunk's x tile goes out one 1 KB piece per row block and its units and metadata
     // after the third piece, so the workgroup's requests do not all queue up at once behind the
     // barrier (measured on MI355X: 5 % faster than issuing everything before the chunk).
@@ -422,7 +469,8 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     cur = nxt;
   }
 
-  store_tiles<OB, WM, WN>(a, acc, m0, ct0, col, q);
+  if (a.part) store_part<OB, WM, WN>(a, acc, ks, m0, ct0, col, q);
+  else store_tiles<OB, WM, WN>(a, acc, m0, ct0, col, q);
 }
 
 template <int BITS, int OB, int WM, int WN, int SEG, int NW>
@@ -430,28 +478,97 @@ static hipError_t run_tiled(const TiledArgs& a0, hipStream_t s) {
   TiledArgs a = a0;
   a.MB = (a.M + 16 * WM - 1) / (16 * WM);
   a.NB = (a.CT + NW * WN - 1) / (NW * WN);
-  hipLaunchKernelGGL((tiled_kernel<BITS, OB, WM, WN, SEG, NW>), dim3((unsigned)(a.MB * a.NB)), dim3(64 * NW), 0, s,
-                     a);
+  hipLaunchKernelGGL((tiled_kernel<BITS, OB, WM, WN, SEG, NW>), dim3((unsigned)(a.MB * a.NB * a.KS)), dim3(64 * NW),
+                     0, s, a);
   return hipGetLastError();
 }
 
-// M > 128: wave tile 256 x 32, eight waves (workgroup tile 256 x 256, two waves per SIMD).
-// Smaller M, and 32-input segments (group sizes that are not a multiple of 128, whose four scales
-// per chunk do not fit the larger tile's registers): wave tile 128 x 16, eight waves (128 x 128).
+// Tile table: (rows, columns) of a workgroup tile, its wave tile and wave count.
+struct TileShape { int WM, WN, NW; };
+constexpr TileShape kTiles[] = {
+  {16, 2, 8},   // 0: 256 x 256, wave 256 x 32
+  {8, 1, 8},    // 1: 128 x 128, wave 128 x 16 (also every 32-input-segment layer)
+  {8, 2, 4},    // 2: 128 x 128, wave 128 x 32
+  {4, 2, 4},    // 3:  64 x 128, wave  64 x 32
+  {8, 2, 8},    // 4: 128 x 256, wave 128 x 32
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+struct TiledPlan { int tile, KS, kcs; };
+
+static int64_t tiles_of(const gptq_layer* L, int64_t M, int t) {
+  const TileShape& ts = kTiles[t];
+  return ((M + 16 * ts.WM - 1) / (16 * ts.WM)) * ((L->CT + ts.NW * ts.WN - 1) / (ts.NW * ts.WN));
+}
+
+static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Tile and K split of a call: an M-bucketed tile table as in "Formats and kernels ...", section
+// "Tile tables, and what happens when your shape does not fit", re-derived for gfx950 from a sweep
+// of every tile and split on MI355X (4-bit g128, 4096 x 14336 and 8192 x 28672 layers, M = 4 ..
+// 1024): a call runs best with about one eight-wave workgroup (or two four-wave ones) per compute
+// unit, from the largest tile that gets there, and splits K only as far as needed to get there:
+//   * M <= 64: the 64 x 128 tile, K split up to ~448 workgroups;
+//   * larger M: the 256 x 256 tile once it alone gives ~192 workgroups, else the 128 x 256 tile,
+//     K split up to ~224 workgroups when it gives fewer than ~150;
+//   * 32-input segments: the 128 x 128 tile (wave 128 x 16), split the same way.
+// Split K only while one slice of partial sums stays addressable by 32-bit offsets and the rows
+// are one launch.
+static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
+  TiledPlan p;
+  p.KS = 1;
+  if (L->seg_steps != 4) {
+    p.tile = 1;
+  } else if (M <= 64) {
+    p.tile = 3;
+  } else if (tiles_of(L, M, 0) >= 192) {
+    p.tile = 0;
+  } else {
+    p.tile = 4;
+  }
+  const int64_t t = tiles_of(L, M, p.tile);
+  if (p.tile == 3) p.KS = ceil_div(448, t);
+  else if (t < 150) p.KS = ceil_div(224, t);
+#ifdef GQ_TUNE
+  if (const char* e = getenv("GQ_TILED")) {
+    int tt = p.tile, ks = 1;
+    if (sscanf(e, "%d:%d", &tt, &ks) == 2 && tt >= 0 && tt < kNumTiles && ks >= 1 && (L->seg_steps == 4 || tt == 1)) {
+      p.tile = tt;
+      p.KS = ks;
+    }
+  }
+#endif
+  if (p.KS > 1 && (M * (int64_t)L->N * 4 > (int64_t)INT32_MAX || M > 768)) p.KS = 1;
+  if (p.KS > L->KC / 4) p.KS = L->KC / 4 > 1 ? L->KC / 4 : 1;     // at least four chunks per slice
+  p.kcs = (L->KC + p.KS - 1) / p.KS;
+  p.KS = (L->KC + p.kcs - 1) / p.kcs;
+  return p;
+}
+
+size_t ws_tiled_part_bytes(const gptq_layer* L, int64_t M) {
+  const TiledPlan p = tiled_plan(L, M);
+  return p.KS > 1 ? align256((size_t)p.KS * M * L->N * 4) : 0;
+}
+
 template <int BITS, int OB>
-static hipError_t run_tiled_m(const TiledArgs& a, int seg, hipStream_t s) {
+static hipError_t run_tiled_m(const TiledArgs& a, int tile, int seg, hipStream_t s) {
   if (seg != 4) return run_tiled<BITS, OB, 8, 1, 1, 8>(a, s);
-  if (a.M > 128) return run_tiled<BITS, OB, 16, 2, 4, 8>(a, s);
-  return run_tiled<BITS, OB, 8, 1, 4, 8>(a, s);
+  switch (tile) {
+    case 0: return run_tiled<BITS, OB, 16, 2, 4, 8>(a, s);
+    case 2: return run_tiled<BITS, OB, 8, 2, 4, 4>(a, s);
+    case 3: return run_tiled<BITS, OB, 4, 2, 4, 4>(a, s);
+    case 4: return run_tiled<BITS, OB, 8, 2, 4, 8>(a, s);
+    default: return run_tiled<BITS, OB, 8, 1, 4, 8>(a, s);
+  }
 }
 
 template <int OB>
-static hipError_t run_tiled_bits(const TiledArgs& a, int bits, int seg, hipStream_t s) {
+static hipError_t run_tiled_bits(const TiledArgs& a, int bits, int tile, int seg, hipStream_t s) {
   switch (bits) {
-    case 2: return run_tiled_m<2, OB>(a, seg, s);
-    case 3: return run_tiled_m<3, OB>(a, seg, s);
-    case 4: return run_tiled_m<4, OB>(a, seg, s);
-    default: return run_tiled_m<8, OB>(a, seg, s);
+    case 2: return run_tiled_m<2, OB>(a, tile, seg, s);
+    case 3: return run_tiled_m<3, OB>(a, tile, seg, s);
+    case 4: return run_tiled_m<4, OB>(a, tile, seg, s);
+    default: return run_tiled_m<8, OB>(a, tile, seg, s);
   }
 }
 
@@ -481,6 +598,16 @@ hipError_t launch_tiled(const GemmCall& c) {
   a.scale_kind = L->scales_dtype;
   a.bias = c.bias;
   a.MB = a.NB = 0;
+  const TiledPlan p = tiled_plan(L, c.M);
+  a.KS = p.KS;
+  a.kcs = p.kcs;
+  a.part = nullptr;
+  if (p.KS > 1) {
+    uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
+    if (tiled_needs_xsorted(L, c.x_bf16)) base += ws_xsorted_bytes(L, c.M);
+    if (c.x_bf16) base += ws_rowexp_bytes(c.M);
+    a.part = reinterpret_cast<float*>(base);
+  }
   // rows per slice: x and y byte offsets inside a slice stay below 2^31 (at least 768 rows, as
   // K, N <= 2^20)
   const int64_t lim = ((int64_t(1) << 31) - 1) / (2 * (int64_t)(a.ld > a.N ? a.ld : a.N));
@@ -490,8 +617,10 @@ hipError_t launch_tiled(const GemmCall& c) {
     a.x = x + m0 * a.ld;
     a.rowexp = rowexp ? rowexp + m0 : nullptr;
     a.y = reinterpret_cast<uint16_t*>(c.y) + m0 * a.N;
-    const hipError_t e = c.x_bf16 ? run_tiled_bits<1>(a, L->bits, L->seg_steps, c.stream)
-                                  : run_tiled_bits<0>(a, L->bits, L->seg_steps, c.stream);
+    hipError_t e = c.x_bf16 ? run_tiled_bits<1>(a, L->bits, p.tile, L->seg_steps, c.stream)
+                            : run_tiled_bits<0>(a, L->bits, p.tile, L->seg_steps, c.stream);
+    if (e == hipSuccess && a.part)      // (split K implies one row slice)
+      e = launch_part_reduce(a.part, a.y, a.M, a.N, a.KS, c.bias, L->scales_dtype, c.x_bf16, c.stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
