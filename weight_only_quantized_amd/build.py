@@ -39,6 +39,17 @@ def spilled_kernels(remarks: str) -> list:
     return out
 
 
+def undefined_kernel_stubs(lib: str) -> list:
+    """Kernel launch stubs the library references but does not define.  hipcc's host pass can drop
+    a kernel's stub without a diagnostic (seen with some buffer-to-LDS builtin arguments); the
+    library then fails to load, so the build checks for it instead."""
+    try:
+        r = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    except FileNotFoundError:
+        return []
+    return [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compile every source (in parallel, one hipcc per file) and link LIB.  Always rebuilds.
     Returns the library path."""
@@ -72,6 +83,10 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"link failed ({r.returncode})")
+    missing = undefined_kernel_stubs(tmp)
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError(f"kernels without a host launch stub (the host pass dropped them): {missing[:4]}")
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)
