@@ -22,6 +22,14 @@ Sources (page title, then section):
          error from output-rounding error).
   [FK]   "Formats and kernels: FP8, INT8, INT4, Marlin, Machete", opening section
          (effective bits b_eff = bits + 16 / group_size with fp16 scales).
+  [PLN]  "Kernel Backends Reference", section "Planar packing": GPTQ_P words -- a b-bit
+         code (b = 2 .. 8) split into planes of widths 2 | 2+1 | 4 | 4+1 | 4+2 | 4+2+1 | 8,
+         low bits first; each plane width divides 32 so no field straddles a word; the
+         plane words of every 32 codes are adjacent, low plane first; single-plane 2/4/8
+         are bit-identical to continuous packing, planar 3-bit is not.
+  [V2]   "39. Quantized checkpoints ...", section "GPTQ" (the corrected layout newer tools
+         call gptq_v2: no "minus one" on stored zeros) and "Kernel Backends Reference",
+         section "Packed storage and execution concepts" (v1 / v2 zero semantics).
   [AWQ]  "39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes", section
          "AWQ", its checkpoint part: AutoAWQ GEMM tensors qweight [in, out / 8] and
          qzeros [groups, out / 8] pack eight 4-bit fields along the OUTPUT dimension in
@@ -39,6 +47,10 @@ Readings where the pages are silent or ambiguous (each is listed in the design doc):
   * int32 words are two's-complement images of 32-bit fields ([FMT] as_int32);
     fields are read with logical shifts of the unsigned image.
   * group_size = -1 means one group covering all inputs ([SPEC] QuantizeConfig).
+  * GPTQ_P: inside a plane, code j of a block of 32 sits at bit w*j mod 32 of the plane's
+    word w*j // 32 (continuous packing of that plane, which is what makes single-plane
+    layouts identical to continuous ones); the same rule packs qzeros along the output
+    dimension; its zeros keep the GPTQ (v1) "minus one" ([PLN] names only the packing).
 """
 from __future__ import annotations
 
@@ -51,6 +63,8 @@ __all__ = [
     "decode_float_bits", "round_to_dtype_bits", "validate_layer",
     "dequant", "gemm", "gemm_bias", "gemm_entries", "runtime_perm", "compare", "effective_bits",
     "AWQ_ORDER", "unpack_awq", "pack_awq", "dequant_awq", "gemm_awq",
+    "PLANES", "planar_unpack_rows", "planar_pack_rows", "planar_unpack_cols", "planar_pack_cols",
+    "FORMATS", "dequant_fmt", "gemm_fmt",
 ]
 
 SUPPORTED_BITS = (2, 3, 4, 8)          # [SPEC] QuantizeConfig / GPTQ-001
@@ -397,3 +411,87 @@ def compare(y_bits, out_dtype: str, y_ref) -> dict:
         "max_abs_vs_rne": float(np.max(np.abs(y - y_rne))) if d.size else 0.0,
         "nonfinite": int(np.count_nonzero(~np.isfinite(y))),
     }
+
+
+# ----------------------------------------------------------------------------------------------
+# GPTQ_P planar packing and GPTQ v2 zeros: the same W equation from other encodings
+# ----------------------------------------------------------------------------------------------
+
+PLANES = {2: (2,), 3: (2, 1), 4: (4,), 5: (4, 1), 6: (4, 2), 7: (4, 2, 1), 8: (8,)}   # [PLN]
+
+
+def planar_unpack_rows(words, bits: int) -> np.ndarray:
+    """int32 [K * bits / 32, C] -> codes [K, C] (int64) ([PLN]): rows bits*t .. bits*t + bits - 1
+    hold codes 32t .. 32t + 31, plane by plane (PLANES[bits], low bits first); a plane of width w
+    takes w of those rows, code j's field at bit w*(j % (32/w)) of its row j // (32/w)."""
+    u = to_u32(words)
+    R, C = u.shape
+    if bits not in PLANES or R % bits:
+        raise ValueError("planar rows must hold whole 32-code blocks")
+    out = np.zeros((R // bits * 32, C), dtype=np.int64)
+    for t in range(R // bits):
+        row, low = bits * t, 0
+        for w in PLANES[bits]:
+            per = 32 // w
+            for j in range(32):
+                field = (u[row + j // per] >> (w * (j % per))) & ((1 << w) - 1)
+                out[32 * t + j] |= field.astype(np.int64) << low
+            row += w
+            low += w
+    return out
+
+
+def planar_pack_rows(codes, bits: int) -> np.ndarray:
+    """Inverse of planar_unpack_rows (used by the pins and generators of fixtures only)."""
+    q = np.asarray(codes, dtype=np.int64)
+    K, C = q.shape
+    if bits not in PLANES or K % 32 or q.min(initial=0) < 0 or q.max(initial=0) >= (1 << bits):
+        raise ValueError("codes must fill whole 32-code blocks and fit the width")
+    out = np.zeros((K * bits // 32, C), dtype=np.int64)
+    for t in range(K // 32):
+        row, low = bits * t, 0
+        for w in PLANES[bits]:
+            per = 32 // w
+            for j in range(32):
+                field = (q[32 * t + j] >> low) & ((1 << w) - 1)
+                out[row + j // per] |= field << (w * (j % per))
+            row += w
+            low += w
+    return to_i32(out)
+
+
+def planar_unpack_cols(words, bits: int) -> np.ndarray:
+    return planar_unpack_rows(np.asarray(words).T, bits).T
+
+
+def planar_pack_cols(codes, bits: int) -> np.ndarray:
+    return planar_pack_rows(np.asarray(codes).T, bits).T.copy()
+
+
+FORMATS = ("gptq", "gptq_v2", "gptq_p")
+
+
+def dequant_fmt(fmt: str, qweight, qzeros, scales, scales_dtype: str, g_idx, bits: int) -> np.ndarray:
+    """W[n, k] = (code[k, n] - zero[g, n]) * scale[g, n], g = g_idx[k], in float64, with codes and
+    zeros read as the checkpoint format stores them:
+      gptq     continuous words, zero = stored + 1 (v1)            -- dequant()
+      gptq_v2  continuous words, zero = stored ([V2])
+      gptq_p   planar words ([PLN]), zero = stored + 1 (v1 reading)."""
+    if fmt == "gptq":
+        return dequant(qweight, qzeros, scales, scales_dtype, g_idx, bits)
+    if fmt == "gptq_v2":
+        code, zero = unpack_codes(qweight, bits), unpack_along_cols(qzeros, bits)
+    elif fmt == "gptq_p":
+        code, zero = planar_unpack_rows(qweight, bits), planar_unpack_cols(qzeros, bits) + 1
+    else:
+        raise ValueError(fmt)
+    s = decode_float_bits(scales, scales_dtype)
+    g = np.asarray(g_idx, dtype=np.int64)
+    return ((code.astype(np.float64) - zero.astype(np.float64)[g]) * s[g]).T.copy()
+
+
+def gemm_fmt(fmt: str, x_bits, x_dtype: str, qweight, qzeros, scales, scales_dtype: str, g_idx,
+             bits: int) -> np.ndarray:
+    """y_ref = x . W^T for a layer of checkpoint format `fmt`, float64."""
+    x = decode_float_bits(x_bits, x_dtype)
+    return x @ dequant_fmt(fmt, qweight, qzeros, scales, scales_dtype, g_idx, bits).T

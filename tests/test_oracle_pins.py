@@ -411,3 +411,111 @@ def test_awq_layer_equals_the_gptq_layer_of_the_same_codes():
     ya = o.gemm_awq(x, "bf16", o.pack_awq(codes), o.pack_awq(zeros), scales, "f16", gs)
     yg = o.gemm(x, "bf16", o.pack_codes(codes, 4), o.pack_zeros(zeros, 4), scales, "f16", g_idx, 4)
     assert np.allclose(ya, yg, rtol=1e-13, atol=1e-13)
+
+
+# ---- GPTQ_P planar packing and GPTQ v2 zeros ------------------------------------------------------
+
+def test_planar_words_unpack_to_stated_codes():
+    """Hand-derived words ("Kernel Backends Reference", section "Planar packing")."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "planar_words.json")))
+    for case in g["cases"]:
+        bits = case["bits"]
+        words = np.array([[int(h, 16)] for h in case["words_hex"]], dtype=np.uint32)
+        assert o.planar_unpack_rows(o.to_i32(words), bits)[:, 0].tolist() == case["codes"], case["why"]
+        assert o.to_u32(o.planar_pack_rows(np.array(case["codes"])[:, None], bits)).ravel().tolist() == \
+            [int(h, 16) for h in case["words_hex"]], case["why"]
+        # the same rule along the output dimension (qzeros)
+        assert o.planar_unpack_cols(o.to_i32(words.T), bits)[0].tolist() == case["codes"]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_single_plane_widths_are_continuous_packing(bits):
+    """The page states that single-plane 2/4/8-bit layouts are bit-identical to continuous ones."""
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, 1 << bits, size=(96, 5))
+    assert np.array_equal(o.planar_pack_rows(codes, bits), o.pack_codes(codes, bits))
+    words = rng.integers(0, 2 ** 32, size=(3 * bits, 4), dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(o.planar_unpack_rows(o.to_i32(words), bits), o.unpack_codes(o.to_i32(words), bits))
+
+
+def test_planar_3bit_differs_from_continuous_3bit():
+    """...and that planar 3-bit is not the continuous cross-word 3-bit layout."""
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 8, size=(64, 3))
+    assert not np.array_equal(o.planar_pack_rows(codes, 3), o.pack_codes(codes, 3))
+    assert np.array_equal(o.planar_unpack_rows(o.planar_pack_rows(codes, 3), 3), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_planar_single_hot_and_round_trip(bits):
+    """Each bit of each code lands in exactly one bit of one word of its own 32-code block, its
+    plane's words come in low-to-high order, and every word pattern is a valid encoding."""
+    lows = np.cumsum((0,) + o.PLANES[bits])               # first code bit of each plane
+    for j in range(32):
+        for b in range(bits):
+            c = np.zeros((64, 1), dtype=np.int64)
+            c[32 + j, 0] = 1 << b
+            w = o.to_u32(o.planar_pack_rows(c, bits))[:, 0]
+            assert np.count_nonzero(w) == 1 and bin(int(w.max())).count("1") == 1
+            row = int(np.nonzero(w)[0][0])
+            p = int(np.searchsorted(lows, b, side="right") - 1)
+            wp = o.PLANES[bits][p]
+            assert row == bits + lows[p] + j // (32 // wp)        # second block, plane p's rows
+            assert int(w[row]) == 1 << (wp * (j % (32 // wp)) + b - lows[p])
+    rng = np.random.default_rng(100 + bits)
+    words = rng.integers(0, 2 ** 32, size=(2 * bits, 6), dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(o.to_u32(o.planar_pack_rows(o.planar_unpack_rows(o.to_i32(words), bits), bits)), words)
+
+
+@pytest.mark.parametrize("bits", [3, 5, 6, 7])
+def test_planar_dequant_matches_exact_rationals(bits):
+    """GPTQ_P W = (code - (stored + 1)) * scale, brute force in exact rationals, act-order g_idx."""
+    rng = np.random.default_rng(20 + bits)
+    K, N, gs = 64, 32, 32
+    codes = rng.integers(0, 1 << bits, size=(K, N))
+    stored = rng.integers(0, 1 << bits, size=(K // gs, N))
+    g_idx = (rng.permutation(K) // gs).astype(np.int32)
+    scales = gi.to_bf16_bits(rng.uniform(0.005, 0.02, size=(K // gs, N)))
+    W = o.dequant_fmt("gptq_p", o.planar_pack_rows(codes, bits), o.planar_pack_cols(stored, bits), scales, "bf16",
+                      g_idx, bits)
+    s = o.decode_float_bits(scales, "bf16")
+    for n in range(N):
+        for k in range(K):
+            g = int(g_idx[k])
+            assert Fraction(float(W[n, k])) == (int(codes[k, n]) - int(stored[g, n]) - 1) * Fraction(float(s[g, n]))
+    x = gi.make_x(2, K, "f16", seed=bits)
+    y = o.gemm_fmt("gptq_p", x, "f16", o.planar_pack_rows(codes, bits), o.planar_pack_cols(stored, bits), scales,
+                   "bf16", g_idx, bits)
+    xf = o.decode_float_bits(x, "f16")
+    for m in range(2):
+        for n in range(0, N, 7):
+            exact = sum(Fraction(float(xf[m, k])) * Fraction(float(W[n, k])) for k in range(K))
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 60)
+
+
+def test_planar_layer_of_a_single_plane_width_equals_the_gptq_layer():
+    L = gi.make_layer(128, 64, 4, 32, desc_act=True, seed=31)
+    assert np.array_equal(o.dequant_fmt("gptq_p", L.qweight, L.qzeros, L.scales, "f16", L.g_idx, 4),
+                          o.dequant(L.qweight, L.qzeros, L.scales, "f16", L.g_idx, 4))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_v2_zeros_are_stored_as_they_are(bits):
+    """A v2 layer storing z equals the v1 layer storing z - 1 (the same logical zero), and a v2
+    zero of 0 is representable: W = code * scale there."""
+    rng = np.random.default_rng(40 + bits)
+    K, N, gs = 96, 32, 32
+    L = gi.make_layer(K, N, bits, gs, desc_act=True, seed=40 + bits)
+    zeros = rng.integers(0, 1 << bits, size=(K // gs, N))
+    zeros[0, :3] = 0
+    W2 = o.dequant_fmt("gptq_v2", L.qweight, o.pack_along_cols(zeros, bits), L.scales, "f16", L.g_idx, bits)
+    codes = o.unpack_codes(L.qweight, bits)
+    s = o.decode_float_bits(L.scales, "f16")
+    g = L.g_idx.astype(np.int64)
+    assert np.array_equal(W2, ((codes - zeros[g]) * s[g]).T)
+    ok = zeros[:, :] >= 1                                   # where v1 can express the same zero
+    W1 = o.dequant(L.qweight, o.pack_along_cols(np.where(ok, zeros - 1, 0), bits), L.scales, "f16", L.g_idx, bits)
+    cols = np.all(ok, axis=0)
+    assert cols.sum() > 0 and np.array_equal(W1[cols], W2[cols])
+    first = np.nonzero(g == 0)[0]
+    assert np.array_equal(W2[:3][:, first], (codes[first][:, :3] * s[0, :3]).T)
