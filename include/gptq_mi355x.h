@@ -43,7 +43,8 @@ typedef enum {
   GPTQ_E_SHAPE = 2,       /* rule GPTQ-002 / GPTQ-003: qweight, qzeros or scales shape wrong,
                              in_features or out_features not a multiple of 32 */
   GPTQ_E_GIDX = 3,        /* rule GPTQ-004: g_idx length wrong or an index outside [0, G) */
-  GPTQ_E_UNSUPPORTED = 4, /* rule GPTQ-001 (bits not 2/3/4/8), GPTQ-005 (a private layout such as
+  GPTQ_E_UNSUPPORTED = 4, /* rule GPTQ-001 (bits not 2/3/4/8, or 2..8 for GPTQ_P), GPTQ-005 (a
+                             private layout such as
                              marlin), an AWQ_GEMM layer that is not 4-bit or sets desc_act,
                              group_size not -1 and not a positive multiple of 32, or a
                              g_idx whose groups are not whole (its stable sort is not j // gs) */
@@ -55,20 +56,29 @@ typedef enum {
 
 typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype;
 
-/* Checkpoint formats.  GPTQ_FORMAT_GPTQ (AutoGPTQ "cuda" pack, v1 stored-minus-one zeros) and
- * GPTQ_FORMAT_AWQ_GEMM are accepted and repack into the same runtime layout; MARLIN and GPTQ_V2
- * are named so that callers can pass what the checkpoint declares and be refused with
- * GPTQ_E_UNSUPPORTED (rule GPTQ-005). */
+/* Checkpoint formats.  Every accepted format repacks into the same runtime layout; MARLIN (a
+ * private runtime layout) is named so that callers can pass what the checkpoint declares and be
+ * refused with GPTQ_E_UNSUPPORTED (rule GPTQ-005). */
 typedef enum {
-  GPTQ_FORMAT_GPTQ = 0,
+  GPTQ_FORMAT_GPTQ = 0,      /* AutoGPTQ "cuda" pack, 2/3/4/8-bit, v1 stored-minus-one zeros    */
   GPTQ_FORMAT_MARLIN = 1,
+  /* The same words with the corrected zeros newer tools call gptq_v2 ("39. Quantized
+   * checkpoints ...", section "GPTQ"; "Kernel Backends Reference", section "Packed storage and
+   * execution concepts"): zero = the stored field, no "minus one".  2/3/4/8-bit. */
   GPTQ_FORMAT_GPTQ_V2 = 2,
   /* AutoAWQ GEMM tensors ("39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes",
    * section "AWQ"): 4-bit only; qweight int32 [K, N/8] and qzeros int32 [G, N/8] hold eight
    * fields along the OUTPUT dimension in the order 0 2 4 6 1 3 5 7 (field j of word w is output
    * 8w + order[j]); zeros are stored as they are (no "minus one"); scales [G, N]; sequential
    * groups g = k / group_size, so no g_idx.  Same W = (code - zero) * scale, same runtime layout. */
-  GPTQ_FORMAT_AWQ_GEMM = 3
+  GPTQ_FORMAT_AWQ_GEMM = 3,
+  /* GPTQ_P planar words ("Kernel Backends Reference", section "Planar packing"), 2..8-bit: each
+   * 32 codes take `bits` consecutive words (qweight rows, qzeros columns), one group of words per
+   * plane of widths 2 | 2+1 | 4 | 4+1 | 4+2 | 4+2+1 | 8, low bits first; inside a plane the
+   * fields are packed continuously, low bits first.  Zeros keep the v1 "minus one".  Shapes as
+   * GPTQ.  5/6/7-bit codes are widened to the 8-bit runtime layout (exact; 8 / bits of the
+   * checkpoint's bytes per call). */
+  GPTQ_FORMAT_GPTQ_P = 4
 } gptq_format;
 
 /* Kernel family for gptq_gemm.  AUTO picks SKINNY for M <= 16 (M <= 32 when K spans more than
@@ -81,7 +91,7 @@ typedef enum { GPTQ_PATH_AUTO = 0, GPTQ_PATH_SKINNY = 1, GPTQ_PATH_TILED = 2 } g
 typedef struct {
   int32_t in_features;       /* K                                                              */
   int32_t out_features;      /* N                                                              */
-  int32_t bits;              /* 2, 3, 4 or 8 (GPTQ-001)                                        */
+  int32_t bits;              /* 2, 3, 4 or 8 (GPTQ-001); 2 .. 8 for GPTQ_P                     */
   int32_t group_size;        /* -1 = one group over all K, else a positive multiple of 32      */
   int32_t desc_act;          /* informational; act-order is taken from g_idx itself (must be 0
                                 for AWQ_GEMM, which has no g_idx)                              */

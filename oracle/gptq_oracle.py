@@ -237,19 +237,29 @@ def round_to_dtype_bits(y, dtype: str) -> np.ndarray:
 # ----------------------------------------------------------------------------------------------
 
 def validate_layer(K, N, bits, group_size, qweight_shape, qzeros_shape, scales_shape, g_idx=None,
-                   checkpoint_format="gptq") -> str:
-    """Return "ok", "unsupported", "shape" or "gidx" for a checkpoint layer."""
-    if bits not in SUPPORTED_BITS:                                      # GPTQ-001
+                   checkpoint_format="gptq", desc_act=False) -> str:
+    """Return "ok", "unsupported", "shape" or "gidx" for a checkpoint layer.  Formats: "gptq"
+    and "gptq_v2" (2/3/4/8-bit, [SPEC] shapes), "gptq_p" (2..8-bit, the same shapes: `bits` words
+    per 32 codes, [PLN]), "awq_gemm" (4-bit, qweight [K, N/8], qzeros [G, N/8], no g_idx and no
+    act-order, [AWQ]); anything else (a private layout such as marlin) is GPTQ-005."""
+    fmt = checkpoint_format
+    if fmt not in ("gptq", "gptq_v2", "gptq_p", "awq_gemm"):            # GPTQ-005
         return "unsupported"
-    if checkpoint_format != "gptq":                                     # GPTQ-005
+    allowed = tuple(range(2, 9)) if fmt == "gptq_p" else ((4,) if fmt == "awq_gemm" else SUPPORTED_BITS)
+    if bits not in allowed or (fmt == "awq_gemm" and desc_act):         # GPTQ-001
         return "unsupported"
     if group_size != -1 and (group_size <= 0 or group_size % 32):       # reading: gs multiple of 32
         return "unsupported"
-    if K <= 0 or K % 32 or tuple(qweight_shape) != (K // 32 * bits, N):  # GPTQ-002
+    if K <= 0 or K % 32 or N <= 0 or N % 32:                            # GPTQ-002
         return "shape"
     G = num_groups(K, group_size)
-    if N <= 0 or N % 32 or tuple(qzeros_shape) != (G, N // 32 * bits):  # GPTQ-003
-        return "shape"
+    if fmt == "awq_gemm":
+        if tuple(qweight_shape) != (K, N // 8) or tuple(qzeros_shape) != (G, N // 8):
+            return "shape"
+        if g_idx is not None:
+            return "gidx"
+    elif tuple(qweight_shape) != (K // 32 * bits, N) or tuple(qzeros_shape) != (G, N // 32 * bits):
+        return "shape"                                                  # GPTQ-002 / GPTQ-003
     if tuple(scales_shape) != (G, N):                                   # [SPEC] GptqLayer scales
         return "shape"
     if g_idx is not None:

@@ -73,6 +73,11 @@ def test_example_header_rules_match_the_oracle():
         (dict(qz=(8, 5)), g, "shape"),
         (dict(sc=(8, 31)), g, "shape"),
         (dict(fmt="marlin"), g, "unsupported"),
+        (dict(fmt="gptq_v2"), g, "ok"),
+        (dict(fmt="gptq_p"), g, "ok"),
+        (dict(fmt="gptq_p", bits=5), g, "ok"),
+        (dict(fmt="gptq_p", bits=9), g, "unsupported"),
+        (dict(fmt="gptq_v2", bits=6), g, "unsupported"),
         (dict(gs=48), None, "unsupported"),
     ]
     for kw, gi_, want in cases:
@@ -96,11 +101,12 @@ def test_validation_agrees_with_oracle_on_random_mutations():
     for trial in range(400):
         K = int(rng.choice([64, 96, 256, 288, 4096]))
         N = int(rng.choice([32, 64, 96, 128]))
-        bits = int(rng.choice([2, 3, 4, 8, 5, 1]))
+        bits = int(rng.choice([2, 3, 4, 8, 5, 6, 7, 1, 9]))
+        fmt = str(rng.choice(["gptq", "gptq", "gptq_v2", "gptq_p", "awq_gemm", "marlin"]))
         gs = int(rng.choice([-1, 32, 64, 128, 96, 48, 0]))
         G = o.num_groups(K, gs) if (gs == -1 or gs > 0) else 1
-        qw = [K // 32 * bits, N]
-        qz = [G, N // 32 * bits]
+        qw = [K, N // 8] if fmt == "awq_gemm" else [K // 32 * bits, N]
+        qz = [G, N // 8] if fmt == "awq_gemm" else [G, N // 32 * bits]
         sc = [G, N]
         which = rng.integers(0, 6)
         if which == 1: qw[0] += int(rng.choice([-1, 1]))
@@ -115,9 +121,11 @@ def test_validation_agrees_with_oracle_on_random_mutations():
         if which == 5 and G > 1:
             g[0], g[-1] = g[-1], 0
             g[1] = g[-1]
-        d = wq.make_desc(K, N, bits, gs, wq.F16, qw, qz, sc, K)
-        ref = o.validate_layer(K, N, bits, gs, qw, qz, sc, g)
-        assert wq.validate(d, g) == CODES[ref], (K, N, bits, gs, which, ref)
+        if fmt == "awq_gemm" and rng.random() < 0.7:
+            g = None                                 # an AWQ layer has no g_idx
+        d = wq.make_desc(K, N, bits, gs, wq.F16, qw, qz, sc, K if g is not None else 0, checkpoint_format=fmt)
+        ref = o.validate_layer(K, N, bits, gs, qw, qz, sc, g, checkpoint_format=fmt)
+        assert wq.validate(d, g) == CODES[ref], (K, N, bits, gs, fmt, which, ref)
 
 
 def test_runtime_layout_map_is_a_bijection():

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi3
 STATUS = {0: "OK", 1: "E_INVALID_ARG", 2: "E_SHAPE", 3: "E_GIDX", 4: "E_UNSUPPORTED", 5: "E_HIP",
           6: "E_OOM", 7: "E_WORKSPACE", 8: "E_DEVICE"}
 F16, BF16, F32 = 0, 1, 2
-FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2, "awq_gemm": 3}
+FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2, "awq_gemm": 3, "gptq_p": 4}
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
 # Every symbol include/gptq_mi355x.h declares.
@@ -229,7 +229,8 @@ def repack(qweight, qzeros, scales, g_idx=None, *, bits, group_size, desc_act=Fa
     """Build the runtime layout from checkpoint tensors on the current GPU (int32 qweight/qzeros,
     fp16/bf16/fp32 scales, optional int32 g_idx).  The inputs may be freed afterwards.
     checkpoint_format "awq_gemm" reads AutoAWQ GEMM tensors instead (4-bit, qweight [K, N/8],
-    qzeros [G, N/8], zeros as stored, no g_idx)."""
+    qzeros [G, N/8], zeros as stored, no g_idx), "gptq_v2" GPTQ words with zeros as stored, and
+    "gptq_p" GPTQ_P planar words (2..8-bit, v1 zeros)."""
     import torch
     lib = load_library()
     for name, t in (("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
@@ -241,7 +242,7 @@ def repack(qweight, qzeros, scales, g_idx=None, *, bits, group_size, desc_act=Fa
     if awq:  # AutoAWQ GEMM: qweight [K, N / 8], eight 4-bit fields per word along the outputs
         K, N = qweight.shape[0], qweight.shape[1] * 8
     else:
-        K = qweight.shape[0] * 32 // bits if bits in (2, 3, 4, 8) else 0
+        K = qweight.shape[0] * 32 // bits if 2 <= bits <= 8 else 0
         N = qweight.shape[1]
     if g_idx is not None:
         if g_idx.dtype != torch.int32 or not g_idx.is_cuda or not g_idx.is_contiguous():

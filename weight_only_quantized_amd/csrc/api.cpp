@@ -51,12 +51,21 @@ static bool is_gfx950_device(int dev) {
 }
 
 // Shape/format checks that need no g_idx values.
+static RepackSource repack_source(int32_t format) {
+  switch (format) {
+    case GPTQ_FORMAT_AWQ_GEMM: return kSrcAwqGemm;
+    case GPTQ_FORMAT_GPTQ_V2: return kSrcGptqV2;
+    case GPTQ_FORMAT_GPTQ_P: return kSrcGptqPlanar;
+    default: return kSrcGptq;
+  }
+}
+
 static gptq_status validate_desc(const gptq_layer_desc* d) {
   if (!d || d->reserved != 0) return GPTQ_E_INVALID_ARG;
-  const int b = d->bits;
-  if (b != 2 && b != 3 && b != 4 && b != 8) return GPTQ_E_UNSUPPORTED;           // GPTQ-001
-  const bool awq = d->checkpoint_format == GPTQ_FORMAT_AWQ_GEMM;
-  if (d->checkpoint_format != GPTQ_FORMAT_GPTQ && !awq) return GPTQ_E_UNSUPPORTED;  // GPTQ-005
+  const int b = d->bits, f = d->checkpoint_format;
+  const bool awq = f == GPTQ_FORMAT_AWQ_GEMM, planar = f == GPTQ_FORMAT_GPTQ_P;
+  if (f != GPTQ_FORMAT_GPTQ && f != GPTQ_FORMAT_GPTQ_V2 && !awq && !planar) return GPTQ_E_UNSUPPORTED;  // GPTQ-005
+  if (planar ? (b < 2 || b > 8) : (b != 2 && b != 3 && b != 4 && b != 8)) return GPTQ_E_UNSUPPORTED;  // GPTQ-001
   if (awq && (b != 4 || d->desc_act)) return GPTQ_E_UNSUPPORTED;                // 4-bit, sequential groups
   if (d->scales_dtype != GPTQ_F16 && d->scales_dtype != GPTQ_BF16 && d->scales_dtype != GPTQ_F32)
     return GPTQ_E_INVALID_ARG;
@@ -174,7 +183,9 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
   std::memset(L, 0, sizeof(*L));
   L->magic = GQ_MAGIC;
   L->device = dev;
-  L->K = K; L->N = N; L->bits = desc->bits; L->group_size = desc->group_size;
+  L->K = K; L->N = N; L->group_size = desc->group_size;
+  L->ckpt_bits = desc->bits;
+  L->bits = desc->bits >= 5 && desc->bits <= 7 ? 8 : desc->bits;   // 5/6/7-bit codes run as 8-bit
   L->gs_eff = desc->group_size == -1 ? K : desc->group_size;
   L->G = groups_of(K, desc->group_size);
   L->Kp = Kp; L->KC = Kp / kChunkK; L->CT = N / kTileN;
@@ -197,7 +208,7 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
   L->bytes = (int64_t)(wq_bytes + meta_n * 4 + s32_bytes + (has_perm ? perm_bytes : 0));
   e = hipMemcpyAsync(L->perm, perm_host.data(), perm_bytes, hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
-    e = launch_repack(L, qweight, qzeros, scales, desc->checkpoint_format == GPTQ_FORMAT_AWQ_GEMM ? 1 : 0, s);
+    e = launch_repack(L, qweight, qzeros, scales, repack_source(desc->checkpoint_format), s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     free_layer(L);
@@ -327,7 +338,7 @@ gptq_status gptq_info(gptq_handle_t h, gptq_handle_info* info) {
   if (!info) return GPTQ_E_INVALID_ARG;
   info->in_features = h->K;
   info->out_features = h->N;
-  info->bits = h->bits;
+  info->bits = h->ckpt_bits;
   info->group_size = h->group_size;
   info->groups = h->G;
   info->padded_in_features = h->Kp;

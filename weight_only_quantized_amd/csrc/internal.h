@@ -12,7 +12,8 @@
 struct gptq_layer {
   uint32_t magic;
   int device;
-  int K, N, bits, group_size, gs_eff, G, Kp, KC, CT;
+  int K, N, bits, group_size, gs_eff, G, Kp, KC, CT;   // bits: runtime code width (2/3/4/8)
+  int ckpt_bits;      // the checkpoint's code width (bits, or 5/6/7 for planar layers run as 8)
   int scales_dtype;   // gptq_dtype of the stored scales
   int has_perm;       // 1 when the sorted order is not the identity
   int seg_steps;      // MFMA K steps (of 32) per scale-fixup segment: 4 or 1
@@ -29,10 +30,15 @@ namespace gq {
 // Set the calling thread's last HIP error and return GPTQ_E_HIP.
 gptq_status hip_fail(hipError_t e);
 
-// Repack kernels (repack.hip).
-// awq: the tensors are AutoAWQ GEMM packed (fields along the output dimension, zeros as stored).
+// Repack kernels (repack.hip), by how the checkpoint encodes codes and zeros:
+enum RepackSource {
+  kSrcGptq = 0,        // continuous words, v1 zeros (stored = zero - 1)
+  kSrcAwqGemm = 1,     // AutoAWQ GEMM: 4-bit fields along the output dimension, zeros as stored
+  kSrcGptqV2 = 2,      // continuous words, zeros as stored
+  kSrcGptqPlanar = 3,  // GPTQ_P planar words, v1 zeros
+};
 hipError_t launch_repack(const gptq_layer* L, const int32_t* qweight, const int32_t* qzeros,
-                         const void* scales, int awq, hipStream_t s);
+                         const void* scales, RepackSource src, hipStream_t s);
 
 // Parameters of one gptq_gemm call as the launchers see them.
 struct GemmCall {
