@@ -15,3 +15,4 @@ word layout (no 3-bit bytes are printed on the pages) -- its *upstream byte pari
 is unpinned*.
 """
 from .gptq_oracle import *  # noqa: F401,F403
+from . import gptq_quant_oracle as quant  # noqa: E402,F401  (the GPTQ quantizer: oracle.quant)

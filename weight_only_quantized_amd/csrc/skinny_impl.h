@@ -442,15 +442,24 @@ static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
 template <int BITS, int XT>
 static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
   if (x_fits_lds(a.M, a.Kp)) {
-    if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, 4>(a, seg, s);
+#ifndef GQ_D2
+#define GQ_D2 4
+#define GQ_D3 4
+#endif
+    if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, (BITS == 2 ? GQ_D2 : (BITS == 3 ? GQ_D3 : 4))>(a, seg, s);
     // M = 1 over 32 chunks: two waves per column tile, each a straight-line 16-chunk range with a
     // 4-deep ring, measured 3 % faster on MI355X than four waves of 8 chunks (4096-input layers)
     // the offset operand for bf16 activations (it replaces the bias MFMAs: 4 % on MI355X for the
     // 8192-input layer); fp16 keeps its exact operands (no gain measured)
     constexpr int ONE = XT == 1 && BITS <= 4;
-    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16, ONE>(a, seg, s);
-    if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE>(a, seg, s);
-    return run<BITS, XT, 1, 1, 4, 1, 4>(a, seg, s);
+#ifndef GQ_D2
+#define GQ_D2 4
+#define GQ_D3 4
+#endif
+    constexpr int D1 = BITS == 2 ? GQ_D2 : (BITS == 3 ? GQ_D3 : 4);
+    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, D1, 16, ONE>(a, seg, s);
+    if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, D1, 16, ONE>(a, seg, s);
+    return run<BITS, XT, 1, 1, 4, 1, D1>(a, seg, s);
   }
   if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
   return hipErrorInvalidValue;   // larger M goes to the mid family
