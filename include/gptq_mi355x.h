@@ -51,7 +51,8 @@ typedef enum {
   GPTQ_E_HIP = 5,         /* a HIP runtime call failed (see gptq_last_hip_error) */
   GPTQ_E_OOM = 6,         /* device allocation for the runtime layout failed */
   GPTQ_E_WORKSPACE = 7,   /* workspace smaller than gptq_workspace_size() or not 256-B aligned */
-  GPTQ_E_DEVICE = 8       /* no gfx950 device, or the handle lives on another device */
+  GPTQ_E_DEVICE = 8,      /* no gfx950 device, or the handle lives on another device */
+  GPTQ_E_NUMERIC = 9      /* gptq_quantize: the damped Hessian is not positive definite */
 } gptq_status;
 
 typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype;
@@ -185,6 +186,44 @@ const char* gptq_status_str(gptq_status s);
 
 /* hipError_t behind the calling thread's last GPTQ_E_HIP (0 if none). */
 int32_t gptq_last_hip_error(void);
+
+/* ---- GPTQ quantizer: the step that produces a layer's codes -------------------------------------
+ * "39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes", section "GPTQ".  All tensor
+ * pointers are DEVICE pointers on the current device, row-major; calls are stream-ordered. */
+
+/* H[K, K] (float32) = 2 X^T X / S for calibration inputs x [S, K] (x_dtype F16, BF16 or F32): the
+ * Hessian every output row shares.  Sums in float64, rounded once.  H is overwritten; K <= 32768.
+ * Errors: GPTQ_E_INVALID_ARG (NULL, S or K out of range, bad dtype), GPTQ_E_HIP. */
+gptq_status gptq_hessian(const void* x, int64_t S, int32_t K, int32_t x_dtype, float* H, void* stream);
+
+typedef struct {
+  int32_t bits;        /* 2 .. 8: codes in [0, 2^bits - 1]                                      */
+  int32_t group_size;  /* -1 (one group) or a positive multiple of 32, counted in visiting order */
+  int32_t act_order;   /* 1: visit inputs from the largest H_ii down (desc_act)                  */
+  float damp;          /* fraction of the mean diagonal added to H's diagonal (the page: 0.01)  */
+  int32_t reserved;    /* must be 0                                                             */
+} gptq_quant_params;
+
+/* Device workspace gptq_quantize needs for an [N, K] layer (256-byte aligned). */
+gptq_status gptq_quantize_workspace_size(int32_t N, int32_t K, size_t* bytes);
+
+/* Quantize W [N, K] (float32, rows are outputs) against H [K, K] (float32, e.g. from gptq_hessian)
+ * with the page's GPTQ: never-active inputs (H_ii = 0) zeroed, optional act-order, damped Cholesky
+ * inverse, per-column error feedback through the upper Cholesky factor of H^-1 in blocks of 128
+ * columns with one update product per block, group grids from the corrected weights.  Grid of a
+ * group (a reading; the page names the step only): asymmetric min-max over each row's group values
+ * widened to contain 0: scale = (hi - lo) / (2^bits - 1), zero = round(-lo / scale).
+ * Outputs (device, caller-owned): codes uint8 [N, K] in the ORIGINAL input order, scales float32
+ * [N, G] and zeros int32 [N, G] (the logical zero, 0 .. 2^bits - 1; a zero of 0 needs
+ * GPTQ_FORMAT_GPTQ_V2 to be stored) with G = ceil(K / group_size), g_idx int32 [K] (group of each
+ * input).  W and H are read only.  Synchronises the stream.  Uses rocSOLVER (POTRF, POTRI) and
+ * rocBLAS (SGEMM), loaded on first use.
+ * Errors: GPTQ_E_INVALID_ARG (NULL, reserved != 0, damp outside [0, 1]), GPTQ_E_UNSUPPORTED (bits,
+ * group_size, or the solver libraries not found), GPTQ_E_SHAPE (K not a multiple of 32 or > 16384,
+ * N > 2^20, N * K > 2^31), GPTQ_E_WORKSPACE, GPTQ_E_NUMERIC, GPTQ_E_HIP. */
+gptq_status gptq_quantize(const float* W, const float* H, int32_t N, int32_t K, const gptq_quant_params* params,
+                          uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = wq.load_library()
-    for s in range(9):
+    for s in range(10):
         assert lib.gptq_status_str(s)
     assert lib.gptq_status_str(0) == b"ok"
 

@@ -19,14 +19,15 @@ __all__ = ["LIB_PATH", "GPTQError", "Desc", "Handle", "load_library", "repack", 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi355x.so")
 
 STATUS = {0: "OK", 1: "E_INVALID_ARG", 2: "E_SHAPE", 3: "E_GIDX", 4: "E_UNSUPPORTED", 5: "E_HIP",
-          6: "E_OOM", 7: "E_WORKSPACE", 8: "E_DEVICE"}
+          6: "E_OOM", 7: "E_WORKSPACE", 8: "E_DEVICE", 9: "E_NUMERIC"}
 F16, BF16, F32 = 0, 1, 2
 FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2, "awq_gemm": 3, "gptq_p": 4}
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
 # Every symbol include/gptq_mi355x.h declares.
 symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
-           "gptq_info", "gptq_decode_runtime", "gptq_status_str", "gptq_last_hip_error"]
+           "gptq_info", "gptq_decode_runtime", "gptq_status_str", "gptq_last_hip_error", "gptq_hessian",
+           "gptq_quantize_workspace_size", "gptq_quantize"]
 
 
 class GPTQError(RuntimeError):
@@ -39,6 +40,11 @@ class GPTQError(RuntimeError):
         super().__init__(f"{where}: {msg}")
         self.status = status
         self.name = STATUS.get(status, str(status))
+
+
+class QuantParams(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("act_order", ctypes.c_int32),
+                ("damp", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
 
 class Desc(ctypes.Structure):
@@ -83,8 +89,12 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_status_str.argtypes = [I32]
     lib.gptq_status_str.restype = ctypes.c_char_p
     lib.gptq_last_hip_error.argtypes = []
+    lib.gptq_hessian.argtypes = [P, I64, I32, I32, P, P]
+    lib.gptq_quantize_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
+    lib.gptq_quantize.argtypes = [P, P, I32, I32, ctypes.POINTER(QuantParams), P, P, P, P, P, SZ, P]
     for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
-              "gptq_info", "gptq_decode_runtime", "gptq_last_hip_error"):
+              "gptq_info", "gptq_decode_runtime", "gptq_last_hip_error", "gptq_hessian",
+              "gptq_quantize_workspace_size", "gptq_quantize"):
         getattr(lib, f).restype = I32
     _lib = lib
     return lib
@@ -256,3 +266,47 @@ def repack(qweight, qzeros, scales, g_idx=None, *, bits, group_size, desc_act=Fa
     if st:
         raise GPTQError(st, "gptq_repack", lib)
     return Handle(lib, out, K, N, bits, group_size)
+
+
+def hessian(x, stream=None):
+    """H = 2 X^T X / S (float32 [K, K]) of calibration inputs x [S, K] (fp16/bf16/fp32 GPU tensor)."""
+    import torch
+    lib = load_library()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous 2-D GPU tensor")
+    S, K = x.shape
+    H = torch.empty((K, K), dtype=torch.float32, device=x.device)
+    st = lib.gptq_hessian(x.data_ptr(), S, K, _dtype_code(x.dtype), H.data_ptr(), _stream_ptr(stream))
+    if st:
+        raise GPTQError(st, "gptq_hessian", lib)
+    return H
+
+
+def quantize(W, H, *, bits=4, group_size=128, act_order=False, damp=0.01, stream=None):
+    """GPTQ-quantize W [N, K] (float32 GPU tensor) against H [K, K] on the GPU.  Returns (codes uint8
+    [N, K], scales float32 [N, G], zeros int32 [N, G], g_idx int32 [K]) as torch GPU tensors."""
+    import torch
+    lib = load_library()
+    for name, t in (("W", W), ("H", H)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    N, K = W.shape
+    if tuple(H.shape) != (K, K):
+        raise ValueError("H must be [K, K]")
+    G = 1 if group_size == -1 else -(-K // group_size)
+    dev = W.device
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, G), dtype=torch.float32, device=dev)
+    zeros = torch.empty((N, G), dtype=torch.int32, device=dev)
+    g_idx = torch.empty((K,), dtype=torch.int32, device=dev)
+    n = ctypes.c_size_t(0)
+    st = lib.gptq_quantize_workspace_size(N, K, ctypes.byref(n))
+    if st:
+        raise GPTQError(st, "gptq_quantize_workspace_size", lib)
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    p = QuantParams(bits, group_size, int(bool(act_order)), float(damp), 0)
+    st = lib.gptq_quantize(W.data_ptr(), H.data_ptr(), N, K, ctypes.byref(p), codes.data_ptr(), scales.data_ptr(),
+                           zeros.data_ptr(), g_idx.data_ptr(), ws.data_ptr(), n.value, _stream_ptr(stream))
+    if st:
+        raise GPTQError(st, "gptq_quantize", lib)
+    return codes, scales, zeros, g_idx

@@ -415,6 +415,7 @@ const char* gptq_status_str(gptq_status s) {
     case GPTQ_E_HIP: return "HIP runtime error";
     case GPTQ_E_OOM: return "out of device memory";
     case GPTQ_E_WORKSPACE: return "workspace too small or misaligned";
+    case GPTQ_E_NUMERIC: return "the damped Hessian is not positive definite";
     case GPTQ_E_DEVICE: return "no gfx950 device, or handle used on another device";
   }
   return "unknown status";
