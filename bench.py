@@ -239,6 +239,33 @@ def extra_workloads():
     return out
 
 
+def time_quantize(K, N, S, bits, gs, act, reps=3):
+    """Wall time of the GPU quantizer on one layer: Hessian of S calibration rows, then GPTQ."""
+    import numpy as np
+    import torch
+    import gptq_inputs as gi
+    import weight_only_quantized_amd as wq
+    x = torch.from_numpy(gi.make_calib(S, K, "bf16", seed=K + S).view(np.int16).copy()).cuda().view(torch.bfloat16)
+    W = torch.from_numpy(gi.make_weight(N, K, seed=N + K)).cuda()
+    wq.quantize(W, wq.hessian(x), bits=bits, group_size=gs, act_order=act)       # loads the solver libraries
+    th, tq = [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        H = wq.hessian(x)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wq.quantize(W, H, bits=bits, group_size=gs, act_order=act)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        th.append(t1 - t0)
+        tq.append(t2 - t1)
+    g = "g-1" if gs == -1 else f"g{gs}"
+    return {"workload": f"quantize_{K}x{N}_S{S}_b{bits}_{g}" + ("_actorder" if act else ""),
+            "hessian_ms": round(min(th) * 1e3, 3), "quantize_ms": round(min(tq) * 1e3, 3),
+            "ms_per_layer": round((min(th) + min(tq)) * 1e3, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,6 +332,10 @@ def main():
                                    "kernel": "gq::tiled_kernel<4,1,16,2,4,8>", "algorithmic_flops_per_launch": fl}
             extra.append(rec)
             print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
+        # the step before the path: GPTQ on the GPU for the same 4096 x 14336 layer
+        rec = time_quantize(4096, 14336, 512, 4, 128, True)
+        extra.append(rec)
+        print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_oracle_baseline(w)
     line = {
         "metric": "GPTQ-W4A16 linear: us/call + achieved TB/s (M=1) and TFLOP/s (M=4096) vs roofline",

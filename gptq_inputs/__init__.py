@@ -17,7 +17,8 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Layer", "AwqLayer", "make_layer", "make_awq_layer", "make_x", "make_bias", "to_f16_bits",
+__all__ = ["Layer", "AwqLayer", "make_layer", "make_awq_layer", "make_x", "make_bias", "make_weight", "make_calib",
+           "to_f16_bits",
            "to_bf16_bits", "WORKLOADS", "seed_for"]
 
 
@@ -110,6 +111,20 @@ def make_awq_layer(K, N, group_size, scales_dtype="f16", seed=0, scale_lo=0.005,
     qzeros = rng.integers(0, 2 ** 32, size=(G, N // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
     scales = _round(rng.uniform(scale_lo, scale_hi, size=(G, N)), scales_dtype)
     return AwqLayer(K, N, group_size, qweight, qzeros, scales, scales_dtype)
+
+
+def make_weight(N, K, seed=0, std=0.02) -> np.ndarray:
+    """A float layer weight [N, K] ~ N(0, std^2), float32 (the quantizer's input)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal((N, K)) * std).astype(np.float32)
+
+
+def make_calib(S, K, dtype="bf16", seed=0) -> np.ndarray:
+    """Calibration activations [S, K] with correlated inputs: z A with z ~ N(0, 1) and
+    A = I + N(0, 0.25 / K) entries, rounded to the activation dtype (bit patterns)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = rng.standard_normal((K, K)) * (0.5 / np.sqrt(K)) + np.eye(K)
+    return _round(rng.standard_normal((S, K)) @ A, dtype)
 
 
 def make_x(M, K, dtype="f16", seed=0) -> np.ndarray:

@@ -37,11 +37,7 @@ def say(*a):
 
 
 def calib(S, K, seed, dtype="bf16"):
-    """Correlated synthetic calibration inputs, rounded to the activation dtype (bit patterns)."""
-    rng = np.random.default_rng(seed)
-    A = rng.standard_normal((K, K)) * (0.5 / np.sqrt(K)) + np.eye(K)
-    X = rng.standard_normal((S, K)) @ A
-    return gi.to_bf16_bits(X) if dtype == "bf16" else gi.to_f16_bits(X)
+    return gi.make_calib(S, K, dtype, seed)
 
 
 def to_dev(a, tag):
