@@ -7,6 +7,8 @@ package smoke check and the CPU-baseline leg of the benchmark may use it.
 It is a plain, slow, obviously-correct definition of what the GPU path computes:
 unpack the int32 words, dequantise in float64 with W[n, k] = (code - zero) * scale,
 and multiply in float64.  See ``gptq_oracle`` for the per-function citations.
+``gptq_quant_oracle`` (``oracle.quant``) is the GPTQ quantizer, the step before the path, in the
+page's float32 steps; its pins are in ``tests/test_quant_oracle_pins.py``.
 
 Parity status: every function in ``gptq_oracle`` is pinned by the not-gpu tests in
 ``tests/test_oracle_pins.py``.  One reading is pinned only against itself and the
