@@ -63,7 +63,11 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // bias + code with no zero subtraction (build_b_offset), and the term -(bias + zero) * sum_k x[k]
 // of each chunk is applied to the fp32 partial instead; each wave sums its chunks of x once while
 // staging them and keeps the sums in LDS.  Only row 0 of the accumulators is carried.
-template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH, int ONE = 0>
+// F32S: the layer's scales are float32 (a parallel array of scale bits); otherwise the 16-bit scale
+// sits in the metadata record and no second load is issued per chunk (2 % on the 8192-input M = 1
+// and M = 4 calls on MI355X).
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH, int ONE = 0,
+          int F32S = 1>
 __global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) __attribute__((amdgpu_waves_per_eu(2)))
 skinny_kernel(const SkinnyArgs a) {
   static_assert(!ONE || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
@@ -127,7 +131,8 @@ skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
         c.rec[i][s] = load_b32(rm[i], voff_m, (uint32_t)g * 64u);
-        c.s32[i][s] = load_b32(rs[i], voff_m, (uint32_t)g * 64u);   // zero-size resource unless f32
+        if constexpr (F32S) c.s32[i][s] = load_b32(rs[i], voff_m, (uint32_t)g * 64u);
+        else c.s32[i][s] = 0u;
       }
     }
   };
@@ -413,7 +418,7 @@ inline bool x_fits_lds(int64_t M, int Kp) {
 // L2 per chunk (on MI355X faster there than the mid family's split K, slower for longer K).
 inline bool skinny_reads_x_from_l2(int64_t M, int KC) { return M <= 16 && KC <= 32; }
 
-template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE = 0>
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE, int F32S>
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;
   constexpr int CGS = NWV / KSPLIT;
@@ -421,53 +426,49 @@ static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   // staged rows + the zero row (+ the per-chunk sums of x of every wave, ONE)
   const size_t lds = (XLDS ? (size_t)(a.M + 1) * (a.Kp + 8) * 2 : 0) + (ONE ? (size_t)NWV * TCH * 4 : 0);
   if (seg == 4)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE>), dim3(blocks), dim3(64 * NWV), lds, s, a);
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S>), dim3(blocks),
+                       dim3(64 * NWV), lds, s, a);
   else if constexpr (TCH == 0)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0>), dim3(blocks), dim3(64 * NWV), lds, s, a);
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0, 0, F32S>), dim3(blocks),
+                       dim3(64 * NWV), lds, s, a);
   return hipGetLastError();
 }
 
-template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH>
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int F32S>
 static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
   // Straight-line variants for the whole-chunk-segment case; ring depths measured best on
   // MI355X for 4-bit M=1 (2 for 8 chunks per wave, 4 for 16).
-  if (seg == 4 && a.KC == 4 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 4>(a, seg, s);
-  if (seg == 4 && a.KC == 8 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 8>(a, seg, s);
-  if (seg == 4 && a.KC == 16 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 16>(a, seg, s);
-  return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 0>(a, seg, s);
+  if (seg == 4 && a.KC == 4 * KSPLIT)
+    return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 4, 0, F32S>(a, seg, s);
+  if (seg == 4 && a.KC == 8 * KSPLIT)
+    return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, (DEPTH < 2 ? DEPTH : 2), 8, 0, F32S>(a, seg, s);
+  if (seg == 4 && a.KC == 16 * KSPLIT) return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 16, 0, F32S>(a, seg, s);
+  return run_tch<BITS, XT, MT, TW, KSPLIT, XLDS, DEPTH, 0, 0, F32S>(a, seg, s);
 }
 
 // x staged in LDS whole, or (M <= 16, see skinny_reads_x_from_l2) read from L2 per chunk, two
 // column tiles per wave so that x traffic stays near the weight traffic.
-template <int BITS, int XT>
+template <int BITS, int XT, int F32S>
 static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
   if (x_fits_lds(a.M, a.Kp)) {
-#ifndef GQ_D2
-#define GQ_D2 4
-#define GQ_D3 4
-#endif
-    if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, (BITS == 2 ? GQ_D2 : (BITS == 3 ? GQ_D3 : 4))>(a, seg, s);
+    if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, 4, F32S>(a, seg, s);
     // M = 1 over 32 chunks: two waves per column tile, each a straight-line 16-chunk range with a
     // 4-deep ring, measured 3 % faster on MI355X than four waves of 8 chunks (4096-input layers)
     // the offset operand for bf16 activations (it replaces the bias MFMAs: 4 % on MI355X for the
     // 8192-input layer); fp16 keeps its exact operands (no gain measured)
     constexpr int ONE = XT == 1 && BITS <= 4;
-#ifndef GQ_D2
-#define GQ_D2 4
-#define GQ_D3 4
-#endif
-    constexpr int D1 = BITS == 2 ? GQ_D2 : (BITS == 3 ? GQ_D3 : 4);
-    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, D1, 16, ONE>(a, seg, s);
-    if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, D1, 16, ONE>(a, seg, s);
-    return run<BITS, XT, 1, 1, 4, 1, D1>(a, seg, s);
+    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16, ONE, F32S>(a, seg, s);
+    if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE, F32S>(a, seg, s);
+    return run<BITS, XT, 1, 1, 4, 1, 4, F32S>(a, seg, s);
   }
-  if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4>(a, seg, s);
+  if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4, F32S>(a, seg, s);
   return hipErrorInvalidValue;   // larger M goes to the mid family
 }
 
 template <int BITS>
 hipError_t skinny_bits(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s) {
-  return x_bf16 ? run_m<BITS, 1>(a, seg, s) : run_m<BITS, 0>(a, seg, s);
+  if (a.scale_kind == 2) return x_bf16 ? run_m<BITS, 1, 1>(a, seg, s) : run_m<BITS, 0, 1>(a, seg, s);
+  return x_bf16 ? run_m<BITS, 1, 0>(a, seg, s) : run_m<BITS, 0, 0>(a, seg, s);
 }
 hipError_t skinny_b2(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
 hipError_t skinny_b3(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
