@@ -47,7 +47,8 @@ __device__ __forceinline__ int mid_segment_group(int si, uint32_t gmagic, int gs
   return group_of_segment(si, gmagic, gshift, G);
 }
 
-template <int BITS, int XT, int MT, int WN, int NW, int SEG, int DEPTH, int TCH>
+// F32S: float32 scales in a parallel array (one more load per chunk); otherwise none is issued.
+template <int BITS, int XT, int MT, int WN, int NW, int SEG, int DEPTH, int TCH, int F32S>
 __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   constexpr int BMR = 16 * MT;                  // rows held in LDS (rows >= M are zero)
   constexpr int NSEG = 4 / SEG;
@@ -92,7 +93,8 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         c.rec[j][s] = load_b32(rm[j], voff_m, (uint32_t)g * 64u);
-        c.s32[j][s] = load_b32(rs[j], voff_m, (uint32_t)g * 64u);
+        if constexpr (F32S) c.s32[j][s] = load_b32(rs[j], voff_m, (uint32_t)g * 64u);
+        else c.s32[j][s] = 0u;
       }
     }
   };
@@ -233,42 +235,43 @@ inline MidPlan mid_plan(const gptq_layer* L, int64_t M) {
   return p;
 }
 
-template <int BITS, int XT, int MT, int SEG, int TCH>
+template <int BITS, int XT, int MT, int SEG, int TCH, int F32S>
 static hipError_t run_mid_cfg(const MidArgs& a, int KS, hipStream_t s) {
   constexpr int DEPTH = 2;
   const int nbk = (a.CT + kMidNW * kMidWN - 1) / (kMidNW * kMidWN);
   const size_t lds = (size_t)TCH * 16 * MT * 256;
-  hipLaunchKernelGGL((mid_kernel<BITS, XT, MT, kMidWN, kMidNW, SEG, DEPTH, TCH>), dim3(nbk, KS), dim3(64 * kMidNW), lds,
-                     s, a);
+  hipLaunchKernelGGL((mid_kernel<BITS, XT, MT, kMidWN, kMidNW, SEG, DEPTH, TCH, F32S>), dim3(nbk, KS),
+                     dim3(64 * kMidNW), lds, s, a);
   return hipGetLastError();
 }
 
-template <int BITS, int XT, int SEG>
+template <int BITS, int XT, int SEG, int F32S>
 static hipError_t run_mid_seg(const MidArgs& a, const MidPlan& p, hipStream_t s) {
   if (p.MT == 1) {
-    if (p.cpw == 16) return run_mid_cfg<BITS, XT, 1, SEG, 16>(a, p.KS, s);
-    if (p.cpw == 8) return run_mid_cfg<BITS, XT, 1, SEG, 8>(a, p.KS, s);
-    return run_mid_cfg<BITS, XT, 1, SEG, 4>(a, p.KS, s);
+    if (p.cpw == 16) return run_mid_cfg<BITS, XT, 1, SEG, 16, F32S>(a, p.KS, s);
+    if (p.cpw == 8) return run_mid_cfg<BITS, XT, 1, SEG, 8, F32S>(a, p.KS, s);
+    return run_mid_cfg<BITS, XT, 1, SEG, 4, F32S>(a, p.KS, s);
   }
   if (p.MT == 2) {
-    if (p.cpw == 8) return run_mid_cfg<BITS, XT, 2, SEG, 8>(a, p.KS, s);
-    return run_mid_cfg<BITS, XT, 2, SEG, 4>(a, p.KS, s);
+    if (p.cpw == 8) return run_mid_cfg<BITS, XT, 2, SEG, 8, F32S>(a, p.KS, s);
+    return run_mid_cfg<BITS, XT, 2, SEG, 4, F32S>(a, p.KS, s);
   }
-  return run_mid_cfg<BITS, XT, 4, SEG, 4>(a, p.KS, s);
+  return run_mid_cfg<BITS, XT, 4, SEG, 4, F32S>(a, p.KS, s);
 }
 
 // 32-input segments (four scales per chunk) always run 4-chunk slices of at most two row blocks
 // (the launcher splits larger M into passes of 32 rows).
-template <int BITS, int XT>
+template <int BITS, int XT, int F32S>
 static hipError_t run_mid_m(const MidArgs& a, const MidPlan& p, int seg, hipStream_t s) {
-  if (seg == 4) return run_mid_seg<BITS, XT, 4>(a, p, s);
-  if (p.MT == 1) return run_mid_cfg<BITS, XT, 1, 1, 4>(a, p.KS, s);
-  return run_mid_cfg<BITS, XT, 2, 1, 4>(a, p.KS, s);
+  if (seg == 4) return run_mid_seg<BITS, XT, 4, F32S>(a, p, s);
+  if (p.MT == 1) return run_mid_cfg<BITS, XT, 1, 1, 4, F32S>(a, p.KS, s);
+  return run_mid_cfg<BITS, XT, 2, 1, 4, F32S>(a, p.KS, s);
 }
 
 template <int BITS>
 hipError_t mid_bits(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s) {
-  return x_bf16 ? run_mid_m<BITS, 1>(a, p, seg, s) : run_mid_m<BITS, 0>(a, p, seg, s);
+  if (a.scale_kind == 2) return x_bf16 ? run_mid_m<BITS, 1, 1>(a, p, seg, s) : run_mid_m<BITS, 0, 1>(a, p, seg, s);
+  return x_bf16 ? run_mid_m<BITS, 1, 0>(a, p, seg, s) : run_mid_m<BITS, 0, 0>(a, p, seg, s);
 }
 hipError_t mid_b2(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
 hipError_t mid_b3(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
