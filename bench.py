@@ -346,7 +346,7 @@ def main():
                    "desc_act": w.desc_act, "handles_rotated": R, "graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic("skinny_" + w.label()),
-                     "kernel": "gq::skinny_kernel<4,0,1,1,2,4,1,4,16,0>", "algorithmic_bytes_per_launch": abytes},
+                     "kernel": "gq::skinny_kernel<4,0,1,1,2,4,1,4,16,0,0>", "algorithmic_bytes_per_launch": abytes},
         "cpu_baseline": cpu,
         "extra": extra,
     }
