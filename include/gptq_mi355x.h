@@ -225,6 +225,19 @@ gptq_status gptq_quantize(const float* W, const float* H, int32_t N, int32_t K, 
                           uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* The checkpoint writer ("39. Quantized checkpoints ...", section "GPTQ": codes along the input
+ * dimension low bits first, zeros along the output dimension, scales [groups, out]): logical codes
+ * uint8 [N, K], scales float32 [N, G] and zeros int32 [N, G] (as gptq_quantize returns them) ->
+ * qweight int32 [K / 32 * bits, N], qzeros int32 [G, N / 32 * bits] and scales_out [G, N] in
+ * scales_dtype (F16 / BF16 rounded to nearest even, or F32), for checkpoint_format GPTQ (v1: the
+ * stored zero is (zero - 1) & mask, so a zero of 0 reads back as 2^bits, the format's own quirk),
+ * GPTQ_V2 (zeros as they are) or GPTQ_P (planar words, v1 zeros; 2..8-bit).  Device pointers,
+ * stream-ordered, no synchronisation.  Errors: GPTQ_E_INVALID_ARG, GPTQ_E_UNSUPPORTED (format,
+ * bits, group_size), GPTQ_E_SHAPE (N or K not a multiple of 32, or out of range), GPTQ_E_HIP. */
+gptq_status gptq_pack(const uint8_t* codes, const float* scales, const int32_t* zeros, int32_t N, int32_t K,
+                      int32_t bits, int32_t group_size, int32_t checkpoint_format, int32_t scales_dtype,
+                      int32_t* qweight, int32_t* qzeros, void* scales_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -117,13 +117,15 @@ def test_quantized_layer_runs_through_repack_and_gemm():
     Hd = wq.hessian(to_dev(x, "bf16"))
     rng = np.random.default_rng(78)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
-    c, s, z, g = [t.cpu().numpy() for t in wq.quantize(torch.from_numpy(W).cuda(), Hd, bits=bits, group_size=gs,
-                                                            act_order=True)]
-    qweight = o.pack_codes(c.T.astype(np.int64), bits)            # [K/8, N]
-    qzeros = o.pack_along_cols(z.T.astype(np.int64), bits)        # v2: zeros as they are
-    scales = np.ascontiguousarray(s.T, dtype=np.float32)          # [G, N]
-    h = wq.repack(torch.from_numpy(qweight).cuda(), torch.from_numpy(qzeros).cuda(), torch.from_numpy(scales).cuda(),
-                  torch.from_numpy(g).cuda(), bits=bits, group_size=gs, desc_act=True, checkpoint_format="gptq_v2")
+    cd, sd, zd, gd = wq.quantize(torch.from_numpy(W).cuda(), Hd, bits=bits, group_size=gs, act_order=True)
+    qw_d, qz_d, sc_d = wq.pack(cd, sd, zd, bits=bits, group_size=gs, checkpoint_format="gptq_v2",
+                               scales_dtype=torch.float32)
+    c, s, z, g = [t.cpu().numpy() for t in (cd, sd, zd, gd)]
+    qweight, qzeros, scales = [t.cpu().numpy() for t in (qw_d, qz_d, sc_d)]
+    assert np.array_equal(qweight, o.pack_codes(c.T.astype(np.int64), bits))      # [K/8, N]
+    assert np.array_equal(qzeros, o.pack_along_cols(z.T.astype(np.int64), bits))  # v2: zeros as they are
+    assert np.array_equal(scales, s.T)                                             # [G, N]
+    h = wq.repack(qw_d, qz_d, sc_d, gd, bits=bits, group_size=gs, desc_act=True, checkpoint_format="gptq_v2")
     xt = gi.make_x(33, K, "bf16", seed=79)
     y_ref = o.gemm_fmt("gptq_v2", xt, "bf16", qweight, qzeros, scales, "f32", g, bits)
     for M, p in ((1, wq.PATH_AUTO), (33, wq.PATH_AUTO), (33, wq.PATH_TILED)):
@@ -132,6 +134,43 @@ def test_quantized_layer_runs_through_repack_and_gemm():
     Xf = o.decode_float_bits(xt, "bf16")
     assert np.linalg.norm(y_ref - Xf @ W.T) < 0.2 * np.linalg.norm(Xf @ W.T)
     h.close()
+
+
+@pytest.mark.parametrize("fmt,bits,sdt", [("gptq", 4, "f16"), ("gptq", 3, "bf16"), ("gptq", 2, "f32"), ("gptq", 8, "f16"),
+                                         ("gptq_v2", 4, "bf16"), ("gptq_v2", 3, "f16"), ("gptq_p", 3, "f16"),
+                                         ("gptq_p", 5, "bf16"), ("gptq_p", 7, "f32"), ("gptq_p", 6, "f16")])
+def test_pack_matches_the_writer(fmt, bits, sdt):
+    """gptq_pack against the checkpoint writer written from the pages (oracle pack functions)."""
+    import torch
+    import weight_only_quantized_amd as wq
+    from gpu_util import device_to_bits, torch_dtype
+    rng = np.random.default_rng(bits + len(fmt))
+    N, K, gs = 96, 256, 64
+    G = K // gs
+    c = rng.integers(0, 2 ** bits, size=(N, K)).astype(np.uint8)
+    z = rng.integers(0 if fmt == "gptq_v2" else 1, 2 ** bits, size=(N, G)).astype(np.int32)
+    s = rng.uniform(0.001, 0.05, size=(N, G)).astype(np.float32)
+    qw, qz, sc = wq.pack(torch.from_numpy(c).cuda(), torch.from_numpy(s).cuda(), torch.from_numpy(z).cuda(), bits=bits,
+                         group_size=gs, checkpoint_format=fmt, scales_dtype=torch_dtype(sdt))
+    torch.cuda.synchronize()
+    if fmt == "gptq_p":
+        want_w = o.planar_pack_rows(c.T.astype(np.int64), bits)
+        want_z = o.planar_pack_cols(((z.astype(np.int64) - 1) & (2 ** bits - 1)).T, bits)
+    else:
+        want_w = o.pack_codes(c.T.astype(np.int64), bits)
+        want_z = o.pack_zeros(z.T, bits) if fmt == "gptq" else o.pack_along_cols(z.T.astype(np.int64), bits)
+    assert np.array_equal(qw.cpu().numpy(), want_w)
+    assert np.array_equal(qz.cpu().numpy(), want_z)
+    if sdt == "f32":
+        assert np.array_equal(sc.cpu().numpy(), s.T)
+    else:
+        assert np.array_equal(device_to_bits(sc), o.round_to_dtype_bits(s.T.astype(np.float64), sdt))
+    # and the reader gets the logical values back
+    d = o.dequant_fmt(fmt, want_w, want_z, o.round_to_dtype_bits(s.T.astype(np.float64), sdt) if sdt != "f32" else s.T,
+                      sdt, (np.arange(K) // gs).astype(np.int32), bits)
+    sv = o.decode_float_bits(o.round_to_dtype_bits(s.T.astype(np.float64), sdt), sdt) if sdt != "f32" else s.T
+    g = np.arange(K) // gs
+    assert np.array_equal(d, (sv[g].T * (c.astype(np.float64) - z[:, g])))
 
 
 def test_quantize_argument_errors():

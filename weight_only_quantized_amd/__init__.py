@@ -27,7 +27,7 @@ PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 # Every symbol include/gptq_mi355x.h declares.
 symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
            "gptq_info", "gptq_decode_runtime", "gptq_status_str", "gptq_last_hip_error", "gptq_hessian",
-           "gptq_quantize_workspace_size", "gptq_quantize"]
+           "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack"]
 
 
 class GPTQError(RuntimeError):
@@ -92,9 +92,10 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_hessian.argtypes = [P, I64, I32, I32, P, P]
     lib.gptq_quantize_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
     lib.gptq_quantize.argtypes = [P, P, I32, I32, ctypes.POINTER(QuantParams), P, P, P, P, P, SZ, P]
+    lib.gptq_pack.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]
     for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
               "gptq_info", "gptq_decode_runtime", "gptq_last_hip_error", "gptq_hessian",
-              "gptq_quantize_workspace_size", "gptq_quantize"):
+              "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack"):
         getattr(lib, f).restype = I32
     _lib = lib
     return lib
@@ -310,3 +311,24 @@ def quantize(W, H, *, bits=4, group_size=128, act_order=False, damp=0.01, stream
     if st:
         raise GPTQError(st, "gptq_quantize", lib)
     return codes, scales, zeros, g_idx
+
+
+def pack(codes, scales, zeros, *, bits, group_size, checkpoint_format="gptq_v2", scales_dtype=None, stream=None):
+    """Write quantizer outputs (codes uint8 [N, K], scales float32 [N, G], zeros int32 [N, G], GPU
+    tensors) as checkpoint tensors on the GPU: (qweight int32 [K*bits/32, N], qzeros int32
+    [G, N*bits/32], scales [G, N] in scales_dtype, default float16)."""
+    import torch
+    lib = load_library()
+    N, K = codes.shape
+    G = scales.shape[1]
+    sdt = torch.float16 if scales_dtype is None else scales_dtype
+    dev = codes.device
+    qweight = torch.empty((K * bits // 32, N), dtype=torch.int32, device=dev)
+    qzeros = torch.empty((G, N * bits // 32), dtype=torch.int32, device=dev)
+    s_out = torch.empty((G, N), dtype=sdt, device=dev)
+    fmt = FORMATS[checkpoint_format] if isinstance(checkpoint_format, str) else int(checkpoint_format)
+    st = lib.gptq_pack(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, bits, group_size, fmt,
+                       _dtype_code(sdt), qweight.data_ptr(), qzeros.data_ptr(), s_out.data_ptr(), _stream_ptr(stream))
+    if st:
+        raise GPTQError(st, "gptq_pack", lib)
+    return qweight, qzeros, s_out

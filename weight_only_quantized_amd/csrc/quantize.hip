@@ -209,6 +209,77 @@ __global__ void unpermute_kernel(const uint8_t* __restrict__ cp, const int32_t* 
   if (n == 0) g_idx[perm[c]] = c / gs;
 }
 
+// ---- checkpoint writer: logical codes / zeros / scales -> checkpoint tensors -----------------------
+// "39. Quantized checkpoints ...", section "GPTQ" (the writer: codes along the input dimension, low
+// bits first; zeros along the output dimension, stored minus one; scales [groups, out]), with the
+// word rules of the repack side: continuous words (a 3-bit code may straddle two words of a
+// 96-bit stream), or GPTQ_P planes (widths 2 | 2+1 | 4 | 4+1 | 4+2 | 4+2+1 | 8, low bits first).
+// Packs the 32 values v[0..31] of one block into `bits` words w[0..bits-1].
+__device__ __forceinline__ void pack_block32(const uint32_t* v, int bits, bool planar, uint32_t* w) {
+  for (int i = 0; i < bits; ++i) w[i] = 0u;
+  if (!planar) {
+    for (int j = 0; j < 32; ++j) {
+      const int bit = bits * j, wi = bit >> 5, sh = bit & 31;
+      w[wi] |= v[j] << sh;
+      if (sh + bits > 32) w[wi + 1] |= v[j] >> (32 - sh);
+    }
+    return;
+  }
+  int pw[3], np = 0;
+  if (bits == 3) { pw[0] = 2; pw[1] = 1; np = 2; }
+  else if (bits <= 4 || bits == 8) { pw[0] = bits; np = 1; }
+  else { pw[0] = 4; pw[1] = bits == 5 ? 1 : 2; pw[2] = 1; np = bits == 7 ? 3 : 2; }
+  int row = 0, low = 0;
+  for (int p = 0; p < np; ++p) {
+    const int per = 32 / pw[p];
+    for (int j = 0; j < 32; ++j)
+      w[row + j / per] |= ((v[j] >> low) & ((1u << pw[p]) - 1u)) << (pw[p] * (j % per));
+    row += pw[p];
+    low += pw[p];
+  }
+}
+
+// qweight: thread per (block of 32 inputs kb, output n): codes[n, 32 kb .. 32 kb + 31].
+__global__ void pack_codes_kernel(const uint8_t* __restrict__ codes, int N, int K, int bits, int planar,
+                                  uint32_t* __restrict__ qweight) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)(K / 32) * N) return;
+  const int n = (int)(t % N), kb = (int)(t / N);
+  uint32_t v[32], w[8];
+  for (int j = 0; j < 32; ++j) v[j] = codes[(int64_t)n * K + 32 * kb + j];
+  pack_block32(v, bits, planar != 0, w);
+  for (int i = 0; i < bits; ++i) qweight[(int64_t)(kb * bits + i) * N + n] = w[i];
+}
+
+// qzeros and scales: thread per (group g, block of 32 outputs nb); v1 stores zero - 1 (masked).
+__global__ void pack_meta_kernel(const float* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int G,
+                                 int bits, int planar, int minus_one, int sdt, uint32_t* __restrict__ qzeros,
+                                 void* __restrict__ scales_out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)G * (N / 32)) return;
+  const int g = (int)(t % G), nb = (int)(t / G);
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t v[32], w[8];
+  for (int j = 0; j < 32; ++j) {
+    const int n = 32 * nb + j;
+    const uint32_t z = (uint32_t)zeros[(int64_t)n * G + g];
+    v[j] = (minus_one ? z - 1u : z) & mask;
+    const float sv = scales[(int64_t)n * G + g];
+    const int64_t o = (int64_t)g * N + n;
+    if (sdt == GPTQ_F32) {
+      reinterpret_cast<float*>(scales_out)[o] = sv;
+    } else if (sdt == GPTQ_F16) {
+      reinterpret_cast<uint16_t*>(scales_out)[o] = __builtin_bit_cast(uint16_t, (_Float16)sv);
+    } else {   // bf16, round to nearest even (scales are finite)
+      const uint32_t u = __builtin_bit_cast(uint32_t, sv);
+      reinterpret_cast<uint16_t*>(scales_out)[o] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    }
+  }
+  pack_block32(v, bits, planar != 0, w);
+  const int zld = N / 32 * bits;
+  for (int i = 0; i < bits; ++i) qzeros[(int64_t)g * zld + nb * bits + i] = w[i];
+}
+
 // ---- rocSOLVER / rocBLAS, loaded on first use -----------------------------------------------------
 struct LinAlg {
   bool ok = false;
@@ -366,6 +437,31 @@ gptq_status gptq_quantize(const float* W, const float* H, int32_t N, int32_t K, 
   if (hipStreamSynchronize(s) != hipSuccess && st == GPTQ_OK) st = GPTQ_E_HIP;
   la.destroy(hb);
   return st;
+}
+
+gptq_status gptq_pack(const uint8_t* codes, const float* scales, const int32_t* zeros, int32_t N, int32_t K,
+                      int32_t bits, int32_t group_size, int32_t checkpoint_format, int32_t scales_dtype,
+                      int32_t* qweight, int32_t* qzeros, void* scales_out, void* stream) {
+  if (!codes || !scales || !zeros || !qweight || !qzeros || !scales_out) return GPTQ_E_INVALID_ARG;
+  const int f = checkpoint_format;
+  if (f != GPTQ_FORMAT_GPTQ && f != GPTQ_FORMAT_GPTQ_V2 && f != GPTQ_FORMAT_GPTQ_P) return GPTQ_E_UNSUPPORTED;
+  const bool planar = f == GPTQ_FORMAT_GPTQ_P;
+  if (planar ? (bits < 2 || bits > 8) : (bits != 2 && bits != 3 && bits != 4 && bits != 8)) return GPTQ_E_UNSUPPORTED;
+  if (group_size != -1 && (group_size <= 0 || group_size % 32 != 0)) return GPTQ_E_UNSUPPORTED;
+  if (scales_dtype != GPTQ_F16 && scales_dtype != GPTQ_BF16 && scales_dtype != GPTQ_F32) return GPTQ_E_INVALID_ARG;
+  if (N <= 0 || K <= 0 || N % 32 || K % 32 || N > (1 << 20) || K > (1 << 20) || (int64_t)N * K > (int64_t(1) << 36))
+    return GPTQ_E_SHAPE;
+  const int gs = group_size == -1 ? K : group_size;
+  const int G = (K + gs - 1) / gs;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nw = (int64_t)(K / 32) * N, nm = (int64_t)G * (N / 32);
+  hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, codes, N, K, bits,
+                     planar ? 1 : 0, reinterpret_cast<uint32_t*>(qweight));
+  hipLaunchKernelGGL(pack_meta_kernel, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s, scales, zeros, N, G, bits,
+                     planar ? 1 : 0, f == GPTQ_FORMAT_GPTQ_V2 ? 0 : 1, scales_dtype,
+                     reinterpret_cast<uint32_t*>(qzeros), scales_out);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? GPTQ_OK : hip_fail(e);
 }
 
 }  // extern "C"
