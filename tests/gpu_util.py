@@ -57,10 +57,25 @@ def run_gemm(h, x_bits, x_tag, path=0, bias=None, bias_tag=None):
     return device_to_bits(y)
 
 
+def out_ulp(y_ref, x_tag):
+    """One unit in the last place of the output dtype (fp16: 10 fraction bits, bf16: 7) at |y_ref|
+    (the subnormal step below the normal range)."""
+    frac, emin = (10, -14) if x_tag == "f16" else (7, -126)
+    e = np.floor(np.log2(np.maximum(np.abs(np.asarray(y_ref, dtype=np.float64)), 2.0 ** emin)))
+    return np.ldexp(1.0, (e - frac).astype(np.int64))
+
+
 def check(y_bits, x_tag, y_ref, label=""):
+    """rel-L2 and max-abs bars of the layer.  The max-abs bar (2e-2 * rms) is below the output dtype's
+    own rounding for outputs far above the rms (bf16: beyond ~10 rms); there each output must be
+    within one unit in the last place of y_ref instead, which a correctly rounded result is."""
     m = o.compare(y_bits, x_tag, y_ref)
     tol = TOL[x_tag]
     assert m["nonfinite"] == 0, (label, m)
     assert m["rel_l2"] <= tol["rel_l2"], (label, m)
-    assert m["max_abs_over_rms"] <= tol["max_abs_over_rms"], (label, m)
+    if m["max_abs_over_rms"] > tol["max_abs_over_rms"]:
+        y = o.decode_float_bits(y_bits, x_tag)
+        ref = np.asarray(y_ref, dtype=np.float64)
+        bound = np.maximum(tol["max_abs_over_rms"] * m["rms_ref"], out_ulp(ref, x_tag))
+        assert np.all(np.abs(y - ref) <= bound), (label, m)
     return m

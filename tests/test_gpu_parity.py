@@ -365,3 +365,22 @@ def test_repack_rejects_bad_layers_on_device():
     with pytest.raises(wq.GPTQError) as e:
         wq.repack(qw[:-1].contiguous(), qz, sc, torch.from_numpy(L.g_idx).cuda(), bits=4, group_size=64)
     assert e.value.name in ("E_SHAPE", "E_GIDX")
+
+
+# ---- extreme shapes: very long K, very wide N ------------------------------------------------------
+
+@pytest.mark.parametrize("K,N,bits,gs,desc,xdt", [(65536, 64, 4, 128, False, "bf16"), (32768, 96, 3, 128, True, "f16"),
+                                                  (128, 131072, 4, -1, False, "f16"), (256, 65536, 8, 128, True, "bf16")])
+def test_extreme_shapes(K, N, bits, gs, desc, xdt):
+    """512 chunks of K (split K up to its 255-slice cap on the tiled path, long skinny ranges) and
+    4096-8192 column tiles; every family."""
+    import weight_only_quantized_amd as wq
+    say("extreme", K, N, bits, gs, desc, xdt)
+    L = gi.make_layer(K, N, bits, gs, desc_act=desc, scales_dtype="f16", seed=K % 9973 + N)
+    h = repack_layer(L)
+    x = gi.make_x(130, K, xdt, seed=K + N + 1)
+    y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, "f16", L.g_idx, bits)
+    for M in (1, 5, 33, 130):
+        for p in [wq.PATH_AUTO, wq.PATH_TILED] + ([wq.PATH_SKINNY] if M <= 64 else []):
+            check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=(K, N, M, p))
+    h.close()
