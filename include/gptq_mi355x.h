@@ -216,7 +216,7 @@ gptq_status gptq_quantize_workspace_size(int32_t N, int32_t K, size_t* bytes);
  * Outputs (device, caller-owned): codes uint8 [N, K] in the ORIGINAL input order, scales float32
  * [N, G] and zeros int32 [N, G] (the logical zero, 0 .. 2^bits - 1; a zero of 0 needs
  * GPTQ_FORMAT_GPTQ_V2 to be stored) with G = ceil(K / group_size), g_idx int32 [K] (group of each
- * input).  W and H are read only.  Synchronises the stream.  Uses rocSOLVER (POTRF, POTRI) and
+ * input).  W and H are read only.  Synchronises the stream.  Uses rocSOLVER (POTRF, TRTRI) and
  * rocBLAS (SGEMM), loaded on first use.
  * Errors: GPTQ_E_INVALID_ARG (NULL, reserved != 0, damp outside [0, 1]), GPTQ_E_UNSUPPORTED (bits,
  * group_size, or the solver libraries not found), GPTQ_E_SHAPE (K not a multiple of 32 or > 16384,

@@ -14,7 +14,8 @@
 // Design on gfx950: the output rows are independent given U, so the column loop of a block runs
 // with one wave per row (lane l holds block columns l and l + 64, U's block in LDS, the current
 // column broadcast across the wave); the Hessian is a float64-accumulated product of the inputs;
-// the factorizations (POTRF, POTRI) and the per-block update GEMM are plain library calls
+// the factorization (POTRF), the triangular inverse (TRTRI) and the per-block update GEMM are plain
+// library calls
 // (rocSOLVER / rocBLAS), loaded on first use so that the GEMM path does not depend on them.
 #pragma clang fp contract(off)
 
@@ -198,6 +199,25 @@ __global__ void __launch_bounds__(64 * NW) gptq_block_kernel(const float* __rest
   }
 }
 
+// U from the inverse of the Cholesky factor of the reversed Hessian: with P = J Hp J = L L^T (J the
+// order reversal) Hp = (J L J)(J L J)^T, so the upper factor of Hp^-1 is U = J L^-1 J -- the factor
+// the page obtains from cholesky(cholesky_inverse(cholesky(Hp)), upper), with one factorization and
+// one triangular inverse.  rocSOLVER leaves L^-1 column-major, i.e. mem[i][j] = L^-1[j][i] for
+// j >= i row-major, and U[i][j] = L^-1[K-1-i][K-1-j] = mem[K-1-j][K-1-i]: an involution of the upper
+// triangle, applied in place by swapping each pair once.
+__global__ void reverse_upper_kernel(float* __restrict__ A, int K) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)K * K) return;
+  const int i = (int)(e / K), j = (int)(e % K);
+  if (j < i) return;
+  const int pi = K - 1 - j, pj = K - 1 - i;
+  const int64_t pe = (int64_t)pi * K + pj;
+  if (e >= pe) return;                       // the pair's other element does the swap
+  const float a = A[e], b = A[pe];
+  A[e] = b;
+  A[pe] = a;
+}
+
 // codes back in the original column order; g_idx of original column perm[c] is c / gs.
 __global__ void unpermute_kernel(const uint8_t* __restrict__ cp, const int32_t* __restrict__ perm, int N, int K,
                                  int gs, uint8_t* __restrict__ codes, int32_t* __restrict__ g_idx) {
@@ -290,7 +310,8 @@ struct LinAlg {
                           const float*, const float*, rocblas_int, const float*, rocblas_int, const float*, float*,
                           rocblas_int) = nullptr;
   rocblas_status (*potrf)(rocblas_handle, rocblas_fill, rocblas_int, float*, rocblas_int, rocblas_int*) = nullptr;
-  rocblas_status (*potri)(rocblas_handle, rocblas_fill, rocblas_int, float*, rocblas_int, rocblas_int*) = nullptr;
+  rocblas_status (*trtri)(rocblas_handle, rocblas_fill, rocblas_diagonal, rocblas_int, float*, rocblas_int,
+                          rocblas_int*) = nullptr;
 };
 
 static const LinAlg& linalg() {
@@ -307,8 +328,8 @@ static const LinAlg& linalg() {
     L.set_stream = (decltype(L.set_stream))dlsym(blas, "rocblas_set_stream");
     L.sgemm = (decltype(L.sgemm))dlsym(blas, "rocblas_sgemm");
     L.potrf = (decltype(L.potrf))dlsym(sol, "rocsolver_spotrf");
-    L.potri = (decltype(L.potri))dlsym(sol, "rocsolver_spotri");
-    L.ok = L.create && L.destroy && L.set_stream && L.sgemm && L.potrf && L.potri;
+    L.trtri = (decltype(L.trtri))dlsym(sol, "rocsolver_strtri");
+    L.ok = L.create && L.destroy && L.set_stream && L.sgemm && L.potrf && L.trtri;
   });
   return L;
 }
@@ -387,36 +408,41 @@ gptq_status gptq_quantize(const float* W, const float* H, int32_t N, int32_t K, 
   std::vector<int32_t> perm(K);
   std::iota(perm.begin(), perm.end(), 0);
   if (p->act_order) std::stable_sort(perm.begin(), perm.end(), [&](int a, int b) { return d[a] > d[b]; });
+  std::vector<int32_t> rperm(perm.rbegin(), perm.rend());     // the reversed visiting order
   double sum = 0.0;
   for (int i = 0; i < K; ++i) sum += d[i];
   const float damp_add = p->damp * (float)(sum / K);
-  e = hipMemcpyAsync(perm_d, perm.data(), sizeof(int32_t) * K, hipMemcpyHostToDevice, s);
+  e = hipMemcpyAsync(perm_d, rperm.data(), sizeof(int32_t) * K, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(dead_d, dead.data(), K, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);            // rperm is reused below
   if (e != hipSuccess) return hip_fail(e);
   const int64_t kk = (int64_t)K * K, nk = (int64_t)N * K;
   hipLaunchKernelGGL(permute_h_kernel, dim3((unsigned)((kk + 255) / 256)), dim3(256), 0, s, H, perm_d, dead_d,
                      damp_add, K, Hp);
+  e = hipMemcpyAsync(perm_d, perm.data(), sizeof(int32_t) * K, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e);
   hipLaunchKernelGGL(permute_w_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, W, perm_d, dead_d, N, K,
                      Wp);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e);
 
-  // U = upper Cholesky factor of (L L^T)^-1, L = Cholesky factor of Hp.  rocSOLVER is column-major:
-  // the lower factor it writes is, read row-major, the upper factor U the loop needs.
+  // U = upper Cholesky factor of Hp^-1 = J L^-1 J with L the Cholesky factor of the reversed Hp
+  // (reverse_upper_kernel): one POTRF, one TRTRI, one in-place reversal.
   rocblas_handle hb = nullptr;
   if (la.create(&hb) != rocblas_status_success) return GPTQ_E_UNSUPPORTED;
   gptq_status st = GPTQ_OK;
-  rocblas_int info[3] = {0, 0, 0};
+  rocblas_int info[2] = {0, 0};
   if (la.set_stream(hb, s) != rocblas_status_success ||
       la.potrf(hb, rocblas_fill_lower, K, Hp, K, info_d) != rocblas_status_success ||
       hipMemcpyAsync(&info[0], info_d, sizeof(rocblas_int), hipMemcpyDeviceToHost, s) != hipSuccess ||
-      la.potri(hb, rocblas_fill_lower, K, Hp, K, info_d) != rocblas_status_success ||
+      la.trtri(hb, rocblas_fill_lower, rocblas_diagonal_non_unit, K, Hp, K, info_d) != rocblas_status_success ||
       hipMemcpyAsync(&info[1], info_d, sizeof(rocblas_int), hipMemcpyDeviceToHost, s) != hipSuccess ||
-      la.potrf(hb, rocblas_fill_lower, K, Hp, K, info_d) != rocblas_status_success ||
-      hipMemcpyAsync(&info[2], info_d, sizeof(rocblas_int), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess) {
     st = GPTQ_E_HIP;
-  } else if (info[0] || info[1] || info[2]) {
+  } else if (info[0] || info[1]) {
     st = GPTQ_E_NUMERIC;                       // not positive definite even after damping
+  } else {
+    hipLaunchKernelGGL(reverse_upper_kernel, dim3((unsigned)((kk + 255) / 256)), dim3(256), 0, s, Hp, K);
+    if (hipGetLastError() != hipSuccess) st = GPTQ_E_HIP;
   }
   const float minus_one = -1.f, one = 1.f;
   for (int i1 = 0; st == GPTQ_OK && i1 < K; i1 += kQBlock) {
