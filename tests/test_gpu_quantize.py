@@ -3,8 +3,9 @@ which follows the page's steps in its float32 precision.
 
 The Hessian is float64-accumulated on both sides and rounded once to float32: equal to within one
 float32 unit.  A code is an integer decided by float32 arithmetic on both sides, but the two
-sides factorize H with different algorithms (rocSOLVER's blocked POTRF/POTRI and LAPACK's), so the
-inverse-Hessian rows they use differ in the last few bits; a decision within that distance of a
+sides reach the inverse-Hessian factor by different routes (rocSOLVER: one factorization of the
+reversed H and a triangular inverse; LAPACK through the page's three steps), so the rows they use
+differ in the last few bits; a decision within that distance of a
 rounding boundary may flip, and the flip then propagates along its row through the error
 feedback (rows are independent).  The bar: g_idx exact; at least 95 % of rows identical in every
 code, their grids equal (zeros exactly, scales to 1e-5); the layer's output error within 2 % of
