@@ -280,7 +280,7 @@ def main():
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings); outside the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the kernels run one GPU's share of a layer; no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -36,7 +36,7 @@ Sources (page title, then section):
          the interleaved order 0 2 4 6 1 3 5 7 (output 1's field in bits 16-19), zeros
          are stored as they are (offset = -zero * scale), scales [groups, out].
 
-Readings where the pages are silent or ambiguous (each is listed in the design doc):
+Readings where the pages are silent or ambiguous:
   * v1 zeros: the writer stores (z - 1) & mask, the reader adds 1 with no mask,
     so a stored all-ones field reads back as 2**bits ([FMT] writer vs reader;
     [SPEC] GPTQ-006).
@@ -233,7 +233,7 @@ def round_to_dtype_bits(y, dtype: str) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
-# Validation: [SPEC] "Reject the file when" GPTQ-001..006, plus the readings listed in the design doc
+# Validation: [SPEC] "Reject the file when" GPTQ-001..006, plus the readings in this module's docstring
 # ----------------------------------------------------------------------------------------------
 
 def validate_layer(K, N, bits, group_size, qweight_shape, qzeros_shape, scales_shape, g_idx=None,

@@ -20,7 +20,7 @@ Source: "39. Quantized checkpoints: GPTQ, AWQ, FP8, FP4 and trellis codes", sect
   * a group's range is taken from the CURRENT (already corrected) weights when the loop enters it,
     over the next group_size columns.
 
-Readings where the page is silent (each is listed in the design doc):
+Readings where the page is silent:
   * the per-group parameters ("find_params" is named, not printed): an asymmetric min-max grid
     over each row's group values, widened to contain 0 so that 0 is exact (lo = min(0, min w),
     hi = max(0, max w)); scale = (hi - lo) / (2^bits - 1), zero = round(-lo / scale); a group that
