@@ -414,9 +414,11 @@ inline bool x_fits_lds(int64_t M, int Kp) {
          (M + 1) * 16 * ((Kp / 128 + 3) / 4) <= 512;
 }
 
-// The other case the skinny kernel keeps: M <= 16 over at most 32 chunks of K, with x read from
-// L2 per chunk (on MI355X faster there than the mid family's split K, slower for longer K).
-inline bool skinny_reads_x_from_l2(int64_t M, int KC) { return M <= 16 && KC <= 32; }
+// The other case the skinny kernel keeps: x read from L2 per chunk, for M <= 16 over at most 32
+// chunks of K, and for M <= 4 at any K (on MI355X faster there than the mid family's split K:
+// 8192 x 28672, M = 2 / 3 / 4: 28.3 / 29.5 / 30.7 us against 30.1 / 30.5 / 31.2; slower at longer K
+// for larger M).
+inline bool skinny_reads_x_from_l2(int64_t M, int KC) { return M <= 16 && (KC <= 32 || M <= 4); }
 
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE, int F32S>
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
