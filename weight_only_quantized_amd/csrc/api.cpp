@@ -236,12 +236,12 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
   return GPTQ_OK;
 }
 
-// PATH_AUTO: the skinny family (skinny kernel, or the mid kernel's split K) up to 16 rows, and up
-// to 32 rows of a layer longer than 32 chunks of K; the tiled family (split K up to ~450
-// workgroups) above.  Measured on MI355X with 4-bit g128 layers: 4096 x 14336, M = 24: skinny
+// PATH_AUTO: the skinny family (skinny kernel, or the mid kernel's split K) up to 16 rows, up to
+// 32 rows of a layer longer than 32 chunks of K, and up to 32 rows where the skinny kernel reads x
+// from L2 (skinny_reads_x_from_l2); the tiled family (split K up to ~450 workgroups) above.  Measured on MI355X with 4-bit g128 layers: 4096 x 14336, M = 24: skinny
 // family 20.1 us, tiled 17.3 us; 8192 x 28672, M = 32: 46.1 vs 48.3 us, M = 48: 74.7 vs 50.7 us.
 static int32_t auto_path(const gptq_layer* L, int64_t M) {
-  return (M <= 16 || (M <= 32 && L->KC > 32)) ? GPTQ_PATH_SKINNY : GPTQ_PATH_TILED;
+  return (M <= 16 || (M <= 32 && (L->KC > 32 || skinny_x_from_l2(L, M)))) ? GPTQ_PATH_SKINNY : GPTQ_PATH_TILED;
 }
 
 gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int32_t path,

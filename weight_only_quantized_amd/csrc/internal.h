@@ -67,6 +67,8 @@ bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
 // The SKINNY path (M <= 64) runs the skinny kernel when x fits one workgroup's LDS whole and the
 // mid kernel (split K, mid.hip) otherwise; the mid kernel's partial sums need workspace.
 bool uses_mid(const gptq_layer* L, int64_t M);
+// The skinny kernel reads x from L2 for this M (mid.hip; the rule is skinny_impl.h's).
+bool skinny_x_from_l2(const gptq_layer* L, int64_t M);
 size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M);
 // Split-K partial sums of the tiled family ([KS][M][N] fp32 after the x copy and row exponents).
 size_t ws_tiled_part_bytes(const gptq_layer* L, int64_t M);

@@ -415,12 +415,19 @@ inline bool x_fits_lds(int64_t M, int Kp) {
 }
 
 // The other case the skinny kernel keeps: x read from L2 per chunk, for M <= 16 over at most 32
-// chunks of K, and for M <= 4 at any K (on MI355X faster there than the mid family's split K:
-// 8192 x 28672, M = 2 / 3 / 4: 28.3 / 29.5 / 30.7 us against 30.1 / 30.5 / 31.2; slower at longer K
-// for larger M).
-inline bool skinny_reads_x_from_l2(int64_t M, int KC) { return M <= 16 && (KC <= 32 || M <= 4); }
+// chunks of K, for M <= 4 at any K, and for 17 <= M <= 32 (two 16-row blocks) while M * KC <= 640.
+// Measured on MI355X: faster there than the mid family's split K (8192 x 28672, M = 2 / 3 / 4:
+// 28.3 / 29.5 / 30.7 us against 30.1 / 30.5 / 31.2) and than the tiled family (2048 x 14336,
+// M = 17 / 32: 9.5 / 12.6 us against 15.0 / 17.3; 4096 x 14336, M = 17 / 20: 15.6 / 16.9 against
+// 17.4 / 17.1); slower beyond.
+// (The two-block form is built for whole-chunk groups and 3/4/8-bit codes: with 2-bit codes or
+// 32-input groups it does not fit its registers.)
+inline bool skinny_reads_x_from_l2(int64_t M, int KC, int bits, int seg_steps) {
+  return (M <= 16 && (KC <= 32 || M <= 4)) || (M <= 32 && M * KC <= 640 && bits != 2 && seg_steps == 4);
+}
 
-template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE, int F32S>
+template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE, int F32S,
+          int SEG1 = 1>   // SEG1 = 0: whole-chunk groups only (no 32-input-segment kernel is built)
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;
   constexpr int CGS = NWV / KSPLIT;
@@ -430,7 +437,7 @@ static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   if (seg == 4)
     hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S>), dim3(blocks),
                        dim3(64 * NWV), lds, s, a);
-  else if constexpr (TCH == 0)
+  else if constexpr (TCH == 0 && SEG1)
     hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0, 0, F32S>), dim3(blocks),
                        dim3(64 * NWV), lds, s, a);
   return hipGetLastError();
@@ -464,6 +471,14 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     return run<BITS, XT, 1, 1, 4, 1, 4, F32S>(a, seg, s);
   }
   if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4, F32S>(a, seg, s);
+  if constexpr (BITS != 2) {
+    // two row blocks; M * KC <= 640 leaves at most 37 chunks, so the 16-chunk form is not built
+    if (a.M <= 32 && seg == 4) {
+      if (a.KC == 16) return run_tch<BITS, XT, 2, 2, 4, 0, 2, 4, 0, F32S>(a, seg, s);
+      if (a.KC == 32) return run_tch<BITS, XT, 2, 2, 4, 0, 2, 8, 0, F32S>(a, seg, s);
+      return run_tch<BITS, XT, 2, 2, 4, 0, 4, 0, 0, F32S, 0>(a, seg, s);
+    }
+  }
   return hipErrorInvalidValue;   // larger M goes to the mid family
 }
 
