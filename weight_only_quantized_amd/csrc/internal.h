@@ -69,6 +69,10 @@ bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
 bool uses_mid(const gptq_layer* L, int64_t M);
 // The skinny kernel reads x from L2 for this M (mid.hip; the rule is skinny_impl.h's).
 bool skinny_x_from_l2(const gptq_layer* L, int64_t M);
+// K slices the mid kernel would cut a call into (mid.hip), and chunks per K slice of the tiled
+// plan (tiled.hip): the inputs of PATH_AUTO between 17 and 32 rows.
+int mid_slices(const gptq_layer* L, int64_t M);
+int tiled_slice_chunks(const gptq_layer* L, int64_t M);
 size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M);
 // Split-K partial sums of the tiled family ([KS][M][N] fp32 after the x copy and row exponents).
 size_t ws_tiled_part_bytes(const gptq_layer* L, int64_t M);

@@ -9,10 +9,14 @@ namespace gq {
 
 static inline size_t align256m(size_t b) { return (b + 255) / 256 * 256; }
 
-bool skinny_x_from_l2(const gptq_layer* L, int64_t M) { return skinny_reads_x_from_l2(M, L->KC, L->bits, L->seg_steps); }
+bool skinny_x_from_l2(const gptq_layer* L, int64_t M) {
+  return skinny_reads_x_from_l2(M, L->KC, L->CT, L->bits, L->seg_steps);
+}
+
+int mid_slices(const gptq_layer* L, int64_t M) { return mid_plan(L, M).KS; }
 
 bool uses_mid(const gptq_layer* L, int64_t M) {
-  return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_reads_x_from_l2(M, L->KC, L->bits, L->seg_steps);
+  return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_x_from_l2(L, M);
 }
 
 size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M) {

@@ -545,6 +545,8 @@ static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
   return p;
 }
 
+int tiled_slice_chunks(const gptq_layer* L, int64_t M) { return tiled_plan(L, M).kcs; }
+
 size_t ws_tiled_part_bytes(const gptq_layer* L, int64_t M) {
   const TiledPlan p = tiled_plan(L, M);
   return p.KS > 1 ? align256((size_t)p.KS * M * L->N * 4) : 0;
