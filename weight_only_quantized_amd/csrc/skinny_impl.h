@@ -420,7 +420,8 @@ inline bool x_fits_lds(int64_t M, int Kp) {
 // Measured on MI355X: faster there than the mid family's split K (8192 x 28672, M = 2 / 3 / 4:
 // 28.3 / 29.5 / 30.7 us against 30.1 / 30.5 / 31.2) and than the tiled family (2048 x 14336,
 // M = 17 / 32: 9.5 / 12.6 us against 15.0 / 17.3; 4096 x 14336, M = 17 / 20: 15.6 / 16.9 against
-// 17.4 / 17.1); slower beyond (14336 x 4096, M = 1: 29.3 us against the tiled family's 17.0).
+// 17.4 / 17.1); slower beyond (14336 x 4096, 256 column tiles, M = 1: 29.3 us against the mid
+// kernel's 13.4).
 // (The two-block form is built for whole-chunk groups and 3/4/8-bit codes: with 2-bit codes or
 // 32-input groups it does not fit its registers.)
 inline bool skinny_reads_x_from_l2(int64_t M, int KC, int CT, int bits, int seg_steps) {
