@@ -25,6 +25,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (loads, and loads
+// into LDS, complete in issue order); the other counters are left alone (s_waitcnt fields of
+// gfx9: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // `words` consecutive 32-bit words at voff + soff of resource r.
 template <int WORDS, int AUX>
 __device__ __forceinline__ void load_words(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* out) {

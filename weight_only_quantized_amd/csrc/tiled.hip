@@ -275,8 +275,13 @@ __device__ __forceinline__ void store_part(const TiledArgs& a, const f32x4 (&acc
 // rows (an A operand) then hit sixteen different 16-byte bank groups.  The tile is filled with
 // buffer_load ... lds (lane i of a load writes slot i of its 1 KB destination), so each lane
 // simply fetches the global piece that belongs in its slot.
-template <int BITS, int OB, int WM, int WN, int SEG, int NW>
-__global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
+// DEPTH = 1: one chunk in flight (two x buffers, the next chunk's loads issued during this chunk's
+// compute, then a full wait); DEPTH = 2: two chunks in flight (three x buffers and three register
+// stages, each step waiting only for its own chunk's loads).  The three buffers are distinct LDS
+// arrays: the compiler then knows that a read of one does not wait for the LDS DMA into another.
+template <int BITS, int OB, int WM, int WN, int SEG, int NW, int DEPTH>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(DEPTH == 2 ? 2 : 1)))
+tiled_kernel(const TiledArgs a) {
   constexpr int BM = 16 * WM;
   constexpr int NSEG = 4 / SEG;
   constexpr int PARTS = BITS == 8 ? 2 : 1;
@@ -286,7 +291,10 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   constexpr int A_INST = BM / (4 * NW);        // 1 KB LDS loads per wave per chunk
   static_assert(A_INST * NW * 64 == BM * 16, "x tile must split evenly over the waves");
   static_assert(A_INST <= WM && WM > 2, "one x piece per row block; units after the third");
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[2][A_BYTES];
+  static_assert(DEPTH == 1 || DEPTH == 2, "one or two chunks in flight");
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[DEPTH == 1 ? 2 : 1][A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs_b[DEPTH == 2 ? A_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs_c[DEPTH == 2 ? A_BYTES : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,17 +350,17 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     uint32_t s32[WN][NSEG];
   };
 
-  // Chunk kc: packed units and metadata -> registers, then the x chunk -> xs[buf] by LDS DMA.
-  // One 1 KB piece (j) of chunk kc's x tile -> xs[buf] by LDS DMA.
-  auto issue_x = [&](int kc, int buf, int j) {
+  // Chunk kc: packed units and metadata -> registers, then the x chunk -> LDS buffer xb by DMA.
+  // One 1 KB piece (j) of chunk kc's x tile -> xb by LDS DMA.
+  auto issue_x = [&](int kc, uint8_t* xb, int j) {
     // (the offset goes through a local: passed straight from the array, the host pass of this
     // compiler drops the kernel's launch stub)
     const uint32_t vo = voff_a[j];
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rx, (__attribute__((address_space(3))) void*)(&xs[buf][(wave * A_INST + j) * 1024]), 16, vo,
+        rx, (__attribute__((address_space(3))) void*)(xb + (wave * A_INST + j) * 1024), 16, vo,
         (uint32_t)kc * 256u, 0, 0);
   };
-  auto issue = [&](int kc, int buf, Stage& st, bool with_x) {
+  auto issue = [&](int kc, uint8_t* xb, Stage& st, bool with_x) {
 #pragma unroll
     for (int j = 0; j < WN; ++j)
 #pragma unroll
@@ -369,11 +377,11 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     }
     if (with_x) {
 #pragma unroll
-      for (int j = 0; j < A_INST; ++j) issue_x(kc, buf, j);
+      for (int j = 0; j < A_INST; ++j) issue_x(kc, xb, j);
     }
   };
 
-  auto compute = [&](int buf, const Stage& st, auto&& hook) {
+  auto compute = [&](const uint8_t* xb, const Stage& st, auto&& hook) {
     u32x4 b[WN][4];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
@@ -385,7 +393,6 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) sc[j][s] = scale_of(st.rec[j][s], st.s32[j][s], a.scale_kind);
-    const uint8_t* xb = &xs[buf][0];
     if constexpr (SEG == 1) {
       // four scales per chunk: the plain order keeps the wave within four waves per SIMD
 #pragma unroll
@@ -448,8 +455,54 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
       for (int s = 0; s < NSEG; ++s) acc[WM - 1][j] += sc[j][s] * prev[j][s];
   };
 
+  if constexpr (DEPTH == 2) {
+    // Chunk c (c = 0, 1, ... from kc_lo) sits in buffer and register stage c % 3.  The step of
+    // chunk c waits until at most one chunk's loads (c + 1) are pending, meets the workgroup at the
+    // barrier (every wave is then done with chunk c - 1, whose buffer and stage are free) and
+    // requests chunk c + 2 into them while it computes.  Requests past the slice repeat its last
+    // chunk (L2 hits), so every step of the loop issues the same loads and the wait count is fixed;
+    // the last one or two steps after the loop issue nothing and wait for everything.
+    constexpr int NL = WN * PARTS + 2 * NSEG * WN + A_INST;   // loads per chunk per wave
+    static_assert(NL < 64, "vmcnt holds at most 63");
+    Stage st0, st1, st2;
+    const int n = kc_hi - kc_lo;
+    issue(kc_lo, &xs[0][0], st0, true);
+    issue(kc_lo + (n > 1 ? 1 : 0), xs_b, st1, true);
+    auto step = [&](int c, const Stage& st, const uint8_t* xb, Stage& stn, uint8_t* xbn) {
+      __builtin_amdgcn_sched_barrier(0);     // no instruction crosses a step boundary
+      // this wave's loads of chunk c are in, and its reads of chunk c - 1 (lgkmcnt); no fence
+      // (a workgroup fence waits for every load in flight)
+      wait_vmcnt<NL>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt left alone
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int kn = kc_lo + min(c + 2, n - 1);
+      compute(xb, st, [&](int i) {
+        if (i < A_INST) issue_x(kn, xbn, i);
+        if (i == 2) issue(kn, xbn, stn, false);
+      });
+    };
+    auto last_step = [&](const Stage& st, const uint8_t* xb) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      compute(xb, st, [](int) {});
+    };
+    int c = 0;
+    for (; c + 2 < n; c += 3) {
+      step(c, st0, &xs[0][0], st2, xs_c);
+      step(c + 1, st1, xs_b, st0, &xs[0][0]);
+      step(c + 2, st2, xs_c, st1, xs_b);
+    }
+    if (c < n) last_step(st0, &xs[0][0]);
+    if (c + 1 < n) last_step(st1, xs_b);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (a.part) store_part<OB, WM, WN>(a, acc, ks, m0, ct0, col, q);
+    else store_tiles<OB, WM, WN>(a, acc, m0, ct0, col, q);
+    return;
+  }
+
   Stage cur, nxt;
-  issue(kc_lo, 0, cur, true);
+  issue(kc_lo, &xs[0][0], cur, true);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = kc_lo; it < kc_hi; ++it) {
@@ -459,9 +512,9 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
     // after the third piece, so the workgroup's requests do not all queue up at once behind the
     // barrier (measured on MI355X: 5 % faster than issuing everything before the chunk).
     const int kn = more ? it + 1 : it;
-    compute(buf, cur, [&](int i) {
-      if (i < A_INST) issue_x(kn, buf ^ 1, i);
-      if (i == 2) issue(kn, buf ^ 1, nxt, false);
+    compute(&xs[buf][0], cur, [&](int i) {
+      if (i < A_INST) issue_x(kn, &xs[buf ^ 1][0], i);
+      if (i == 2) issue(kn, &xs[buf ^ 1][0], nxt, false);
     });
     // the next chunk's x tile, units and metadata were issued before this chunk's compute
     __builtin_amdgcn_s_waitcnt(0);
@@ -473,13 +526,13 @@ __global__ void __launch_bounds__(64 * NW) tiled_kernel(const TiledArgs a) {
   else store_tiles<OB, WM, WN>(a, acc, m0, ct0, col, q);
 }
 
-template <int BITS, int OB, int WM, int WN, int SEG, int NW>
+template <int BITS, int OB, int WM, int WN, int SEG, int NW, int DEPTH = 1>
 static hipError_t run_tiled(const TiledArgs& a0, hipStream_t s) {
   TiledArgs a = a0;
   a.MB = (a.M + 16 * WM - 1) / (16 * WM);
   a.NB = (a.CT + NW * WN - 1) / (NW * WN);
-  hipLaunchKernelGGL((tiled_kernel<BITS, OB, WM, WN, SEG, NW>), dim3((unsigned)(a.MB * a.NB * a.KS)), dim3(64 * NW),
-                     0, s, a);
+  hipLaunchKernelGGL((tiled_kernel<BITS, OB, WM, WN, SEG, NW, DEPTH>), dim3((unsigned)(a.MB * a.NB * a.KS)),
+                     dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -491,6 +544,7 @@ constexpr TileShape kTiles[] = {
   {8, 2, 4},    // 2: 128 x 128, wave 128 x 32
   {4, 2, 4},    // 3:  64 x 128, wave  64 x 32
   {8, 2, 8},    // 4: 128 x 256, wave 128 x 32
+  {4, 2, 4},    // 5:  64 x 128 as 3, two chunks in flight
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -520,14 +574,14 @@ static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
   if (L->seg_steps != 4) {
     p.tile = 1;
   } else if (M <= 64) {
-    p.tile = 3;
+    p.tile = 5;
   } else if (tiles_of(L, M, 0) >= 192) {
     p.tile = 0;
   } else {
     p.tile = 4;
   }
   const int64_t t = tiles_of(L, M, p.tile);
-  if (p.tile == 3) p.KS = ceil_div(448, t);
+  if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
   else if (t < 150) p.KS = ceil_div(224, t);
 #ifdef GQ_TUNE
   if (const char* e = getenv("GQ_TILED")) {
@@ -560,6 +614,7 @@ static hipError_t run_tiled_m(const TiledArgs& a, int tile, int seg, hipStream_t
     case 2: return run_tiled<BITS, OB, 8, 2, 4, 4>(a, s);
     case 3: return run_tiled<BITS, OB, 4, 2, 4, 4>(a, s);
     case 4: return run_tiled<BITS, OB, 8, 2, 4, 8>(a, s);
+    case 5: return run_tiled<BITS, OB, 4, 2, 4, 4, 2>(a, s);
     default: return run_tiled<BITS, OB, 8, 1, 4, 8>(a, s);
   }
 }
