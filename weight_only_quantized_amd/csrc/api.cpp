@@ -236,17 +236,18 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
   return GPTQ_OK;
 }
 
-// PATH_AUTO: the skinny family (skinny kernel, or the mid kernel's split K) up to 16 rows; from 17 to
-// 32 rows the skinny kernel where it reads x from L2 (skinny_reads_x_from_l2), else the tiled family
-// when its K slices are long (8 chunks or more) while the mid kernel would cut K into more than 4
-// slices, else the mid kernel; the tiled family (split K up to ~450 workgroups) above 32 rows.
-// Measured on MI355X with 4-bit g128 layers, M = 24 / 32, mid vs tiled: 4096 x 14336 20.1 / 21.6
-// vs 17.3 / 17.9 us (tiled slices of 8, mid slices 8); 4096 x 6144 11.9 / 13.0 vs 12.7 / 13.7
-// (tiled slices of 4); 4096 x 4096 9.9 / 10.9 vs 10.9 / 11.7 (tiled slices of 4); 14336 x 4096
-// 21.0 / 21.8 vs 17.6 / 18.5 (tiled slices of 8, mid slices 28); 8192 x 28672 44.4 / 46.1 vs
-// 47.4 / 48.3 (mid slices 4).  At 48 rows and above the tiled family won on every shape measured.
+// PATH_AUTO: the skinny family (skinny kernel, or the mid kernel's split K) up to 8 rows; from 9
+// to 32 rows the skinny kernel where it reads x from L2 (skinny_reads_x_from_l2), else the tiled
+// family when its K slices are long (8 chunks or more) while the mid kernel would cut K into more
+// than 4 slices, else the mid kernel; the tiled family (split K up to ~450 workgroups) above 32
+// rows.  Measured on MI355X with 4-bit g128 layers, fp16 x, mid vs tiled (two chunks in flight):
+// 14336 x 4096, M = 8 / 16 / 24 / 32: 15.1 / 17.3 / 21.7 / 22.6 vs 17.2 / 16.0 / 16.8 / 17.6 us
+// (tiled slices of 8 chunks, mid slices 28); 4096 x 6144, M = 24 / 32: 11.9 / 12.8 vs 12.3 / 13.7
+// (tiled slices of 4); 8192 x 28672, M = 16 / 32: 33.7 / 45.9 vs 39.3 / 42.5 (tiled slices of 32,
+// mid slices 4 at 16 rows, 8 at 32).  At 48 rows and above the tiled family won on every shape
+// measured.
 static int32_t auto_path(const gptq_layer* L, int64_t M) {
-  if (M <= 16) return GPTQ_PATH_SKINNY;
+  if (M <= 8) return GPTQ_PATH_SKINNY;
   if (M <= 32) {
     if (skinny_x_from_l2(L, M)) return GPTQ_PATH_SKINNY;
     return (tiled_slice_chunks(L, M) >= 8 && mid_slices(L, M) > 4) ? GPTQ_PATH_TILED : GPTQ_PATH_SKINNY;
