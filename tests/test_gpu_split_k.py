@@ -55,6 +55,24 @@ def test_tiled_split_k(K, N, bits, gs, desc, sdt, xdt):
     h.close()
 
 
+@pytest.mark.parametrize("K", [128, 256, 384, 640, 896, 1152, 1664])
+def test_two_deep_tile_every_chunk_count(K):
+    """The 64 x 128 tile keeps two chunks in flight in steps of three and finishes a slice with
+    one or two steps that issue nothing: slices of 1, 2, 3, 5, 7 chunks (one slice), 5 + 4 and
+    5 + 5 + 3 chunks (K split), every one against the oracle."""
+    import weight_only_quantized_amd as wq
+    say("two-deep", K)
+    N = 128
+    L = gi.make_layer(K, N, 4, 128, scales_dtype="f16", seed=K)
+    h = repack_layer(L)
+    for xdt in ("f16", "bf16"):
+        x = gi.make_x(64, K, xdt, seed=K + 1)
+        y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, "f16", L.g_idx, 4)
+        for M in (17, 40, 64):
+            check(run_gemm(h, x[:M], xdt, path=wq.PATH_TILED), xdt, y_ref[:M], label=(K, xdt, M))
+    h.close()
+
+
 @pytest.mark.parametrize("sdt,xdt", [("f16", "f16"), ("bf16", "bf16"), ("f32", "bf16")])
 def test_split_k_bias(sdt, xdt):
     import weight_only_quantized_amd as wq
