@@ -329,7 +329,7 @@ def main():
                 rec["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                                    "traffic": stored_traffic("tiled_" + e.label()),
-                                   "kernel": "gq::tiled_kernel<4,1,16,2,4,8>", "algorithmic_flops_per_launch": fl}
+                                   "kernel": "gq::tiled_kernel<4,1,16,2,4,8,1>", "algorithmic_flops_per_launch": fl}
             extra.append(rec)
             print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
         # the step before the path: GPTQ on the GPU for the same 4096 x 14336 layer
