@@ -563,6 +563,12 @@ static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // 1024): a call runs best with about one eight-wave workgroup (or two four-wave ones) per compute
 // unit, from the largest tile that gets there, and splits K only as far as needed to get there:
 //   * M <= 64: the 64 x 128 tile, K split up to ~448 workgroups;
+//   * M <= 512 on layers of at most 4096 inputs whose 64-row blocks together read at most 128 MB
+//     of packed weights (the repeated passes then come from the Infinity Cache): the 64 x 128
+//     tile too, K split in two below ~192 tiles (4096 x 6144, M = 128 / 512: 24.3 / 52.7 us with
+//     the tiles below against 19.1 / 36.7; 4096 x 14336, M = 256: 43.3 against 39.5; longer K or
+//     more weight passes measured slower: 14336 x 4096 M = 128 31.2 against 45.3, 8192 x 28672
+//     M = 256 120.4 against 148.7);
 //   * larger M: the 256 x 256 tile once it alone gives ~192 workgroups, else the 128 x 256 tile,
 //     K split up to ~224 workgroups when it gives fewer than ~150;
 //   * 32-input segments: the 128 x 128 tile (wave 128 x 16), split the same way.
@@ -571,17 +577,22 @@ static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
   TiledPlan p;
   p.KS = 1;
+  const int64_t wbytes = (int64_t)L->Kp * L->N * L->bits / 8;     // packed codes of the layer
+  const int64_t mb64 = (M + 63) / 64;                            // 64-row blocks
   if (L->seg_steps != 4) {
     p.tile = 1;
   } else if (M <= 64) {
     p.tile = 5;
+  } else if (M <= 512 && L->KC <= 32 && mb64 * wbytes <= (int64_t(128) << 20)) {
+    p.tile = 5;       // short K, and every 64-row block's pass over the weights fits the MALL
   } else if (tiles_of(L, M, 0) >= 192) {
     p.tile = 0;
   } else {
     p.tile = 4;
   }
   const int64_t t = tiles_of(L, M, p.tile);
-  if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
+  if (p.tile == 5 && M > 64) p.KS = t >= 192 ? 1 : 2;
+  else if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
   else if (t < 150) p.KS = ceil_div(224, t);
 #ifdef GQ_TUNE
   if (const char* e = getenv("GQ_TILED")) {
