@@ -101,6 +101,27 @@ def test_gemm_small_shapes_both_paths(K, N, bits, gs, desc, sdt, xdt):
 DISPATCH_MS = [1, 2, 3, 4, 5, 16, 17, 33, 64, 130, 257]
 
 
+@pytest.mark.parametrize("K,bits,gs,desc,xdt", [(14336, 4, 128, False, "f16"), (14336, 4, 128, False, "bf16"),
+                                                (12288, 3, 128, False, "bf16"), (10240, 8, -1, False, "f16"),
+                                                (14304, 2, -1, False, "bf16"), (14336, 4, 128, True, "f16"),
+                                                (12288, 8, 256, False, "bf16"), (10240, 4, 64, False, "f16")])
+def test_long_rows_at_one_row(K, bits, gs, desc, xdt):
+    """M = 1 on 10240 / 12288 / 14336-input layers: x staged in LDS with five to seven waves of 16
+    chunks per column tile (whole-chunk groups, no act-order; 14304 inputs end in a partial chunk);
+    act-order and 64-input groups take the mid kernel.  M = 2 and 3 beside it take the mid kernel."""
+    import weight_only_quantized_amd as wq
+    N = 160
+    say("long-rows", K, bits, gs, desc, xdt)
+    L = gi.make_layer(K, N, bits, gs, desc_act=desc, scales_dtype="f16", seed=K + bits)
+    h = repack_layer(L)
+    x = gi.make_x(3, K, xdt, seed=K + 7)
+    y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, "f16", L.g_idx, bits)
+    for M in (1, 2, 3):
+        for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
+            check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=(K, bits, gs, desc, xdt, M, p))
+    h.close()
+
+
 @pytest.mark.parametrize("K,bits,desc,xdt", [(2048, 4, False, "f16"), (4096, 4, False, "f16"),
                                              (4096, 4, False, "bf16"), (4096, 2, False, "f16"),
                                              (4096, 3, False, "bf16"), (4096, 8, False, "f16"),

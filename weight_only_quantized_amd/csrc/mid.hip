@@ -16,7 +16,8 @@ bool skinny_x_from_l2(const gptq_layer* L, int64_t M) {
 int mid_slices(const gptq_layer* L, int64_t M) { return mid_plan(L, M).KS; }
 
 bool uses_mid(const gptq_layer* L, int64_t M) {
-  return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_x_from_l2(L, M);
+  return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_x_from_l2(L, M) &&
+         !skinny_m1_long(M, L->KC, L->seg_steps, L->has_perm != 0);
 }
 
 size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M) {

@@ -414,6 +414,15 @@ inline bool x_fits_lds(int64_t M, int Kp) {
          (M + 1) * 16 * ((Kp / 128 + 3) / 4) <= 512;
 }
 
+// M = 1 on a long layer without act-order (10240, 12288 or 14336 inputs, whole-chunk groups): x is
+// staged in LDS as for short layers, and the workgroup takes one column tile with KC / 16 waves of
+// 16 chunks each (five to seven waves), the same per-wave work as the 4096-input M = 1 call.  The
+// staged row, its zero row and the waves' partial sums stay under 64 KB of LDS.  Measured on
+// MI355X: 14336 x 4096 at M = 1, 13.4 us with the mid kernel's split K, 8.2 us in this form.
+inline bool skinny_m1_long(int64_t M, int KC, int seg_steps, bool has_perm) {
+  return M == 1 && !has_perm && seg_steps == 4 && (KC == 80 || KC == 96 || KC == 112);
+}
+
 // The other case the skinny kernel keeps: x read from L2 per chunk, for M <= 16 over at most 32
 // chunks of K, for M <= 4 at any K when the layer has at least 1024 column tiles (enough workgroups
 // for its long per-wave ranges), and for 17 <= M <= 32 (two 16-row blocks) while M * KC <= 640.
@@ -472,6 +481,12 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16, ONE, F32S>(a, seg, s);
     if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE, F32S>(a, seg, s);
     return run<BITS, XT, 1, 1, 4, 1, 4, F32S>(a, seg, s);
+  }
+  if (skinny_m1_long(a.M, a.KC, seg, a.iperm != nullptr)) {
+    constexpr int ONE = XT == 1 && BITS <= 4;
+    if (a.KC == 80) return run_tch<BITS, XT, 1, 1, 5, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
+    if (a.KC == 96) return run_tch<BITS, XT, 1, 1, 6, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
+    return run_tch<BITS, XT, 1, 1, 7, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
   }
   if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4, F32S>(a, seg, s);
   if constexpr (BITS != 2) {
