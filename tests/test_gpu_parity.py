@@ -108,17 +108,45 @@ DISPATCH_MS = [1, 2, 3, 4, 5, 16, 17, 33, 64, 130, 257]
 def test_long_rows_at_one_row(K, bits, gs, desc, xdt):
     """M = 1 on 10240 / 12288 / 14336-input layers: x staged in LDS with five to seven waves of 16
     chunks per column tile (whole-chunk groups, no act-order; 14304 inputs end in a partial chunk);
-    act-order and 64-input groups take the mid kernel.  M = 2 and 3 beside it take the mid kernel."""
+    M = 2 .. 12: the same waves with x read from L2; act-order and 64-input groups take the mid
+    kernel, M = 16 here the tiled family."""
     import weight_only_quantized_amd as wq
     N = 160
     say("long-rows", K, bits, gs, desc, xdt)
     L = gi.make_layer(K, N, bits, gs, desc_act=desc, scales_dtype="f16", seed=K + bits)
     h = repack_layer(L)
-    x = gi.make_x(3, K, xdt, seed=K + 7)
+    x = gi.make_x(16, K, xdt, seed=K + 7)
     y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, "f16", L.g_idx, bits)
-    for M in (1, 2, 3):
+    for M in (1, 2, 3, 5, 12, 16):
         for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
             check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=(K, bits, gs, desc, xdt, M, p))
+    h.close()
+
+
+@pytest.mark.parametrize("bits,xdt", [(4, "bf16"), (3, "f16"), (8, "bf16")])
+def test_long_rows_wide_layer(bits, xdt):
+    """10240 inputs x 8192 outputs (512 column tiles: two tiles per wave with x from L2) at
+    M = 1 .. 16, checked on 256 columns at each end of the layer against the oracle on those
+    columns (the packed tensors sliced on whole words)."""
+    import weight_only_quantized_amd as wq
+    K, N = 10240, 8192
+    say("long-rows-wide", bits, xdt)
+    L = gi.make_layer(K, N, bits, 128, scales_dtype="f16", seed=K + bits)
+    h = repack_layer(L)
+    x = gi.make_x(16, K, xdt, seed=K + 9)
+    zc = N * bits // 32                              # qzeros words per group row
+    refs = []
+    for c0 in (0, N - 256):
+        wq_cols = L.qweight[:, c0:c0 + 256]
+        qz_cols = L.qzeros[:, c0 * bits // 32:(c0 + 256) * bits // 32]
+        sc_cols = L.scales[:, c0:c0 + 256]
+        refs.append((c0, o.gemm(x, xdt, wq_cols, qz_cols, sc_cols, "f16", L.g_idx, bits)))
+    assert zc * 32 == N * bits
+    for M in (1, 2, 4, 9, 16):
+        for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
+            y = run_gemm(h, x[:M], xdt, path=p)
+            for c0, yr in refs:
+                check(y[:, c0:c0 + 256], xdt, yr[:M], label=(bits, xdt, M, p, c0))
     h.close()
 
 

@@ -10,7 +10,8 @@ namespace gq {
 static inline size_t align256m(size_t b) { return (b + 255) / 256 * 256; }
 
 bool skinny_x_from_l2(const gptq_layer* L, int64_t M) {
-  return skinny_reads_x_from_l2(M, L->KC, L->CT, L->bits, L->seg_steps);
+  return skinny_reads_x_from_l2(M, L->KC, L->CT, L->bits, L->seg_steps) ||
+         skinny_mx_long(M, L->KC, L->CT, L->seg_steps, L->has_perm != 0);
 }
 
 int mid_slices(const gptq_layer* L, int64_t M) { return mid_plan(L, M).KS; }

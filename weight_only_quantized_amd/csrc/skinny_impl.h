@@ -422,6 +422,16 @@ inline bool x_fits_lds(int64_t M, int Kp) {
 inline bool skinny_m1_long(int64_t M, int KC, int seg_steps, bool has_perm) {
   return M == 1 && !has_perm && seg_steps == 4 && (KC == 80 || KC == 96 || KC == 112);
 }
+// 2 <= M <= 16 on the same layers: the same waves of 16 chunks with x read from L2 per chunk, one
+// column tile per wave below 512 column tiles and two from 512 (enough workgroups either way).
+// Measured on MI355X against the mid kernel / the tiled family (us): 14336 x 4096, M = 2 / 4 / 8 /
+// 12: 9.7 / 10.3 / 12.0 / 14.5 against 14.4 / 14.4 / 14.8 / 15.3; 12288 x 8192, M = 2 / 8 / 16:
+// 13.4 / 14.6 / 18.2 against 16.0 / 19.3 / 20.5.  (At 13 to 16 rows on fewer than 512 column tiles
+// the tiled family measured faster.)
+inline bool skinny_mx_long(int64_t M, int KC, int CT, int seg_steps, bool has_perm) {
+  return M >= 2 && M <= (CT >= 512 ? 16 : 12) && !has_perm && seg_steps == 4 &&
+         (KC == 80 || KC == 96 || KC == 112);
+}
 
 // The other case the skinny kernel keeps: x read from L2 per chunk, for M <= 16 over at most 32
 // chunks of K, for M <= 4 at any K when the layer has at least 1024 column tiles (enough workgroups
@@ -487,6 +497,16 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     if (a.KC == 80) return run_tch<BITS, XT, 1, 1, 5, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
     if (a.KC == 96) return run_tch<BITS, XT, 1, 1, 6, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
     return run_tch<BITS, XT, 1, 1, 7, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
+  }
+  if (skinny_mx_long(a.M, a.KC, a.CT, seg, a.iperm != nullptr)) {
+    if (a.CT >= 512) {
+      if (a.KC == 80) return run_tch<BITS, XT, 1, 2, 5, 0, 4, 16, 0, F32S, 0>(a, seg, s);
+      if (a.KC == 96) return run_tch<BITS, XT, 1, 2, 6, 0, 4, 16, 0, F32S, 0>(a, seg, s);
+      return run_tch<BITS, XT, 1, 2, 7, 0, 4, 16, 0, F32S, 0>(a, seg, s);
+    }
+    if (a.KC == 80) return run_tch<BITS, XT, 1, 1, 5, 0, 4, 16, 0, F32S, 0>(a, seg, s);
+    if (a.KC == 96) return run_tch<BITS, XT, 1, 1, 6, 0, 4, 16, 0, F32S, 0>(a, seg, s);
+    return run_tch<BITS, XT, 1, 1, 7, 0, 4, 16, 0, F32S, 0>(a, seg, s);
   }
   if (a.M <= 16) return run<BITS, XT, 1, 2, 4, 0, 4, F32S>(a, seg, s);
   if constexpr (BITS != 2) {
