@@ -72,6 +72,7 @@ bool skinny_x_from_l2(const gptq_layer* L, int64_t M);
 // K slices the mid kernel would cut a call into (mid.hip), and chunks per K slice of the tiled
 // plan (tiled.hip): the inputs of PATH_AUTO between 17 and 32 rows.
 int mid_slices(const gptq_layer* L, int64_t M);
+int mid_slice_chunks(const gptq_layer* L, int64_t M);
 int tiled_slice_chunks(const gptq_layer* L, int64_t M);
 size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M);
 // Split-K partial sums of the tiled family ([KS][M][N] fp32 after the x copy and row exponents).

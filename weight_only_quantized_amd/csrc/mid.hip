@@ -15,6 +15,7 @@ bool skinny_x_from_l2(const gptq_layer* L, int64_t M) {
 }
 
 int mid_slices(const gptq_layer* L, int64_t M) { return mid_plan(L, M).KS; }
+int mid_slice_chunks(const gptq_layer* L, int64_t M) { return mid_plan(L, M).cpw; }
 
 bool uses_mid(const gptq_layer* L, int64_t M) {
   return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_x_from_l2(L, M) &&
