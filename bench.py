@@ -215,6 +215,9 @@ def extra_workloads():
         out.append(Workload("llama3_8b_up_proj", 4096, 14336, M, 4, 128, False, "f16", "f16", gi.seed_for(1)))
     for M in (1, 8, 16, 32, 64, 128, 256):
         out.append(Workload("llama3_70b_gate_proj", 8192, 28672, M, 4, 128, False, "f16", "bf16", gi.seed_for(2)))
+    # the down projection of the same 8B MLP: 14336 inputs at decode sizes
+    for M in (1, 4):
+        out.append(Workload("llama3_8b_down_proj", 14336, 4096, M, 4, 128, False, "f16", "f16", gi.seed_for(7)))
     for bits in (2, 3, 4, 8):
         for gs in (128, -1):
             for M in (1, 32):
