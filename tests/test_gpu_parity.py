@@ -155,7 +155,9 @@ def test_long_rows_wide_layer(bits, xdt):
                                              (4096, 3, False, "bf16"), (4096, 8, False, "f16"),
                                              (8192, 4, False, "f16"), (8192, 4, False, "bf16"),
                                              (4096, 8, False, "bf16"), (8192, 2, False, "bf16"),
-                                             (4096, 4, True, "f16"), (8192, 3, True, "bf16")])
+                                             (4096, 4, True, "f16"), (8192, 3, True, "bf16"),
+                                             (5120, 4, False, "bf16"), (6144, 3, False, "f16"),
+                                             (7168, 8, False, "bf16"), (5120, 2, False, "f16")])
 def test_gemm_dispatch_variants(K, bits, desc, xdt):
     import weight_only_quantized_amd as wq
     N = 96

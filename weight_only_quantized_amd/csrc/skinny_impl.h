@@ -490,6 +490,11 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     constexpr int ONE = XT == 1 && BITS <= 4;
     if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16, ONE, F32S>(a, seg, s);
     if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE, F32S>(a, seg, s);
+    // 5120 / 6144 / 7168 inputs: five to seven waves of 8 straight-line chunks (the four-wave
+    // split would leave a loop of 10 to 14 chunks per wave)
+    if (a.M == 1 && seg == 4 && a.KC == 40) return run_tch<BITS, XT, 1, 1, 5, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
+    if (a.M == 1 && seg == 4 && a.KC == 48) return run_tch<BITS, XT, 1, 1, 6, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
+    if (a.M == 1 && seg == 4 && a.KC == 56) return run_tch<BITS, XT, 1, 1, 7, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
     return run<BITS, XT, 1, 1, 4, 1, 4, F32S>(a, seg, s);
   }
   if (skinny_m1_long(a.M, a.KC, seg, a.iperm != nullptr)) {
