@@ -123,13 +123,14 @@ def test_long_rows_at_one_row(K, bits, gs, desc, xdt):
     h.close()
 
 
-@pytest.mark.parametrize("bits,xdt", [(4, "bf16"), (3, "f16"), (8, "bf16")])
-def test_long_rows_wide_layer(bits, xdt):
-    """10240 inputs x 8192 outputs (512 column tiles: two tiles per wave with x from L2) at
-    M = 1 .. 16, checked on 256 columns at each end of the layer against the oracle on those
+@pytest.mark.parametrize("K,bits,xdt", [(10240, 4, "bf16"), (10240, 3, "f16"), (10240, 8, "bf16"),
+                                         (5120, 4, "f16"), (7168, 2, "bf16")])
+def test_long_rows_wide_layer(K, bits, xdt):
+    """10240 / 5120 / 7168 inputs x 8192 outputs (512 column tiles: two tiles per wave with x from
+    L2) at M = 1 .. 16, checked on 256 columns at each end of the layer against the oracle on those
     columns (the packed tensors sliced on whole words)."""
     import weight_only_quantized_amd as wq
-    K, N = 10240, 8192
+    N = 8192
     say("long-rows-wide", bits, xdt)
     L = gi.make_layer(K, N, bits, 128, scales_dtype="f16", seed=K + bits)
     h = repack_layer(L)
@@ -157,7 +158,8 @@ def test_long_rows_wide_layer(bits, xdt):
                                              (4096, 8, False, "bf16"), (8192, 2, False, "bf16"),
                                              (4096, 4, True, "f16"), (8192, 3, True, "bf16"),
                                              (5120, 4, False, "bf16"), (6144, 3, False, "f16"),
-                                             (7168, 8, False, "bf16"), (5120, 2, False, "f16")])
+                                             (7168, 8, False, "bf16"), (5120, 2, False, "f16"),
+                                             (3072, 4, False, "bf16")])
 def test_gemm_dispatch_variants(K, bits, desc, xdt):
     import weight_only_quantized_amd as wq
     N = 96

@@ -239,18 +239,21 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
 // PATH_AUTO: the skinny family (skinny kernel, or the mid kernel's split K) up to 8 rows; from 9
 // to 32 rows the skinny kernel where it reads x from L2 (skinny_reads_x_from_l2), else the tiled
 // family when its K slices are long (8 chunks or more) while the mid kernel would cut K into more
-// than 4 slices shorter than 16 chunks, else the mid kernel; the tiled family (split K up to ~450
-// workgroups) above 32 rows.  Measured on MI355X with 4-bit g128 layers, fp16 x, mid vs tiled (two chunks in flight):
+// than 4 slices shorter than 16 chunks (of 4 chunks up to 16 rows), else the mid kernel; the tiled
+// family (split K up to ~450 workgroups) above 32 rows.  Measured on MI355X with 4-bit g128 layers, fp16 x, mid vs tiled (two chunks in flight):
 // 14336 x 4096, M = 8 / 16 / 24 / 32: 15.1 / 17.3 / 21.7 / 22.6 vs 17.2 / 16.0 / 16.8 / 17.6 us
 // (tiled slices of 8 chunks, mid slices 28); 4096 x 6144, M = 24 / 32: 11.9 / 12.8 vs 12.3 / 13.7
 // (tiled slices of 4); 8192 x 28672, M = 16 / 32: 33.7 / 45.9 vs 39.3 / 42.5 (tiled slices of 32,
 // mid slices 4 at 16 rows, 8 at 32); 28672 x 8192, M = 12 / 16: 32.2 / 33.2 vs 38.0 / 38.4 (mid
-// slices of 16 chunks).  At 48 rows and above the tiled family won on every shape measured.
+// slices of 16 chunks); 5120 x 13824, M = 12 / 16: 15.1 / 15.9 vs 20.4 / 20.9 (mid slices of 8).
+// At 48 rows and above the tiled family won on every shape measured.
 static int32_t auto_path(const gptq_layer* L, int64_t M) {
   if (M <= 8) return GPTQ_PATH_SKINNY;
   if (M <= 32) {
     if (skinny_x_from_l2(L, M)) return GPTQ_PATH_SKINNY;
-    return (tiled_slice_chunks(L, M) >= 8 && mid_slices(L, M) > 4 && mid_slice_chunks(L, M) < 16)
+    // up to 16 rows only 4-chunk mid slices lose; from 17 rows any shorter than 16 chunks
+    const int mid_cpw = mid_slice_chunks(L, M);
+    return (tiled_slice_chunks(L, M) >= 8 && mid_slices(L, M) > 4 && (M > 16 ? mid_cpw < 16 : mid_cpw <= 4))
                ? GPTQ_PATH_TILED : GPTQ_PATH_SKINNY;
   }
   return GPTQ_PATH_TILED;

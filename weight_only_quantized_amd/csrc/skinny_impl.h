@@ -428,9 +428,13 @@ inline bool skinny_m1_long(int64_t M, int KC, int seg_steps, bool has_perm) {
 // 12: 9.7 / 10.3 / 12.0 / 14.5 against 14.4 / 14.4 / 14.8 / 15.3; 12288 x 8192, M = 2 / 8 / 16:
 // 13.4 / 14.6 / 18.2 against 16.0 / 19.3 / 20.5.  (At 13 to 16 rows on fewer than 512 column tiles
 // the tiled family measured faster.)
+// 5120 / 6144 / 7168 inputs (40 / 48 / 56 chunks): five to seven waves of 8 chunks, up to M = 8
+// (5120 x 5120 M = 2 / 4 / 8: 8.8 / 9.6 / 9.8 -> 7.5 / 8.0 / 9.4 us; 7168 x 20480 M = 8: 24.5 ->
+// 23.1 us; slower than the mid kernel from 12 rows).
 inline bool skinny_mx_long(int64_t M, int KC, int CT, int seg_steps, bool has_perm) {
-  return M >= 2 && M <= (CT >= 512 ? 16 : 12) && !has_perm && seg_steps == 4 &&
-         (KC == 80 || KC == 96 || KC == 112);
+  if (M < 2 || has_perm || seg_steps != 4) return false;
+  if (KC == 40 || KC == 48 || KC == 56) return M <= 8;
+  return M <= (CT >= 512 ? 16 : 12) && (KC == 80 || KC == 96 || KC == 112);
 }
 
 // The other case the skinny kernel keeps: x read from L2 per chunk, for M <= 16 over at most 32
@@ -492,6 +496,7 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE, F32S>(a, seg, s);
     // 5120 / 6144 / 7168 inputs: five to seven waves of 8 straight-line chunks (the four-wave
     // split would leave a loop of 10 to 14 chunks per wave)
+    if (a.M == 1 && seg == 4 && a.KC == 24) return run_tch<BITS, XT, 1, 1, 6, 1, 2, 4, ONE, F32S, 0>(a, seg, s);
     if (a.M == 1 && seg == 4 && a.KC == 40) return run_tch<BITS, XT, 1, 1, 5, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
     if (a.M == 1 && seg == 4 && a.KC == 48) return run_tch<BITS, XT, 1, 1, 6, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
     if (a.M == 1 && seg == 4 && a.KC == 56) return run_tch<BITS, XT, 1, 1, 7, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
@@ -504,6 +509,16 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     return run_tch<BITS, XT, 1, 1, 7, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
   }
   if (skinny_mx_long(a.M, a.KC, a.CT, seg, a.iperm != nullptr)) {
+    if (a.KC < 64) {     // 40 / 48 / 56 chunks: five to seven waves of 8
+      if (a.CT >= 512) {
+        if (a.KC == 40) return run_tch<BITS, XT, 1, 2, 5, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+        if (a.KC == 48) return run_tch<BITS, XT, 1, 2, 6, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+        return run_tch<BITS, XT, 1, 2, 7, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+      }
+      if (a.KC == 40) return run_tch<BITS, XT, 1, 1, 5, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+      if (a.KC == 48) return run_tch<BITS, XT, 1, 1, 6, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+      return run_tch<BITS, XT, 1, 1, 7, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+    }
     if (a.CT >= 512) {
       if (a.KC == 80) return run_tch<BITS, XT, 1, 2, 5, 0, 4, 16, 0, F32S, 0>(a, seg, s);
       if (a.KC == 96) return run_tch<BITS, XT, 1, 2, 6, 0, 4, 16, 0, F32S, 0>(a, seg, s);
