@@ -82,9 +82,12 @@ typedef enum {
   GPTQ_FORMAT_GPTQ_P = 4
 } gptq_format;
 
-/* Kernel family for gptq_gemm.  AUTO picks SKINNY for M <= 16 (M <= 32 when K spans more than
- * 4096 inputs) and TILED otherwise.  Forcing a family is for tests; SKINNY runs M <= 64 only
- * (GPTQ_E_INVALID_ARG above), TILED any M. */
+/* Kernel family for gptq_gemm.  AUTO picks SKINNY (the streaming kernels) for M <= 8, TILED (the
+ * MFMA tiles) above 32 rows, and in between whichever measured faster for the layer's shape: the
+ * streaming kernel where it reads x from L2, the tiled family where its K slices are long while
+ * the streaming split would cut K into many short slices.  Forcing a family is for tests; SKINNY
+ * runs M <= 64 only (GPTQ_E_INVALID_ARG above), TILED any M.  Every family meets the same
+ * tolerance, so the choice changes time, not results beyond rounding. */
 typedef enum { GPTQ_PATH_AUTO = 0, GPTQ_PATH_SKINNY = 1, GPTQ_PATH_TILED = 2 } gptq_path;
 
 /* Description of one checkpoint layer.  The *_shape fields are the shapes of the tensors the
