@@ -447,8 +447,11 @@ gptq_status gptq_quantize(const float* W, const float* H, int32_t N, int32_t K, 
   const float minus_one = -1.f, one = 1.f;
   for (int i1 = 0; st == GPTQ_OK && i1 < K; i1 += kQBlock) {
     const int bw = std::min(kQBlock, K - i1);
-    hipLaunchKernelGGL(gptq_block_kernel<4>, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, Wp, Hp, cp, Err, scales,
-                       zeros, N, K, i1, bw, gs, G, p->bits);
+    // sixteen rows per workgroup share one 64 KB copy of U's block, so a compute unit keeps eight
+    // waves per SIMD in flight (four rows per workgroup left it two, and each step's dependent
+    // chain of broadcast, divisions and update exposed its latency)
+    hipLaunchKernelGGL(gptq_block_kernel<16>, dim3((unsigned)((N + 15) / 16)), dim3(1024), 0, s, Wp, Hp, cp, Err,
+                       scales, zeros, N, K, i1, bw, gs, G, p->bits);
     if (hipGetLastError() != hipSuccess) { st = GPTQ_E_HIP; break; }
     const int i2 = i1 + bw, R = K - i2;
     if (R > 0 && la.sgemm(hb, rocblas_operation_none, rocblas_operation_none, R, N, bw, &minus_one,
