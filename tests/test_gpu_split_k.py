@@ -34,7 +34,7 @@ def say(*a):
 # per slice at least); M up to 64 takes the 64 x 128 tile, larger M the 128 x 256 tile, and
 # group sizes that are not a multiple of 128 the 128 x 128 tile.  K = 2080 has 17 chunks: slices
 # of 5, 5, 5 and 2.
-SPLIT_MS = [1, 5, 17, 33, 64, 65, 130, 200, 257]
+SPLIT_MS = [1, 5, 17, 33, 64, 65, 130, 200, 257, 1000]
 
 
 @pytest.mark.parametrize("K,N,bits,gs,desc,sdt,xdt", [

@@ -573,7 +573,8 @@ static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 //     K split up to ~224 workgroups when it gives fewer than ~150;
 //   * 32-input segments: the 128 x 128 tile (wave 128 x 16), split the same way.
 // Split K only while one slice of partial sums stays addressable by 32-bit offsets and the rows
-// are one launch.
+// are one launch (14336 x 4096 at M = 1024, the 128 x 256 tile unsplit: 179 us; an earlier fixed
+// 768-row limit had kept such calls unsplit).
 static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
   TiledPlan p;
   p.KS = 1;
@@ -603,7 +604,9 @@ static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
     }
   }
 #endif
-  if (p.KS > 1 && (M * (int64_t)L->N * 4 > (int64_t)INT32_MAX || M > 768)) p.KS = 1;
+  // one row slice of launch_tiled (x and y offsets below 2^31) must hold all M rows
+  const int64_t row_slice = ((int64_t(1) << 31) - 1) / (2 * (int64_t)(L->Kp > L->N ? L->Kp : L->N)) / 256 * 256;
+  if (p.KS > 1 && (M * (int64_t)L->N * 4 > (int64_t)INT32_MAX || M > row_slice)) p.KS = 1;
   if (p.KS > L->KC / 4) p.KS = L->KC / 4 > 1 ? L->KC / 4 : 1;     // at least four chunks per slice
   p.kcs = (L->KC + p.KS - 1) / p.KS;
   p.KS = (L->KC + p.kcs - 1) / p.kcs;
