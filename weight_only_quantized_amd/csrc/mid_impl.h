@@ -21,6 +21,9 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#ifdef GQ_TUNE
+#include <cstdlib>
+#endif
 #include "bufmem.h"
 #include "dequant.h"
 #include "internal.h"
@@ -228,8 +231,18 @@ inline MidPlan mid_plan(const gptq_layer* L, int64_t M) {
   if (M > mid_rows_per_pass(L)) M = mid_rows_per_pass(L);
   p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int nbk = (L->CT + kMidNW * kMidWN - 1) / (kMidNW * kMidWN);
-  int cpw = L->seg_steps == 4 ? 16 / p.MT : 4;
+  // one row block starts from 8-chunk slices while that keeps K in at most 8 slices, else from 16
+  // (MI355X, bf16 x, M = 8 / 16: the 8192 x 28672 layer 33.4 / 35.1 us with 16-chunk slices,
+  // 30.8 / 32.6 with 8; the 28672 x 8192 layer 30.8 / 33.2 with 16, 32.5 / 33.8 with 8, whose 28
+  // slices the reduction then adds)
+  int cpw = L->seg_steps == 4 ? (p.MT == 1 ? (L->KC > 64 ? 16 : 8) : 8 / (p.MT / 2)) : 4;
   while (cpw > 4 && (int64_t)nbk * ((L->KC + cpw - 1) / cpw) < 2 * 256) cpw /= 2;
+#ifdef GQ_TUNE
+  if (const char* e = getenv("GQ_MIDCPW")) {
+    const int c = atoi(e);
+    if ((c == 4 || c == 8 || c == 16) && (p.MT == 1 || c <= 8) && (p.MT < 4 || c == 4) && L->seg_steps == 4) cpw = c;
+  }
+#endif
   p.cpw = cpw;
   p.KS = (L->KC + cpw - 1) / cpw;
   return p;
