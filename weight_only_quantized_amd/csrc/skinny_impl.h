@@ -67,19 +67,21 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // sits in the metadata record and no second load is issued per chunk (2 % on the 8192-input M = 1
 // and M = 4 calls on MI355X).
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH, int ONE = 0,
-          int F32S = 1>
-__global__ void __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) __attribute__((amdgpu_waves_per_eu(2)))
+          int F32S = 1, int WPE = 2, int NWV0 = 0>
+__global__ void __launch_bounds__(64 * (NWV0 ? NWV0 : (KSPLIT > 4 ? KSPLIT : 4))) __attribute__((amdgpu_waves_per_eu(WPE)))
 skinny_kernel(const SkinnyArgs a) {
   static_assert(!ONE || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
                 "the M = 1 form needs whole-chunk segments, per-wave staging and an exact offset operand");
-  constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;  // waves per workgroup
+  constexpr int NWV = NWV0 ? NWV0 : (KSPLIT > 4 ? KSPLIT : 4);  // waves per workgroup
+  static_assert(NWV % KSPLIT == 0, "whole column groups per workgroup");
   constexpr int NT = 64 * NWV;
   constexpr int CGS = NWV / KSPLIT;             // column groups per workgroup
   constexpr int NSEG = 4 / SEG;                 // fixup segments per chunk
   constexpr int PARTS = BITS == 8 ? 2 : 1;      // loads per lane per unit
   constexpr int PW = BITS == 8 ? 4 : BITS;      // words per load
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
-  __shared__ float red[NWV][MT * TW * 4][64];
+  constexpr int NR = ONE ? 1 : 4;                // accumulator registers carried (ONE: output row 0)
+  __shared__ float red[NWV][MT * TW * NR][64];
   extern __shared__ __attribute__((aligned(16))) uint16_t xlds[];
 
   // Chunk and tile bookkeeping is wave-uniform (scalar registers).
@@ -157,12 +159,13 @@ skinny_kernel(const SkinnyArgs a) {
         c.xa[m][t] = load_b128(rx, vo, (uint32_t)kc * 256u);
       }
   };
-  // rows >= M read a zero row placed after the staged rows, so every lane's address is its fixed
-  // base plus the chunk offset (an immediate in the straight-line variants)
-  const int zero_row = a.M * xrow;
+  // A-operand rows >= M read staged row 0: an MFMA output row depends on its own A row only, and
+  // output rows >= M are never stored, so they need no zero row (which would double the LDS of an
+  // M = 1 call and halve the workgroups a compute unit holds).  Every lane's address is its fixed
+  // base plus the chunk offset (an immediate in the straight-line variants).
   int xbase[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) xbase[m] = ((m * 16 + col < a.M) ? (m * 16 + col) * xrow : zero_row) + 8 * q;
+  for (int m = 0; m < MT; ++m) xbase[m] = ((m * 16 + col < a.M) ? (m * 16 + col) * xrow : 0) + 8 * q;
   auto load_x_lds = [&](int kc, XChunk& c) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -172,7 +175,7 @@ skinny_kernel(const SkinnyArgs a) {
   };
 
   // per-chunk sums of x (ONE): TCH floats per wave after the staged rows
-  float* const xsum = reinterpret_cast<float*>(xlds + (XLDS ? (a.M + 1) * xrow : 0)) + wave * TCH;
+  float* const xsum = reinterpret_cast<float*>(xlds + (XLDS ? a.M * xrow : 0)) + wave * TCH;
   auto compute_one = [&](const WChunk& c, const XChunk& xc, int kc) {
     if constexpr (ONE) {
       const float sx = xsum[kc - kc0];
@@ -226,16 +229,14 @@ skinny_kernel(const SkinnyArgs a) {
   u32x4 ipreg[PERMUTE ? XPT : 1][2];
   const int per_row = a.Kp / 8;
   const int n8 = XLDS ? a.M * per_row : 0;        // 16-byte pieces of x (original order if iperm)
-  // Without act-order each wave stages only the inputs of its own K range (rows 0..M-1, then its
-  // part of the zero row), so no wave waits for another before its first chunk.  x_fits_lds bounds
-  // a wave's M * wpr row pieces by 64 * XLW (a fixed count of loads: a load under a branch would
-  // make the compiler wait for it at once) and its (M + 1) * wpr pieces by 64 * XSW.  With TCH > 0
+  // Without act-order each wave stages only the inputs of its own K range (rows 0..M-1), so no wave
+  // waits for another before its first chunk.  x_fits_lds bounds a wave's M * wpr row pieces by
+  // 64 * XLW (a fixed count of loads: a load under a branch would make the compiler wait for it at
+  // once).  With TCH > 0
   // every wave owns exactly TCH chunks, so the piece -> (row, input) split is a shift.
   constexpr int XLW = XLDS == 1 ? (TCH > 0 ? 4 : 8) : 1;
-  constexpr int XSW = 8;
   const int wpr = TCH > 0 ? TCH * (kChunkK / 8) : max(kc1 - kc0, 0) * (kChunkK / 8);
   const int wrows = a.M * wpr;                          // pieces loaded from x
-  const int wn8 = wrows + wpr;                          // ... plus the zero row
   u32x4 xw[XLW];
   if constexpr (XLDS == 1) {
 #pragma unroll
@@ -271,13 +272,12 @@ skinny_kernel(const SkinnyArgs a) {
 
   if constexpr (XLDS == 1) {
 #pragma unroll
-    for (int r = 0; r < XSW; ++r) {
-      if (64 * r < wn8) {                               // wave-uniform
+    for (int r = 0; r < XLW; ++r) {
+      if (64 * r < wrows) {                             // wave-uniform
         const int idx = lane + 64 * r;
-        if (idx < wn8) {
+        if (idx < wrows) {
           const int m = idx / wpr, j0 = kc0 * kChunkK + (idx - m * wpr) * 8;
-          const u32x4 v = (r < XLW && idx < wrows) ? xw[r < XLW ? r : 0] : u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(&xlds[m * xrow + j0]) = v;   // row M: the zero row
+          *reinterpret_cast<u32x4*>(&xlds[m * xrow + j0]) = xw[r];
         }
       }
     }
@@ -325,8 +325,6 @@ skinny_kernel(const SkinnyArgs a) {
         }
       }
     }
-    for (int j = threadIdx.x * 8; j < a.Kp; j += NT * 8)
-      *reinterpret_cast<u32x4*>(&xlds[zero_row + j]) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
 
@@ -374,7 +372,7 @@ skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
       for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][(m * TW + i) * 4 + r][lane] = acc[m][i][r];
+        for (int r = 0; r < NR; ++r) red[wave][(m * TW + i) * NR + r][lane] = acc[m][i][r];
     __syncthreads();
     if (ks != 0) return;
 #pragma unroll
@@ -384,7 +382,7 @@ skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
         for (int i = 0; i < TW; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[m][i][r] += red[wave + w2][(m * TW + i) * 4 + r][lane];
+          for (int r = 0; r < NR; ++r) acc[m][i][r] += red[wave + w2][(m * TW + i) * NR + r][lane];
   }
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
@@ -453,15 +451,17 @@ inline bool skinny_reads_x_from_l2(int64_t M, int KC, int CT, int bits, int seg_
 }
 
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE, int F32S,
-          int SEG1 = 1>   // SEG1 = 0: whole-chunk groups only (no 32-input-segment kernel is built)
+          int SEG1 = 1,   // SEG1 = 0: whole-chunk groups only (no 32-input-segment kernel is built)
+          int WPE = 2,    // minimum waves per SIMD the register allocation must allow
+          int NWV0 = 0>   // waves per workgroup (0: max(KSPLIT, 4)); a multiple of KSPLIT
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
-  constexpr int NWV = KSPLIT > 4 ? KSPLIT : 4;
+  constexpr int NWV = NWV0 ? NWV0 : (KSPLIT > 4 ? KSPLIT : 4);
   constexpr int CGS = NWV / KSPLIT;
   const int blocks = (a.CT + TW * CGS - 1) / (TW * CGS);
-  // staged rows + the zero row (+ the per-chunk sums of x of every wave, ONE)
-  const size_t lds = (XLDS ? (size_t)(a.M + 1) * (a.Kp + 8) * 2 : 0) + (ONE ? (size_t)NWV * TCH * 4 : 0);
+  // staged rows (+ the per-chunk sums of x of every wave, ONE)
+  const size_t lds = (XLDS ? (size_t)a.M * (a.Kp + 8) * 2 : 0) + (ONE ? (size_t)NWV * TCH * 4 : 0);
   if (seg == 4)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S>), dim3(blocks),
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S, WPE, NWV0>), dim3(blocks),
                        dim3(64 * NWV), lds, s, a);
   else if constexpr (TCH == 0 && SEG1)
     hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0, 0, F32S>), dim3(blocks),
@@ -493,7 +493,13 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     // 8192-input layer); fp16 keeps its exact operands (no gain measured)
     constexpr int ONE = XT == 1 && BITS <= 4;
     if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16, ONE, F32S>(a, seg, s);
-    if (a.M == 1 && seg == 4 && a.KC == 64) return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE, F32S>(a, seg, s);
+    // 8192 inputs: eight waves of 8 chunks with every load of a wave's range issued at once
+    // (70B gate_proj 28672 x 8192, bf16: 22.2 -> 20.9 us on MI355X against four waves of 16);
+    // wider codes keep four waves of 16 (their 8-deep ring would not fit the registers)
+    if (a.M == 1 && seg == 4 && a.KC == 64) {
+      if constexpr (BITS == 4) return run_tch<BITS, XT, 1, 1, 8, 1, 8, 8, ONE, F32S>(a, seg, s);
+      else return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE, F32S>(a, seg, s);
+    }
     // 5120 / 6144 / 7168 inputs: five to seven waves of 8 straight-line chunks (the four-wave
     // split would leave a loop of 10 to 14 chunks per wave)
     if (a.M == 1 && seg == 4 && a.KC == 24) return run_tch<BITS, XT, 1, 1, 6, 1, 2, 4, ONE, F32S, 0>(a, seg, s);
