@@ -7,9 +7,11 @@ sides reach the inverse-Hessian factor by different routes (rocSOLVER: one facto
 reversed H and a triangular inverse; LAPACK through the page's three steps), so the rows they use
 differ in the last few bits; a decision within that distance of a
 rounding boundary may flip, and the flip then propagates along its row through the error
-feedback (rows are independent).  The bar: g_idx exact; at least 95 % of rows identical in every
-code, their grids equal (zeros exactly, scales to 1e-5); the layer's output error within 2 % of
-the oracle's.  Where no error is fed back (a diagonal Hessian) every code must be bit-exact."""
+feedback (rows are independent).  Observed on MI355X: every row of every layer below identical.
+The bar: g_idx exact; at most one row per layer with a differing code (room for one such flip),
+the identical rows' grids equal (zeros exactly, scales to 1e-5); the layer's output error within
+2 % of the oracle's.  Where no error is fed back (a diagonal Hessian) every code must be
+bit-exact."""
 import sys
 
 import numpy as np
@@ -83,7 +85,8 @@ def test_quantize_matches_oracle(N, K, bits, gs, act):
     assert np.array_equal(g, rg)
     assert c.max() <= 2 ** bits - 1 and z.min() >= 0 and z.max() <= 2 ** bits - 1 and np.all(s > 0)
     same = np.all(c == rc, axis=1)
-    assert same.mean() >= 0.95, same.mean()
+    say("rows identical in every code:", same.mean(), "codes equal:", np.mean(c == rc))
+    assert np.count_nonzero(~same) <= 1, same.mean()
     assert np.array_equal(z[same], rz[same])
     assert np.allclose(s[same], rs[same], rtol=1e-5, atol=0)
     lg, lr = q.layer_loss(W, c, s, z, g, X), q.layer_loss(W, rc, rs, rz, rg, X)

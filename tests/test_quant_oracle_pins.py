@@ -2,7 +2,9 @@
 it must reduce to round-to-nearest when the Hessian is a multiple of the identity, agree with the
 sequential Optimal-Brain-Quantization elimination written from the explicit inverse Hessian (no
 Cholesky, no lazy batching), not depend on the lazy block size, lower the layer's output error
-below round-to-nearest's, and zero never-active inputs exactly."""
+below round-to-nearest's, and zero never-active inputs exactly.  The Hessian 2 X^T X / n and the
+output-error objective are pinned by hand-worked values and exact rationals ("39. Quantized
+checkpoints ...", section "GPTQ": the objective and H = 2 X^T X)."""
 import numpy as np
 import pytest
 
@@ -118,3 +120,56 @@ def test_never_active_inputs_quantize_to_exact_zero():
     c, s, z, g = q.gptq_quantize(W, q.hessian(X), 4, 32, act_order=True)
     deq = s[:, g] * (c.astype(np.float32) - z[:, g])
     assert np.all(deq[:, [3, 50, 77]] == 0)
+
+
+def test_hessian_hand_computed_two_inputs():
+    """H = 2 X^T X / n worked by hand: X = [[1, 0], [2, 1], [0, 3], [1, 1]] (n = 4) gives
+    X^T X = [[6, 3], [3, 11]], so H = [[3, 1.5], [1.5, 5.5]] (a dropped factor 2 or a dropped 1/n
+    gives another matrix)."""
+    X = np.array([[1, 0], [2, 1], [0, 3], [1, 1]], dtype=np.float32)
+    H = q.hessian(X)
+    assert H.dtype == np.float32
+    assert np.array_equal(H, np.array([[3.0, 1.5], [1.5, 5.5]], dtype=np.float32))
+
+
+def test_hessian_exact_rationals():
+    """Every entry equals the exact rational sum over rows of 2 x_s,i x_s,j / n, rounded once to
+    float32 (inputs on a dyadic grid, so the rational is computed without error)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    n, K = 7, 5
+    X = (rng.integers(-64, 65, size=(n, K)) / 16.0).astype(np.float32)
+    H = q.hessian(X)
+    for i in range(K):
+        for j in range(K):
+            exact = sum(Fraction(float(X[s, i])) * Fraction(float(X[s, j])) for s in range(n)) * 2 / n
+            assert H[i, j] == np.float32(float(exact)), (i, j)
+    assert np.array_equal(H, H.T)
+
+
+def test_layer_loss_hand_computed():
+    """||X Wq^T - X W^T||^2 worked by hand.  W = [[1, -2], [0.5, 0]]; the codes, scales and zeros
+    give Wq = [[1.5, -2], [0.5, 0.25]] (one group: scale 0.25, zeros 8 and 2), so Wq - W =
+    [[0.5, 0], [0, 0.25]]; with X = [[2, 1], [0, 3]], X (Wq - W)^T = [[1, 0.25], [0, 0.75]] and the
+    loss is 1 + 0.0625 + 0 + 0.5625 = 1.625."""
+    W = np.array([[1.0, -2.0], [0.5, 0.0]], dtype=np.float32)
+    codes = np.array([[14, 0], [4, 3]], dtype=np.uint8)
+    scales = np.array([[0.25], [0.25]], dtype=np.float32)
+    zeros = np.array([[8], [2]], dtype=np.int32)
+    g_idx = np.array([0, 0], dtype=np.int32)
+    X = np.array([[2.0, 1.0], [0.0, 3.0]])
+    assert q.layer_loss(W, codes, scales, zeros, g_idx, X) == 1.625
+    # and it is zero exactly when the quantized weights equal the weights
+    assert q.layer_loss(scales[:, [0, 0]] * (codes.astype(np.float32) - zeros[:, [0, 0]]), codes, scales, zeros,
+                        g_idx, X) == 0.0
+
+
+def test_layer_loss_uses_g_idx():
+    """With act-order groups the loss reads each input's own group: swapping g_idx changes it."""
+    W = np.zeros((1, 2), dtype=np.float32)
+    codes = np.array([[1, 1]], dtype=np.uint8)
+    scales = np.array([[1.0, 2.0]], dtype=np.float32)
+    zeros = np.array([[0, 0]], dtype=np.int32)
+    X = np.array([[1.0, 0.0]])
+    assert q.layer_loss(W, codes, scales, zeros, np.array([0, 1], dtype=np.int32), X) == 1.0
+    assert q.layer_loss(W, codes, scales, zeros, np.array([1, 0], dtype=np.int32), X) == 4.0
