@@ -23,7 +23,8 @@
  *    the calling thread.
  *  - The library is thread-safe for calls on distinct handles.  A handle is immutable after
  *    gptq_repack, so gptq_gemm may run on one handle from several streams at once as long as
- *    each call has its own workspace.
+ *    each call has its own workspace.  Handles are checked against the set of live handles: a
+ *    destroyed or never-issued pointer returns GPTQ_E_INVALID_ARG.
  */
 #ifndef GPTQ_MI355X_H
 #define GPTQ_MI355X_H
@@ -136,10 +137,16 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
                         const void* scales, const int32_t* g_idx, void* stream, gptq_handle_t* out);
 
 /* Device bytes of workspace gptq_gemm needs for this handle, M, activation dtype and path
- * (0 when none).  The size depends only on (handle, M, x_dtype, path): act-order layers need a
- * sorted copy of x; the TILED family also copies x when in_features is not a multiple of 128
- * (rows zero-padded) and, for BF16 activations, makes that copy fp16 (exactly rescaled per row
- * by a power of two) with one exponent per row. */
+ * (0 when none).  "Kernel Backends Reference", section "Marlin and caller-owned scratch" (its
+ * scratch API): the caller may supply the GEMM's scratch, the size query and the GEMM share one
+ * size calculation, and supplied scratch that is too small or misaligned makes the GEMM fail
+ * rather than fall back -- here gptq_gemm calls this same function and returns GPTQ_E_WORKSPACE.
+ * The size depends only on (handle, M, x_dtype, path): act-order layers need a sorted copy of x;
+ * the TILED family also copies x when in_features is not a multiple of 128 (rows zero-padded)
+ * and, for BF16 activations, makes that copy fp16 (exactly rescaled per row by a power of two)
+ * with one exponent per row; calls split along K add their fp32 partial sums.
+ * Errors: GPTQ_E_INVALID_ARG (handle not live, bytes NULL, M < 0, bad dtype or path, SKINNY with
+ * M > 64).  Host-only: touches no device memory. */
 gptq_status gptq_workspace_size(gptq_handle_t h, int64_t M, int32_t x_dtype, int32_t path,
                                 size_t* bytes);
 
@@ -167,14 +174,30 @@ gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype
 gptq_status gptq_gemm_bias(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, const void* bias, void* y,
                            void* workspace, size_t workspace_bytes, int32_t path, void* stream);
 
-/* Frees the handle's device memory (after synchronising the device).  NULL is accepted. */
+/* Frees the handle's device memory after synchronising its device.  "Kernel Backends Reference",
+ * "Kernel implementation and validation checklist" item 5: a runtime handle must be invalidated
+ * when the layer it was built from changes -- a changed checkpoint needs gptq_destroy and a new
+ * gptq_repack (the handle never aliases the checkpoint tensors).  The library keeps the set of
+ * live handles: after this call the pointer is no longer live, and any later call with it
+ * (gptq_destroy included) returns GPTQ_E_INVALID_ARG without reading the freed memory.  NULL is
+ * accepted (GPTQ_OK).  Errors: GPTQ_E_INVALID_ARG (not a live handle), GPTQ_E_HIP (the device
+ * synchronisation failed; the memory is freed regardless). */
 gptq_status gptq_destroy(gptq_handle_t h);
 
-/* Handle properties (sizes, groups, whether a permutation is in effect). */
+/* Handle properties.  "Kernel Backends Reference", section "Packed storage and execution concepts":
+ * after the runtime initialisation a layer no longer exposes the checkpoint's tensors, so this is
+ * where callers read what the runtime layout holds -- the layer's sizes, groups, padded input
+ * width, whether a load-time permutation is in effect, and runtime_bytes, the device memory the
+ * handle owns (the section "Pitfalls" warns against estimating memory from checkpoint bytes).
+ * Errors: GPTQ_E_INVALID_ARG (handle not live, info NULL).  Host-only. */
 gptq_status gptq_info(gptq_handle_t h, gptq_handle_info* info);
 
 /* Test hook: reads the runtime layout back and decodes it on the host into the checkpoint's
- * logical values, in ORIGINAL input order:
+ * logical values, in ORIGINAL input order.  "Kernel Backends Reference", "Kernel implementation and
+ * validation checklist" item 6 asks repack changes to be checked against an independent oracle;
+ * this is how tests compare the runtime layout with the oracle's unpack, bit for bit.  The section
+ * "Pitfalls" says a private runtime layout must not be saved under a checkpoint format: this hook
+ * returns logical values, never the runtime words.
  *   codes_kn_host  uint8 [K * N]  code[k, n] at k * N + n
  *   zeros_gn_host  int32 [G * N]  zero[g, n] (GPTQ: stored + 1; AWQ_GEMM: as stored)
  *   scales_gn_host uint32 [G * N] raw scale bits (16-bit patterns zero-extended, or f32 bits)
@@ -184,10 +207,15 @@ gptq_status gptq_info(gptq_handle_t h, gptq_handle_info* info);
 gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t* zeros_gn_host,
                                 uint32_t* scales_gn_host, int32_t* perm_host);
 
-/* Static message for a status code. */
+/* Static message for a status code, naming the rule of "GPTQ packed checkpoint (safetensors /
+ * torch)", section "Reject the file when", where a status stands for one (GPTQ-001 .. GPTQ-005).
+ * Unknown codes give "unknown status".  Never NULL; the string is owned by the library. */
 const char* gptq_status_str(gptq_status s);
 
-/* hipError_t behind the calling thread's last GPTQ_E_HIP (0 if none). */
+/* hipError_t behind the calling thread's last GPTQ_E_HIP (0 if none).  Thread-local: a failure is
+ * reported to the thread that made the call, never silently replaced by another path ("Kernel
+ * Backends Reference", section "Marlin and caller-owned scratch": failures are reported, not
+ * papered over by a fallback). */
 int32_t gptq_last_hip_error(void);
 
 /* ---- GPTQ quantizer: the step that produces a layer's codes -------------------------------------

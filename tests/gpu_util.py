@@ -66,9 +66,13 @@ def out_ulp(y_ref, x_tag):
 
 
 def check(y_bits, x_tag, y_ref, label=""):
-    """rel-L2 and max-abs bars of the layer.  The max-abs bar (2e-2 * rms) is below the output dtype's
-    own rounding for outputs far above the rms (bf16: beyond ~10 rms); there each output must be
-    within one unit in the last place of y_ref instead, which a correctly rounded result is."""
+    """rel-L2 and max-abs bars of the layer (rel-L2 1e-3 for fp16 outputs, 4e-3 for bf16; max-abs
+    2e-2 * rms(y_ref)).  The max-abs bar sits below the output dtype's own rounding for outputs far
+    above the rms (bf16 carries 8 significant bits, so beyond ~10 rms half a unit in the last place
+    exceeds 2e-2 * rms): only for those elements, where half an ulp of y_ref is larger than the bar,
+    the bound is half an ulp plus the bar (the correctly rounded result is within half an ulp of the
+    fp32 sum, and the fp32 sum within far less than the bar of y_ref).  Every other element keeps
+    the bar itself."""
     m = o.compare(y_bits, x_tag, y_ref)
     tol = TOL[x_tag]
     assert m["nonfinite"] == 0, (label, m)
@@ -76,6 +80,12 @@ def check(y_bits, x_tag, y_ref, label=""):
     if m["max_abs_over_rms"] > tol["max_abs_over_rms"]:
         y = o.decode_float_bits(y_bits, x_tag)
         ref = np.asarray(y_ref, dtype=np.float64)
-        bound = np.maximum(tol["max_abs_over_rms"] * m["rms_ref"], out_ulp(ref, x_tag))
-        assert np.all(np.abs(y - ref) <= bound), (label, m)
+        bar = tol["max_abs_over_rms"] * m["rms_ref"]
+        half_ulp = 0.5 * out_ulp(ref, x_tag)
+        wide = half_ulp > bar
+        err = np.abs(y - ref)
+        assert np.all(err[~wide] <= bar), (label, m, float(err[~wide].max()) / m["rms_ref"])
+        assert np.all(err[wide] <= half_ulp[wide] + bar), (label, m)
+        print(f"half-ulp bar used: {label} ({int(np.count_nonzero(wide & (err > bar)))} outputs past "
+              f"2e-2 rms, {int(np.count_nonzero(wide))} where half an ulp exceeds it)", flush=True)
     return m

@@ -139,10 +139,38 @@ def validate(desc: Desc, g_idx_host=None) -> int:
     return lib.gptq_validate(ctypes.byref(desc), None)
 
 
-def _stream_ptr(stream=None):
-    import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+class _OnStream:
+    """Run one library call on `stream` (default: the current stream).  When that is not the
+    current stream, it first waits for the current stream (which produced the inputs), tensors
+    created inside the block are allocated on it, and `keep(t)` records caller tensors on it so
+    that torch's caching allocator does not hand their memory to other work while the call may
+    still read or write them."""
+
+    def __init__(self, stream, device):
+        import torch
+        self.cur = torch.cuda.current_stream(device)
+        self.stream = stream if stream is not None else self.cur
+        self.side = self.stream.cuda_stream != self.cur.cuda_stream
+        self._ctx = torch.cuda.stream(self.stream)
+
+    def __enter__(self):
+        if self.side:
+            self.stream.wait_stream(self.cur)
+        self._ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        return self._ctx.__exit__(*exc)
+
+    def keep(self, *tensors):
+        if self.side:
+            for t in tensors:
+                if t is not None:
+                    t.record_stream(self.stream)
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.stream.cuda_stream)
 
 
 class Handle:
@@ -175,35 +203,41 @@ class Handle:
     def gemm(self, x, out=None, workspace=None, path=PATH_AUTO, stream=None, bias=None):
         """y = x . W^T (+ bias); x [M, K] fp16/bf16 on this handle's GPU; bias, when given, an [N]
         tensor in the scales' dtype (gptq_gemm_bias).  `workspace` (uint8 tensor) is allocated from
-        torch's caching allocator when not given."""
+        torch's caching allocator when not given.  With `stream` (a torch stream) the call runs on
+        it after the current stream's pending work; two calls in flight at once need workspaces of
+        their own."""
         import torch
         if x.dim() != 2 or x.shape[1] != self.K:
             raise ValueError(f"x must be [M, {self.K}]")
-        x = x.contiguous()
-        M = x.shape[0]
-        if out is None:
-            out = torch.empty((M, self.N), dtype=x.dtype, device=x.device)
-        elif out.shape != (M, self.N) or out.dtype != x.dtype or not out.is_contiguous():
+        if out is not None and (tuple(out.shape) != (x.shape[0], self.N) or out.dtype != x.dtype
+                                or not out.is_contiguous()):
             raise ValueError("out must be a contiguous [M, N] tensor of x's dtype")
+        if bias is not None:
+            if bias.dim() != 1 or bias.shape[0] != self.N or not bias.is_contiguous():
+                raise ValueError(f"bias must be a contiguous [{self.N}] tensor")
+            if _dtype_code(bias.dtype) != self.info()["scales_dtype"]:
+                raise TypeError("bias must have the scales' dtype")
+        M = x.shape[0]
         need = self.workspace_size(M, x.dtype, path)
-        if workspace is None and need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-        ws_ptr = workspace.data_ptr() if workspace is not None else None
-        ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        if bias is None:
-            st = self._lib.gptq_gemm(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), out.data_ptr(), ws_ptr, ws_n,
-                                     path, _stream_ptr(stream))
-            if st:
-                raise GPTQError(st, "gptq_gemm", self._lib)
-            return out
-        if bias.dim() != 1 or bias.shape[0] != self.N or not bias.is_contiguous():
-            raise ValueError(f"bias must be a contiguous [{self.N}] tensor")
-        if _dtype_code(bias.dtype) != self.info()["scales_dtype"]:
-            raise TypeError("bias must have the scales' dtype")
-        st = self._lib.gptq_gemm_bias(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), bias.data_ptr(), out.data_ptr(),
-                                      ws_ptr, ws_n, path, _stream_ptr(stream))
+        with _OnStream(stream, x.device) as on:
+            on.keep(x, out, workspace, bias)
+            x = x.contiguous()
+            if out is None:
+                out = torch.empty((M, self.N), dtype=x.dtype, device=x.device)
+            if workspace is None and need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            ws_ptr = workspace.data_ptr() if workspace is not None else None
+            ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            if bias is None:
+                st = self._lib.gptq_gemm(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), out.data_ptr(), ws_ptr,
+                                         ws_n, path, on.ptr)
+                where = "gptq_gemm"
+            else:
+                st = self._lib.gptq_gemm_bias(self.ptr, x.data_ptr(), M, _dtype_code(x.dtype), bias.data_ptr(),
+                                              out.data_ptr(), ws_ptr, ws_n, path, on.ptr)
+                where = "gptq_gemm_bias"
         if st:
-            raise GPTQError(st, "gptq_gemm_bias", self._lib)
+            raise GPTQError(st, where, self._lib)
         return out
 
     def decode(self) -> dict:
@@ -262,8 +296,9 @@ def repack(qweight, qzeros, scales, g_idx=None, *, bits, group_size, desc_act=Fa
     d = make_desc(K, N, bits, group_size, _dtype_code(scales.dtype), qweight.shape, qzeros.shape, scales.shape,
                   0 if g_idx is None else g_idx.shape[0], desc_act, checkpoint_format)
     out = ctypes.c_void_p()
-    st = lib.gptq_repack(ctypes.byref(d), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
-                         None if g_idx is None else g_idx.data_ptr(), _stream_ptr(stream), ctypes.byref(out))
+    with _OnStream(stream, qweight.device) as on:       # gptq_repack synchronises its stream
+        st = lib.gptq_repack(ctypes.byref(d), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                             None if g_idx is None else g_idx.data_ptr(), on.ptr, ctypes.byref(out))
     if st:
         raise GPTQError(st, "gptq_repack", lib)
     return Handle(lib, out, K, N, bits, group_size)
@@ -276,8 +311,10 @@ def hessian(x, stream=None):
     if not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
         raise ValueError("x must be a contiguous 2-D GPU tensor")
     S, K = x.shape
-    H = torch.empty((K, K), dtype=torch.float32, device=x.device)
-    st = lib.gptq_hessian(x.data_ptr(), S, K, _dtype_code(x.dtype), H.data_ptr(), _stream_ptr(stream))
+    with _OnStream(stream, x.device) as on:
+        on.keep(x)
+        H = torch.empty((K, K), dtype=torch.float32, device=x.device)
+        st = lib.gptq_hessian(x.data_ptr(), S, K, _dtype_code(x.dtype), H.data_ptr(), on.ptr)
     if st:
         raise GPTQError(st, "gptq_hessian", lib)
     return H
@@ -296,18 +333,19 @@ def quantize(W, H, *, bits=4, group_size=128, act_order=False, damp=0.01, stream
         raise ValueError("H must be [K, K]")
     G = 1 if group_size == -1 else -(-K // group_size)
     dev = W.device
-    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    scales = torch.empty((N, G), dtype=torch.float32, device=dev)
-    zeros = torch.empty((N, G), dtype=torch.int32, device=dev)
-    g_idx = torch.empty((K,), dtype=torch.int32, device=dev)
     n = ctypes.c_size_t(0)
     st = lib.gptq_quantize_workspace_size(N, K, ctypes.byref(n))
     if st:
         raise GPTQError(st, "gptq_quantize_workspace_size", lib)
-    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
     p = QuantParams(bits, group_size, int(bool(act_order)), float(damp), 0)
-    st = lib.gptq_quantize(W.data_ptr(), H.data_ptr(), N, K, ctypes.byref(p), codes.data_ptr(), scales.data_ptr(),
-                           zeros.data_ptr(), g_idx.data_ptr(), ws.data_ptr(), n.value, _stream_ptr(stream))
+    with _OnStream(stream, dev) as on:                  # gptq_quantize synchronises its stream
+        codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        scales = torch.empty((N, G), dtype=torch.float32, device=dev)
+        zeros = torch.empty((N, G), dtype=torch.int32, device=dev)
+        g_idx = torch.empty((K,), dtype=torch.int32, device=dev)
+        ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+        st = lib.gptq_quantize(W.data_ptr(), H.data_ptr(), N, K, ctypes.byref(p), codes.data_ptr(),
+                               scales.data_ptr(), zeros.data_ptr(), g_idx.data_ptr(), ws.data_ptr(), n.value, on.ptr)
     if st:
         raise GPTQError(st, "gptq_quantize", lib)
     return codes, scales, zeros, g_idx
@@ -323,12 +361,14 @@ def pack(codes, scales, zeros, *, bits, group_size, checkpoint_format="gptq_v2",
     G = scales.shape[1]
     sdt = torch.float16 if scales_dtype is None else scales_dtype
     dev = codes.device
-    qweight = torch.empty((K * bits // 32, N), dtype=torch.int32, device=dev)
-    qzeros = torch.empty((G, N * bits // 32), dtype=torch.int32, device=dev)
-    s_out = torch.empty((G, N), dtype=sdt, device=dev)
     fmt = FORMATS[checkpoint_format] if isinstance(checkpoint_format, str) else int(checkpoint_format)
-    st = lib.gptq_pack(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, bits, group_size, fmt,
-                       _dtype_code(sdt), qweight.data_ptr(), qzeros.data_ptr(), s_out.data_ptr(), _stream_ptr(stream))
+    with _OnStream(stream, dev) as on:
+        on.keep(codes, scales, zeros)
+        qweight = torch.empty((K * bits // 32, N), dtype=torch.int32, device=dev)
+        qzeros = torch.empty((G, N * bits // 32), dtype=torch.int32, device=dev)
+        s_out = torch.empty((G, N), dtype=sdt, device=dev)
+        st = lib.gptq_pack(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, bits, group_size, fmt,
+                           _dtype_code(sdt), qweight.data_ptr(), qzeros.data_ptr(), s_out.data_ptr(), on.ptr)
     if st:
         raise GPTQError(st, "gptq_pack", lib)
     return qweight, qzeros, s_out

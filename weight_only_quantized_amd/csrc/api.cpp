@@ -13,6 +13,7 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <unordered_set>
 #include <vector>
 
 #include "internal.h"
@@ -125,13 +126,31 @@ static void free_layer(gptq_layer* L) {
   if (L->scale32) (void)hipFree(L->scale32);
   if (L->perm) (void)hipFree(L->perm);
   if (L->iperm) (void)hipFree(L->iperm);
-  L->magic = 0;
   delete L;
 }
 
+// Live handles: every handle gptq_repack returned and gptq_destroy has not yet taken back.  A
+// handle is checked by membership, so a destroyed (or never issued) pointer is refused without
+// reading the memory it points to.
+static std::mutex g_live_mu;
+static std::unordered_set<const gptq_layer*>& live_handles() {
+  static std::unordered_set<const gptq_layer*> s;
+  return s;
+}
+static void register_handle(const gptq_layer* L) {
+  std::lock_guard<std::mutex> g(g_live_mu);
+  live_handles().insert(L);
+}
+// Removes h from the live set; false if it was not there.
+static bool retire_handle(const gptq_layer* L) {
+  std::lock_guard<std::mutex> g(g_live_mu);
+  return live_handles().erase(L) == 1;
+}
+
 static gptq_status check_handle(gptq_handle_t h) {
-  if (!h || h->magic != GQ_MAGIC) return GPTQ_E_INVALID_ARG;
-  return GPTQ_OK;
+  if (!h) return GPTQ_E_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_live_mu);
+  return live_handles().count(h) ? GPTQ_OK : GPTQ_E_INVALID_ARG;
 }
 
 }  // namespace gq
@@ -181,7 +200,6 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
   gptq_layer* L = new (std::nothrow) gptq_layer();
   if (!L) return GPTQ_E_OOM;
   std::memset(L, 0, sizeof(*L));
-  L->magic = GQ_MAGIC;
   L->device = dev;
   L->K = K; L->N = N; L->group_size = desc->group_size;
   L->ckpt_bits = desc->bits;
@@ -232,6 +250,7 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
     }
     L->bytes += (int64_t)sizeof(int32_t) * K;
   }
+  register_handle(L);
   *out = L;
   return GPTQ_OK;
 }
@@ -336,8 +355,7 @@ gptq_status gptq_gemm_bias(gptq_handle_t h, const void* x, int64_t M, int32_t x_
 
 gptq_status gptq_destroy(gptq_handle_t h) {
   if (!h) return GPTQ_OK;
-  gptq_status st = check_handle(h);
-  if (st != GPTQ_OK) return st;
+  if (!retire_handle(h)) return GPTQ_E_INVALID_ARG;   // destroyed already, or never issued
   int cur = -1;
   (void)hipGetDevice(&cur);
   if (cur != h->device) (void)hipSetDevice(h->device);

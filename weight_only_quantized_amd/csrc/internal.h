@@ -7,10 +7,7 @@
 #include "gptq_mi355x.h"
 #include "layout.h"
 
-#define GQ_MAGIC 0x47505451u  // "GPTQ"
-
 struct gptq_layer {
-  uint32_t magic;
   int device;
   int K, N, bits, group_size, gs_eff, G, Kp, KC, CT;   // bits: runtime code width (2/3/4/8)
   int ckpt_bits;      // the checkpoint's code width (bits, or 5/6/7 for planar layers run as 8)
