@@ -53,8 +53,13 @@ typedef enum {
   GPTQ_E_OOM = 6,         /* device allocation for the runtime layout failed */
   GPTQ_E_WORKSPACE = 7,   /* workspace smaller than gptq_workspace_size() or not 256-B aligned */
   GPTQ_E_DEVICE = 8,      /* no gfx950 device, or the handle lives on another device */
-  GPTQ_E_NUMERIC = 9      /* gptq_quantize: the damped Hessian is not positive definite */
+  GPTQ_E_NUMERIC = 9,     /* gptq_quantize: the damped Hessian is not positive definite */
+  GPTQ_E_SCRATCH_LIMIT = 10 /* gptq_gemm_noalloc: the call needs more than
+                               GPTQ_NOALLOC_SCRATCH_BYTES of scratch */
 } gptq_status;
+
+/* Size of the static scratch buffer behind gptq_gemm_noalloc (bytes, per device). */
+#define GPTQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype;
 
@@ -173,6 +178,24 @@ gptq_status gptq_gemm(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype
  * Everything else (arguments, workspace, errors, graph capture) is as for gptq_gemm. */
 gptq_status gptq_gemm_bias(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, const void* bias, void* y,
                            void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
+/* gptq_gemm_bias (bias may be NULL, then it is gptq_gemm) for callers that cannot allocate or pass
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The call's scratch (the sorted or fp16 copy of x, row exponents, split-K partial
+ * sums) lives in a static device buffer of GPTQ_NOALLOC_SCRATCH_BYTES (32 MiB) that the library
+ * holds on every device it runs on until the process ends; no device memory is allocated or freed
+ * by this call, and no workspace is passed.  The first call on a device (a call with M == 0 will do)
+ * looks up that device's buffer once; later calls only launch kernels.
+ * Every call on one device shares that device's buffer and leaves its last contents there (nothing
+ * in it needs to start at zero): calls that may overlap in time on one device -- on different
+ * streams, or from different threads -- race on it and must be ordered by the caller (one stream,
+ * or events).  gptq_gemm with its own workspace has no such restriction.
+ * Arguments, layouts, results and other errors are those of gptq_gemm_bias.  Errors:
+ * GPTQ_E_SCRATCH_LIMIT when gptq_workspace_size() for this (handle, M, x_dtype, path) exceeds the
+ * buffer (nothing is launched; typically prefill-sized M: use gptq_gemm with a workspace), and
+ * GPTQ_E_DEVICE when the current device is not the handle's. */
+gptq_status gptq_gemm_noalloc(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, const void* bias, void* y,
+                              int32_t path, void* stream);
 
 /* Frees the handle's device memory after synchronising its device.  "Kernel Backends Reference",
  * "Kernel implementation and validation checklist" item 5: a runtime handle must be invalidated

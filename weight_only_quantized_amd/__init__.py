@@ -19,13 +19,15 @@ __all__ = ["LIB_PATH", "GPTQError", "Desc", "Handle", "load_library", "repack", 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi355x.so")
 
 STATUS = {0: "OK", 1: "E_INVALID_ARG", 2: "E_SHAPE", 3: "E_GIDX", 4: "E_UNSUPPORTED", 5: "E_HIP",
-          6: "E_OOM", 7: "E_WORKSPACE", 8: "E_DEVICE", 9: "E_NUMERIC"}
+          6: "E_OOM", 7: "E_WORKSPACE", 8: "E_DEVICE", 9: "E_NUMERIC", 10: "E_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 32 << 20    # GPTQ_NOALLOC_SCRATCH_BYTES
 F16, BF16, F32 = 0, 1, 2
 FORMATS = {"gptq": 0, "marlin": 1, "gptq_v2": 2, "awq_gemm": 3, "gptq_p": 4}
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
 # Every symbol include/gptq_mi355x.h declares.
-symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
+symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_gemm_noalloc",
+           "gptq_destroy",
            "gptq_info", "gptq_decode_runtime", "gptq_status_str", "gptq_last_hip_error", "gptq_hessian",
            "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack"]
 
@@ -83,6 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_workspace_size.argtypes = [P, I64, I32, I32, ctypes.POINTER(SZ)]
     lib.gptq_gemm.argtypes = [P, P, I64, I32, P, P, SZ, I32, P]
     lib.gptq_gemm_bias.argtypes = [P, P, I64, I32, P, P, P, SZ, I32, P]
+    lib.gptq_gemm_noalloc.argtypes = [P, P, I64, I32, P, P, I32, P]
     lib.gptq_destroy.argtypes = [P]
     lib.gptq_info.argtypes = [P, ctypes.POINTER(Info)]
     lib.gptq_decode_runtime.argtypes = [P, P, P, P, P]
@@ -93,7 +96,8 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_quantize_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
     lib.gptq_quantize.argtypes = [P, P, I32, I32, ctypes.POINTER(QuantParams), P, P, P, P, P, SZ, P]
     lib.gptq_pack.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]
-    for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_destroy",
+    for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_gemm_noalloc",
+              "gptq_destroy",
               "gptq_info", "gptq_decode_runtime", "gptq_last_hip_error", "gptq_hessian",
               "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack"):
         getattr(lib, f).restype = I32

@@ -153,6 +153,31 @@ static gptq_status check_handle(gptq_handle_t h) {
   return live_handles().count(h) ? GPTQ_OK : GPTQ_E_INVALID_ARG;
 }
 
+// Library-owned scratch of gptq_gemm_noalloc, one copy per device for the life of the process.  In
+// host code `scratch` is only the host-side stand-in of the symbol: its device address (different on
+// every device) comes from hipGetSymbolAddress, taken once per device with that device current and
+// kept in g_scratch_dev, and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = GPTQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];
+
+// Device address of the current device's scratch (dev is the current device).
+static gptq_status scratch_of_device(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxDevices) return GPTQ_E_DEVICE;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p || !aligned(p, 256)) return GPTQ_E_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return GPTQ_OK;
+}
+
 }  // namespace gq
 
 using namespace gq;
@@ -353,6 +378,24 @@ gptq_status gptq_gemm_bias(gptq_handle_t h, const void* x, int64_t M, int32_t x_
   return gemm_impl(h, x, M, x_dtype, bias, y, workspace, workspace_bytes, path, stream);
 }
 
+gptq_status gptq_gemm_noalloc(gptq_handle_t h, const void* x, int64_t M, int32_t x_dtype, const void* bias, void* y,
+                              int32_t path, void* stream) {
+  gptq_status st = check_handle(h);
+  if (st != GPTQ_OK) return st;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev != h->device) return GPTQ_E_DEVICE;
+  void* ws = nullptr;
+  st = scratch_of_device(dev, &ws);              // one-time set-up per device (no allocation)
+  if (st != GPTQ_OK) return st;
+  size_t need = 0;
+  st = gptq_workspace_size(h, M, x_dtype, path, &need);
+  if (st != GPTQ_OK) return st;
+  if (need > kScratchBytes) return GPTQ_E_SCRATCH_LIMIT;
+  return gemm_impl(h, x, M, x_dtype, bias, y, ws, kScratchBytes, path, stream);
+}
+
 gptq_status gptq_destroy(gptq_handle_t h) {
   if (!h) return GPTQ_OK;
   if (!retire_handle(h)) return GPTQ_E_INVALID_ARG;   // destroyed already, or never issued
@@ -450,6 +493,8 @@ const char* gptq_status_str(gptq_status s) {
     case GPTQ_E_WORKSPACE: return "workspace too small or misaligned";
     case GPTQ_E_NUMERIC: return "the damped Hessian is not positive definite";
     case GPTQ_E_DEVICE: return "no gfx950 device, or handle used on another device";
+    case GPTQ_E_SCRATCH_LIMIT:
+      return "the call needs more scratch than gptq_gemm_noalloc's static buffer holds (use gptq_gemm with a workspace)";
   }
   return "unknown status";
 }
