@@ -230,6 +230,15 @@ gptq_status gptq_info(gptq_handle_t h, gptq_handle_info* info);
 gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t* zeros_gn_host,
                                 uint32_t* scales_gn_host, int32_t* perm_host);
 
+/* Device read floor: reads `bytes` of device memory at p once and discards them (sink, 4 bytes of
+ * device memory, is written only for a value the data cannot produce).  "Formats and kernels: FP8,
+ * INT8, INT4, Marlin, Machete", opening section, prices a small-M call of a weight-only layer by the
+ * time to stream its packed weight bytes; this is that stream alone, for timing a layer's call
+ * against the device's own read rate at the same byte count.  p 16-byte aligned, bytes a positive
+ * multiple of 16 (at most 2^40), queued on `stream`, no synchronisation.
+ * Errors: GPTQ_E_INVALID_ARG, GPTQ_E_HIP. */
+gptq_status gptq_read_floor(const void* p, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static message for a status code, naming the rule of "GPTQ packed checkpoint (safetensors /
  * torch)", section "Reject the file when", where a status stands for one (GPTQ-001 .. GPTQ-005).
  * Unknown codes give "unknown status".  Never NULL; the string is owned by the library. */

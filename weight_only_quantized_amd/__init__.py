@@ -29,7 +29,7 @@ PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 symbols = ["gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_gemm_noalloc",
            "gptq_destroy",
            "gptq_info", "gptq_decode_runtime", "gptq_status_str", "gptq_last_hip_error", "gptq_hessian",
-           "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack"]
+           "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack", "gptq_read_floor"]
 
 
 class GPTQError(RuntimeError):
@@ -96,10 +96,11 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_quantize_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
     lib.gptq_quantize.argtypes = [P, P, I32, I32, ctypes.POINTER(QuantParams), P, P, P, P, P, SZ, P]
     lib.gptq_pack.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]
+    lib.gptq_read_floor.argtypes = [P, SZ, P, P]
     for f in ("gptq_validate", "gptq_repack", "gptq_workspace_size", "gptq_gemm", "gptq_gemm_bias", "gptq_gemm_noalloc",
               "gptq_destroy",
               "gptq_info", "gptq_decode_runtime", "gptq_last_hip_error", "gptq_hessian",
-              "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack"):
+              "gptq_quantize_workspace_size", "gptq_quantize", "gptq_pack", "gptq_read_floor"):
         getattr(lib, f).restype = I32
     _lib = lib
     return lib

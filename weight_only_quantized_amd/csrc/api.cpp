@@ -481,6 +481,14 @@ gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t
   return GPTQ_OK;
 }
 
+gptq_status gptq_read_floor(const void* p, size_t bytes, uint32_t* sink, void* stream) {
+  if (!p || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(p, 16) || !aligned(sink, 4) ||
+      bytes / 16 > (size_t(1) << 36))
+    return GPTQ_E_INVALID_ARG;
+  hipError_t e = launch_read_floor(p, bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : hip_fail(e);
+}
+
 const char* gptq_status_str(gptq_status s) {
   switch (s) {
     case GPTQ_OK: return "ok";

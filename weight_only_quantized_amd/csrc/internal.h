@@ -80,6 +80,9 @@ size_t ws_tiled_part_bytes(const gptq_layer* L, int64_t M);
 hipError_t launch_part_reduce(const float* part, uint16_t* y, int64_t rows, int N, int KS, const void* bias,
                               int bias_kind, int x_bf16, hipStream_t s);
 
+// The device read floor (read_floor.hip): reads `bytes` at p once.
+hipError_t launch_read_floor(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // Family launchers.  All assume the call was validated.
 hipError_t launch_skinny(const GemmCall& c);
 hipError_t launch_mid(const GemmCall& c);
