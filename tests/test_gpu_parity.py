@@ -106,10 +106,10 @@ DISPATCH_MS = [1, 2, 3, 4, 5, 16, 17, 33, 64, 130, 257]
                                                 (14304, 2, -1, False, "bf16"), (14336, 4, 128, True, "f16"),
                                                 (12288, 8, 256, False, "bf16"), (10240, 4, 64, False, "f16")])
 def test_long_rows_at_one_row(K, bits, gs, desc, xdt):
-    """M = 1 on 10240 / 12288 / 14336-input layers: x staged in LDS with five to seven waves of 16
+    """M = 1 on 10240 / 12288 / 14336-input layers: x staged in LDS by ten to fourteen waves of 8
     chunks per column tile (whole-chunk groups, no act-order; 14304 inputs end in a partial chunk);
-    M = 2 .. 12: the same waves with x read from L2; act-order and 64-input groups take the mid
-    kernel, M = 16 here the tiled family."""
+    M = 2 .. 12: five to seven waves of 16 chunks with x read from L2; act-order and 64-input
+    groups take the mid kernel, M = 16 here the tiled family."""
     import weight_only_quantized_amd as wq
     N = 160
     say("long-rows", K, bits, gs, desc, xdt)
@@ -120,6 +120,33 @@ def test_long_rows_at_one_row(K, bits, gs, desc, xdt):
     for M in (1, 2, 3, 5, 12, 16):
         for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
             check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=(K, bits, gs, desc, xdt, M, p))
+    h.close()
+
+
+# K values of the M = 1 rule (waves of 4 chunks up to 32 chunks, of 8 above, as many waves as K
+# needs): whole waves (9216: 72 chunks, 9 waves; 16384: 128 chunks, 16 waves), a last wave with
+# padding chunks (11008: 86 chunks, 11 waves, 2 padding; 1152: 9 chunks, 3 waves, 3 padding; 16256:
+# 127 chunks, 16 waves, 1 padding), a single wave (128 and 384 inputs), ragged K inside the last
+# chunk (4000, 9024), every width, both activation dtypes, all scale dtypes.
+M1_RULE = [(9216, 4, "bf16", "f16"), (9216, 3, "f16", "bf16"), (11008, 4, "f16", "f16"), (11008, 8, "bf16", "f32"),
+           (11008, 2, "bf16", "bf16"), (1152, 4, "bf16", "f16"), (1152, 8, "f16", "f16"), (16384, 4, "bf16", "bf16"),
+           (16256, 3, "bf16", "f16"), (16256, 8, "f16", "bf16"), (128, 4, "f16", "f16"), (384, 2, "bf16", "f32"),
+           (4000, 4, "bf16", "f16"), (9024, 8, "f16", "f16"), (4096, 4, "f16", "f16"), (8192, 4, "bf16", "f16")]
+
+
+@pytest.mark.parametrize("K,bits,xdt,sdt", M1_RULE)
+def test_m1_rule_any_k(K, bits, xdt, sdt):
+    """M = 1 through the rule's launch-set K split: one column tile per workgroup, ceil(KC / T)
+    waves of T straight-line chunks, padding chunks past the layer; checked against the oracle."""
+    import weight_only_quantized_amd as wq
+    N = 224
+    say("m1-rule", K, bits, xdt, sdt)
+    L = gi.make_layer(K, N, bits, 128, desc_act=False, scales_dtype=sdt, seed=K + 3 * bits)
+    h = repack_layer(L)
+    x = gi.make_x(1, K, xdt, seed=K + 11)
+    y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, sdt, L.g_idx, bits)
+    for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
+        check(run_gemm(h, x, xdt, path=p), xdt, y_ref, label=(K, bits, xdt, sdt, p))
     h.close()
 
 

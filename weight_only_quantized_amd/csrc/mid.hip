@@ -19,7 +19,7 @@ int mid_slice_chunks(const gptq_layer* L, int64_t M) { return mid_plan(L, M).cpw
 
 bool uses_mid(const gptq_layer* L, int64_t M) {
   return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_x_from_l2(L, M) &&
-         !skinny_m1_long(M, L->KC, L->seg_steps, L->has_perm != 0);
+         !skinny_m1_rule(M, L->KC, L->seg_steps, L->has_perm != 0);
 }
 
 size_t ws_mid_part_bytes(const gptq_layer* L, int64_t M) {

@@ -21,9 +21,6 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
-#ifdef GQ_TUNE
-#include <cstdlib>
-#endif
 #include "bufmem.h"
 #include "dequant.h"
 #include "internal.h"
@@ -237,12 +234,6 @@ inline MidPlan mid_plan(const gptq_layer* L, int64_t M) {
   // slices the reduction then adds)
   int cpw = L->seg_steps == 4 ? (p.MT == 1 ? (L->KC > 64 ? 16 : 8) : 8 / (p.MT / 2)) : 4;
   while (cpw > 4 && (int64_t)nbk * ((L->KC + cpw - 1) / cpw) < 2 * 256) cpw /= 2;
-#ifdef GQ_TUNE
-  if (const char* e = getenv("GQ_MIDCPW")) {
-    const int c = atoi(e);
-    if ((c == 4 || c == 8 || c == 16) && (p.MT == 1 || c <= 8) && (p.MT < 4 || c == 4) && L->seg_steps == 4) cpw = c;
-  }
-#endif
   p.cpw = cpw;
   p.KS = (L->KC + cpw - 1) / cpw;
   return p;

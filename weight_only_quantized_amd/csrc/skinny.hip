@@ -16,6 +16,7 @@ hipError_t launch_skinny(const GemmCall& c) {
   a.scale32 = L->scale32;
   a.y = reinterpret_cast<uint16_t*>(c.y);
   a.M = (int)c.M; a.K = L->K; a.Kp = L->Kp; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
+  a.Kx = L->Kp;
   segment_divisor(L, &a.gmagic, &a.gshift);
   a.scale_kind = L->scales_dtype;
   a.bias = c.bias;

@@ -33,10 +33,24 @@ struct SkinnyArgs {
   uint16_t* y;            // [M, N]
   int64_t ld;             // row stride of x in elements
   int M, K, Kp, N, KC, CT, G, scale_kind;
+  int Kx;                 // length of a staged x row in LDS (XLDS = 1): Kp, or the launch's waves
+                          // times their chunks times 128 when the last wave's range runs past Kp
   uint32_t gmagic;        // segment -> group map (segment_divisor): min(segment / d, G - 1)
   int gshift;
   const void* bias;       // [N] in the scales' dtype (scale_kind), or NULL
 };
+
+// Workgroups are handed to the eight XCDs in turn (workgroup i to XCD i mod 8).  This renumbers
+// them so that each XCD takes one contiguous run of workgroup numbers, hence of column tiles and of
+// the tile-major weight bytes: XCD x, holding the workgroups x, x + 8, x + 16, ..., takes the run
+// that starts at x * q + min(x, r) (q, r = nb / 8, nb % 8).  A bijection of [0, nb).  Measured on
+// MI355X for a plain 8 KB-per-wave read of 122 MB: 512-thread workgroups 21.7 us in launch order,
+// 19.4 us renumbered (256-thread workgroups: 19.2 us in launch order).
+__device__ __forceinline__ int xcd_contiguous_block() {
+  const int nb = gridDim.x, i = blockIdx.x;
+  const int x = i & 7, l = i >> 3, q = nb >> 3, r = nb & 7;
+  return x * q + (x < r ? x : r) + l;
+}
 
 // Group of segment `si` (a chunk index when segments are chunks, a 32-input step index when they
 // are steps).  Every operand is wave-uniform, so this runs on the scalar unit.
@@ -55,6 +69,10 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // TCH > 0: every wave owns exactly TCH chunks (the dispatcher guarantees KC == KSPLIT * TCH) and
 // its whole K range is emitted as straight-line code, so each chunk waits only for its own loads
 // (a loop back-edge would make the compiler wait for every load in flight).
+// KSPLIT == 0: the number of waves per column tile is the launch's (blockDim.x / 64, at most 16),
+// each owning TCH chunks; chunks past the layer's last (the tail of the last wave) are padding:
+// their weight loads fall outside the tile's buffer resource and read zeros, their x is staged as
+// zeros (the staged row holds Kx inputs), so they add exactly nothing.
 // XLDS == 2: an act-order layer; the workgroup scatters all of x into sorted order in LDS through
 // the inverse permutation, then meets at a barrier.
 // At least two waves per SIMD: the kernel needs about 60-130 VGPRs, and without the hint the
@@ -67,15 +85,18 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // sits in the metadata record and no second load is issued per chunk (2 % on the 8192-input M = 1
 // and M = 4 calls on MI355X).
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH, int ONE = 0,
-          int F32S = 1, int WPE = 2, int NWV0 = 0>
-__global__ void __launch_bounds__(64 * (NWV0 ? NWV0 : (KSPLIT > 4 ? KSPLIT : 4))) __attribute__((amdgpu_waves_per_eu(WPE)))
+          int F32S = 1, int WPE = 2, int NWV0 = 0, int XMAP = 1>
+__global__ void __launch_bounds__(64 * (NWV0 ? NWV0 : (KSPLIT == 0 ? 16 : (KSPLIT > 4 ? KSPLIT : 4))))
+__attribute__((amdgpu_waves_per_eu(WPE)))
 skinny_kernel(const SkinnyArgs a) {
   static_assert(!ONE || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
                 "the M = 1 form needs whole-chunk segments, per-wave staging and an exact offset operand");
-  constexpr int NWV = NWV0 ? NWV0 : (KSPLIT > 4 ? KSPLIT : 4);  // waves per workgroup
-  static_assert(NWV % KSPLIT == 0, "whole column groups per workgroup");
+  constexpr bool RTK = KSPLIT == 0;             // waves per tile set at launch
+  static_assert(!RTK || (TCH > 0 && TW == 1 && XLDS == 1), "launch-set K split: per-wave ranges");
+  constexpr int NWV = NWV0 ? NWV0 : (RTK ? 16 : (KSPLIT > 4 ? KSPLIT : 4));  // waves per workgroup (at most)
+  static_assert(RTK || NWV % KSPLIT == 0, "whole column groups per workgroup");
   constexpr int NT = 64 * NWV;
-  constexpr int CGS = NWV / KSPLIT;             // column groups per workgroup
+  constexpr int CGS = RTK ? 1 : NWV / KSPLIT;   // column groups per workgroup
   constexpr int NSEG = 4 / SEG;                 // fixup segments per chunk
   constexpr int PARTS = BITS == 8 ? 2 : 1;      // loads per lane per unit
   constexpr int PW = BITS == 8 ? 4 : BITS;      // words per load
@@ -87,13 +108,14 @@ skinny_kernel(const SkinnyArgs a) {
   // Chunk and tile bookkeeping is wave-uniform (scalar registers).
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int cg = wave / KSPLIT, ks = wave % KSPLIT;
-  const int ct0 = (blockIdx.x * CGS + cg) * TW;
-  const int cpw = (a.KC + KSPLIT - 1) / KSPLIT;
+  const int cg = RTK ? 0 : wave / KSPLIT, ks = RTK ? wave : wave % KSPLIT;
+  const int nks = RTK ? (int)(blockDim.x >> 6) : KSPLIT;   // waves sharing the tile
+  const int ct0 = ((XMAP ? xcd_contiguous_block() : (int)blockIdx.x) * CGS + cg) * TW;
+  const int cpw = RTK ? TCH : (a.KC + KSPLIT - 1) / KSPLIT;
   const int kc0 = ks * cpw;
   const int kc1 = min(a.KC, kc0 + cpw);
   const int col = lane & 15, q = lane >> 4;
-  const int xrow = a.Kp + 8;                    // LDS row stride (halves)
+  const int xrow = a.Kx + 8;                    // LDS row stride (halves)
 
   f32x4 acc[MT][TW];
 #pragma unroll
@@ -366,7 +388,7 @@ skinny_kernel(const SkinnyArgs a) {
   }
 
   // ---- reduce the KSPLIT partial sums of each column group, then store ---------------------
-  if constexpr (KSPLIT > 1) {
+  if constexpr (RTK || KSPLIT > 1) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -375,14 +397,19 @@ skinny_kernel(const SkinnyArgs a) {
         for (int r = 0; r < NR; ++r) red[wave][(m * TW + i) * NR + r][lane] = acc[m][i][r];
     __syncthreads();
     if (ks != 0) return;
+    // unrolled to the workgroup's largest wave count, slots of absent waves masked, so that every
+    // LDS read is issued before the first add (a loop bounded at run time waited for each in turn)
 #pragma unroll
-    for (int w2 = 1; w2 < KSPLIT; ++w2)
+    for (int w2 = 1; w2 < (RTK ? NWV : KSPLIT); ++w2)
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < TW; ++i)
 #pragma unroll
-          for (int r = 0; r < NR; ++r) acc[m][i][r] += red[wave + w2][(m * TW + i) * NR + r][lane];
+          for (int r = 0; r < NR; ++r) {
+            const float v = red[wave + w2][(m * TW + i) * NR + r][lane];
+            acc[m][i][r] += (!RTK || w2 < nks) ? v : 0.f;
+          }
   }
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
@@ -412,14 +439,22 @@ inline bool x_fits_lds(int64_t M, int Kp) {
          (M + 1) * 16 * ((Kp / 128 + 3) / 4) <= 512;
 }
 
-// M = 1 on a long layer without act-order (10240, 12288 or 14336 inputs, whole-chunk groups): x is
-// staged in LDS as for short layers, and the workgroup takes one column tile with KC / 16 waves of
-// 16 chunks each (five to seven waves), the same per-wave work as the 4096-input M = 1 call.  The
-// staged row, its zero row and the waves' partial sums stay under 64 KB of LDS.  Measured on
-// MI355X: 14336 x 4096 at M = 1, 13.4 us with the mid kernel's split K, 8.2 us in this form.
-inline bool skinny_m1_long(int64_t M, int KC, int seg_steps, bool has_perm) {
-  return M == 1 && !has_perm && seg_steps == 4 && (KC == 80 || KC == 96 || KC == 112);
+// M = 1 without act-order, whole-chunk groups, up to 128 chunks (16384 inputs): one column tile per
+// workgroup, whose ceil(KC / T) waves each stage their own T chunks of x in LDS and stream those
+// chunks' weights (T = 4 or 8: every load in flight at once; T = 16: four chunks in flight); the
+// last wave's chunks past the layer are padding (zeros).  A rule, not a table: any K in range takes
+// it.  T = 4 up to 32 chunks, 8 up to 72 chunks or when the chunk count is not a multiple of 16,
+// else 16.  Measured on MI355X (us, interleaved on one device): 4096 x 14336 7.69 -> 7.44 against two
+// waves of 16 chunks; 8192 x 28672 bf16 22.2 -> 20.46 against four waves of 16; T = 8 vs 16:
+// 9216 x 8192 9.38 / 9.71, 11008 x 4096 6.82 / 7.43, 12288 x 8192 10.68 / 11.07 (the one layer the
+// rule gives away), 10240 x 8192 9.90 / 9.32, 14336 x 4096 7.94 / 7.73, 16384 x 8192 15.0 / 13.9;
+// layers between the exact sizes the previous dispatch knew no longer fall to the split-K mid
+// kernel (9216 x 8192: 14.1 -> 9.4; 11008 x 4096: 10.7 -> 6.9).
+constexpr int kM1MaxChunks = 128;
+inline bool skinny_m1_rule(int64_t M, int KC, int seg_steps, bool has_perm) {
+  return M == 1 && !has_perm && seg_steps == 4 && KC <= kM1MaxChunks;
 }
+inline int skinny_m1_chunks(int KC) { return KC <= 32 ? 4 : (KC <= 72 || KC % 16 != 0 ? 8 : 16); }
 // 2 <= M <= 16 on the same layers: the same waves of 16 chunks with x read from L2 per chunk, one
 // column tile per wave below 512 column tiles and two from 512 (enough workgroups either way).
 // Measured on MI355X against the mid kernel / the tiled family (us): 14336 x 4096, M = 2 / 4 / 8 /
@@ -453,19 +488,42 @@ inline bool skinny_reads_x_from_l2(int64_t M, int KC, int CT, int bits, int seg_
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE, int F32S,
           int SEG1 = 1,   // SEG1 = 0: whole-chunk groups only (no 32-input-segment kernel is built)
           int WPE = 2,    // minimum waves per SIMD the register allocation must allow
-          int NWV0 = 0>   // waves per workgroup (0: max(KSPLIT, 4)); a multiple of KSPLIT
+          int NWV0 = 0,   // waves per workgroup (0: max(KSPLIT, 4)); a multiple of KSPLIT
+          int XMAP = 1>   // 1: workgroups renumbered XCD-contiguously (xcd_contiguous_block)
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   constexpr int NWV = NWV0 ? NWV0 : (KSPLIT > 4 ? KSPLIT : 4);
   constexpr int CGS = NWV / KSPLIT;
   const int blocks = (a.CT + TW * CGS - 1) / (TW * CGS);
   // staged rows (+ the per-chunk sums of x of every wave, ONE)
-  const size_t lds = (XLDS ? (size_t)a.M * (a.Kp + 8) * 2 : 0) + (ONE ? (size_t)NWV * TCH * 4 : 0);
+  const size_t lds = (XLDS ? (size_t)a.M * (a.Kx + 8) * 2 : 0) + (ONE ? (size_t)NWV * TCH * 4 : 0);
   if (seg == 4)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S, WPE, NWV0>), dim3(blocks),
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S, WPE, NWV0, XMAP>), dim3(blocks),
                        dim3(64 * NWV), lds, s, a);
   else if constexpr (TCH == 0 && SEG1)
     hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0, 0, F32S>), dim3(blocks),
                        dim3(64 * NWV), lds, s, a);
+  return hipGetLastError();
+}
+
+// The M = 1 rule (skinny_m1_rule): one tile per workgroup, ceil(KC / TCH) waves set at launch, all
+// of a wave's loads in flight (8-bit codes: four chunks, for the registers), bf16 x in the offset
+// form (build_b_offset) for 2/3/4-bit codes.
+// The kernel is built for at most 8 or at most 16 waves (the smaller build has half the reduction
+// slots: measured on MI355X, the 16-wave build took 4 % longer on the 8-wave 4096 x 14336 call).
+template <int BITS, int XT, int TCH, int F32S>
+static hipError_t run_m1(const SkinnyArgs& a0, hipStream_t s) {
+  constexpr int ONE = XT == 1 && BITS <= 4;
+  constexpr int DEPTH = TCH == 16 || (BITS == 8 && TCH > 4) ? 4 : TCH;
+  SkinnyArgs a = a0;
+  const int waves = (a.KC + TCH - 1) / TCH;
+  a.Kx = waves * TCH * kChunkK;
+  const size_t lds = (size_t)(a.Kx + 8) * 2 + (ONE ? (size_t)16 * TCH * 4 : 0);
+  if (waves <= 8)
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, 1, 1, 0, 4, 1, DEPTH, TCH, ONE, F32S, 2, 8>), dim3(a.CT),
+                       dim3(64 * waves), lds, s, a);
+  else
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, 1, 1, 0, 4, 1, DEPTH, TCH, ONE, F32S, 2, 16>), dim3(a.CT),
+                       dim3(64 * waves), lds, s, a);
   return hipGetLastError();
 }
 
@@ -485,34 +543,15 @@ static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
 // column tiles per wave so that x traffic stays near the weight traffic.
 template <int BITS, int XT, int F32S>
 static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
+  if (skinny_m1_rule(a.M, a.KC, seg, a.iperm != nullptr)) {
+    const int t = skinny_m1_chunks(a.KC);
+    if (t == 4) return run_m1<BITS, XT, 4, F32S>(a, s);
+    if (t == 8) return run_m1<BITS, XT, 8, F32S>(a, s);
+    return run_m1<BITS, XT, 16, F32S>(a, s);
+  }
   if (x_fits_lds(a.M, a.Kp)) {
     if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, 4, F32S>(a, seg, s);
-    // M = 1 over 32 chunks: two waves per column tile, each a straight-line 16-chunk range with a
-    // 4-deep ring, measured 3 % faster on MI355X than four waves of 8 chunks (4096-input layers)
-    // the offset operand for bf16 activations (it replaces the bias MFMAs: 4 % on MI355X for the
-    // 8192-input layer); fp16 keeps its exact operands (no gain measured)
-    constexpr int ONE = XT == 1 && BITS <= 4;
-    if (a.M == 1 && seg == 4 && a.KC == 32) return run_tch<BITS, XT, 1, 1, 2, 1, 4, 16, ONE, F32S>(a, seg, s);
-    // 8192 inputs: eight waves of 8 chunks with every load of a wave's range issued at once
-    // (70B gate_proj 28672 x 8192, bf16: 22.2 -> 20.9 us on MI355X against four waves of 16);
-    // wider codes keep four waves of 16 (their 8-deep ring would not fit the registers)
-    if (a.M == 1 && seg == 4 && a.KC == 64) {
-      if constexpr (BITS == 4) return run_tch<BITS, XT, 1, 1, 8, 1, 8, 8, ONE, F32S>(a, seg, s);
-      else return run_tch<BITS, XT, 1, 1, 4, 1, 4, 16, ONE, F32S>(a, seg, s);
-    }
-    // 5120 / 6144 / 7168 inputs: five to seven waves of 8 straight-line chunks (the four-wave
-    // split would leave a loop of 10 to 14 chunks per wave)
-    if (a.M == 1 && seg == 4 && a.KC == 24) return run_tch<BITS, XT, 1, 1, 6, 1, 2, 4, ONE, F32S, 0>(a, seg, s);
-    if (a.M == 1 && seg == 4 && a.KC == 40) return run_tch<BITS, XT, 1, 1, 5, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
-    if (a.M == 1 && seg == 4 && a.KC == 48) return run_tch<BITS, XT, 1, 1, 6, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
-    if (a.M == 1 && seg == 4 && a.KC == 56) return run_tch<BITS, XT, 1, 1, 7, 1, 2, 8, ONE, F32S, 0>(a, seg, s);
     return run<BITS, XT, 1, 1, 4, 1, 4, F32S>(a, seg, s);
-  }
-  if (skinny_m1_long(a.M, a.KC, seg, a.iperm != nullptr)) {
-    constexpr int ONE = XT == 1 && BITS <= 4;
-    if (a.KC == 80) return run_tch<BITS, XT, 1, 1, 5, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
-    if (a.KC == 96) return run_tch<BITS, XT, 1, 1, 6, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
-    return run_tch<BITS, XT, 1, 1, 7, 1, 4, 16, ONE, F32S, 0>(a, seg, s);
   }
   if (skinny_mx_long(a.M, a.KC, a.CT, seg, a.iperm != nullptr)) {
     if (a.KC < 64) {     // 40 / 48 / 56 chunks: five to seven waves of 8

@@ -35,11 +35,6 @@
 //     order with the bias and rounds once (deterministic, no atomics, no counters to clear).
 #include <hip/hip_runtime.h>
 
-#ifdef GQ_TUNE
-#include <cstdio>
-#include <cstdlib>
-#endif
-
 #include "bufmem.h"
 #include "dequant.h"
 #include "internal.h"
@@ -595,15 +590,6 @@ static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
   if (p.tile == 5 && M > 64) p.KS = t >= 192 ? 1 : 2;
   else if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
   else if (t < 150) p.KS = ceil_div(224, t);
-#ifdef GQ_TUNE
-  if (const char* e = getenv("GQ_TILED")) {
-    int tt = p.tile, ks = 1;
-    if (sscanf(e, "%d:%d", &tt, &ks) == 2 && tt >= 0 && tt < kNumTiles && ks >= 1 && (L->seg_steps == 4 || tt == 1)) {
-      p.tile = tt;
-      p.KS = ks;
-    }
-  }
-#endif
   // one row slice of launch_tiled (x and y offsets below 2^31) must hold all M rows
   const int64_t row_slice = ((int64_t(1) << 31) - 1) / (2 * (int64_t)(L->Kp > L->N ? L->Kp : L->N)) / 256 * 256;
   if (p.KS > 1 && (M * (int64_t)L->N * 4 > (int64_t)INT32_MAX || M > row_slice)) p.KS = 1;
