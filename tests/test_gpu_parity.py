@@ -12,7 +12,7 @@ import pytest
 
 import oracle as o
 import gptq_inputs as gi
-from gpu_util import TOL, bits_to_device, check, device_to_bits, repack_layer, run_gemm
+from gpu_util import TOL, bits_to_device, check, device_to_bits, repack_layer, run_gemm, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -132,21 +132,27 @@ M1_RULE = [(9216, 4, "bf16", "f16"), (9216, 3, "f16", "bf16"), (11008, 4, "f16",
            (11008, 2, "bf16", "bf16"), (1152, 4, "bf16", "f16"), (1152, 8, "f16", "f16"), (16384, 4, "bf16", "bf16"),
            (16256, 3, "bf16", "f16"), (16256, 8, "f16", "bf16"), (128, 4, "f16", "f16"), (384, 2, "bf16", "f32"),
            (4000, 4, "bf16", "f16"), (9024, 8, "f16", "f16"), (4096, 4, "f16", "f16"), (8192, 4, "bf16", "f16")]
+# act-order layers at the same K values (x scattered into sorted order in LDS, or a sorted copy of
+# x past 8192 inputs)
+M1_RULE_ACT = [(8192, 2, "f16", "f16"), (8192, 4, "bf16", "f16"), (8192, 8, "f16", "bf16"), (11008, 3, "bf16", "f16"),
+               (16384, 4, "f16", "f32"), (1152, 4, "bf16", "bf16"), (4000, 8, "bf16", "f16"), (4096, 4, "f16", "f16")]
 
 
-@pytest.mark.parametrize("K,bits,xdt,sdt", M1_RULE)
-def test_m1_rule_any_k(K, bits, xdt, sdt):
+@pytest.mark.parametrize("K,bits,xdt,sdt,desc", [c + (False,) for c in M1_RULE] + [c + (True,) for c in M1_RULE_ACT])
+def test_m1_rule_any_k(K, bits, xdt, sdt, desc):
     """M = 1 through the rule's launch-set K split: one column tile per workgroup, ceil(KC / T)
-    waves of T straight-line chunks, padding chunks past the layer; checked against the oracle."""
+    waves of T straight-line chunks, padding chunks past the layer (act-order layers: the same K
+    values on their own path); checked against the oracle."""
     import weight_only_quantized_amd as wq
     N = 224
-    say("m1-rule", K, bits, xdt, sdt)
-    L = gi.make_layer(K, N, bits, 128, desc_act=False, scales_dtype=sdt, seed=K + 3 * bits)
+    say("m1-rule", K, bits, xdt, sdt, desc)
+    L = gi.make_layer(K, N, bits, 128, desc_act=desc, scales_dtype=sdt, seed=K + 3 * bits)
     h = repack_layer(L)
     x = gi.make_x(1, K, xdt, seed=K + 11)
     y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, sdt, L.g_idx, bits)
     for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
-        check(run_gemm(h, x, xdt, path=p), xdt, y_ref, label=(K, bits, xdt, sdt, p))
+        check(run_gemm(h, x, xdt, path=p), xdt, y_ref, label=(K, bits, xdt, sdt, desc, p))
+    assert h.info()["has_perm"] == int(desc)
     h.close()
 
 

@@ -48,7 +48,13 @@ __device__ __forceinline__ int mid_segment_group(int si, uint32_t gmagic, int gs
 }
 
 // F32S: float32 scales in a parallel array (one more load per chunk); otherwise none is issued.
-template <int BITS, int XT, int MT, int WN, int NW, int SEG, int DEPTH, int TCH, int F32S>
+// XMAP: 0 = workgroups in launch order; 1 / 2 = renumbered so that each XCD (workgroup i runs on
+// XCD i mod 8) takes one contiguous run of (column block, slice) pairs, column-block-major (1: an
+// XCD walks the slices of consecutive column blocks, i.e. contiguous weight bytes) or slice-major
+// (2: an XCD walks the column blocks of one slice, sharing its x slice in L2).  Measured on MI355X
+// (8192 x 28672 bf16, 8-chunk slices, with the reduction; us): M = 8 30.9 / 31.1 / 30.4, M = 16
+// 33.4 / 32.5 / 32.6; deeper weight rings (4, 8 chunks) 1-3 us slower in every numbering.
+template <int BITS, int XT, int MT, int WN, int NW, int SEG, int DEPTH, int TCH, int F32S, int XMAP = 2>
 __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   constexpr int BMR = 16 * MT;                  // rows held in LDS (rows >= M are zero)
   constexpr int NSEG = 4 / SEG;
@@ -61,7 +67,15 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, q = lane >> 4;
-  const int nb = blockIdx.x, ks = blockIdx.y;
+  int nb = blockIdx.x, ks = blockIdx.y;
+  if constexpr (XMAP != 0) {
+    const int nbx = gridDim.x, nks = gridDim.y, total = nbx * nks;
+    const int lin = blockIdx.x + blockIdx.y * nbx;
+    const int x = lin & 7, l = lin >> 3, q = total >> 3, r = total & 7;
+    const int id = x * q + (x < r ? x : r) + l;
+    if constexpr (XMAP == 1) { nb = id / nks; ks = id - nb * nks; }
+    else { ks = id / nbx; nb = id - ks * nbx; }
+  }
   const int k0 = ks * TCH;
   const int ct0 = nb * (NW * WN) + wave * WN;
 
@@ -178,13 +192,13 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   };
 
   // ---- chunk c from ring slot c % DEPTH, then refill it with chunk c + DEPTH ---------------
-  // (a loop of ring-sized steps; every refill is unconditional, the last ones fetch the clamped
-  // chunk again and go unused)
+  // (straight-line: the refills past the slice are left out at compile time)
+#pragma unroll
   for (int base = 0; base < TCH; base += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       compute(base + d, ring[d]);
-      load_w(min(k0 + base + d + DEPTH, a.KC - 1), ring[d]);
+      if (base + d + DEPTH < TCH) load_w(min(k0 + base + d + DEPTH, a.KC - 1), ring[d]);
     }
   }
 
