@@ -89,3 +89,38 @@ def check(y_bits, x_tag, y_ref, label=""):
         print(f"half-ulp bar used: {label} ({int(np.count_nonzero(wide & (err > bar)))} outputs past "
               f"2e-2 rms, {int(np.count_nonzero(wide))} where half an ulp exceeds it)", flush=True)
     return m
+
+
+def check_runtime_perm(perm, g_idx, group_size):
+    """The decoded load-time order against what the sort by g_idx fixes: a permutation of the inputs
+    under which every group is contiguous, groups ascending (oracle runtime_perm gives one such
+    order, the stable one).  The order within a group is free (a group shares one scale and one zero
+    per output).  The library keeps the stable order except for act-order layers that the skinny
+    kernel stages whole in LDS (padded K <= 8192, every group a multiple of 128 inputs): there the
+    inputs 512 b + 8 L + e (lanes L = 0..63 of one 2-byte LDS write instruction) must land on 64
+    distinct LDS banks (4-byte words mod 64), and on 32 distinct banks mod 32 within each half-wave.
+    Checked from the decoded order alone."""
+    g = np.asarray(g_idx, dtype=np.int64)
+    K = g.shape[0]
+    perm = np.asarray(perm, dtype=np.int64)
+    stable = o.runtime_perm(g)
+    assert np.array_equal(np.sort(perm), np.arange(K)), "not a permutation"
+    assert np.array_equal(g[perm], g[stable]), "groups not contiguous in ascending order"
+    gse = K if group_size == -1 else group_size
+    Kp = -(-K // 128) * 128
+    spread = not np.array_equal(stable, np.arange(K)) and Kp <= 8192 and K % 128 == 0 and gse % 128 == 0
+    if not spread:
+        assert np.array_equal(perm, stable)
+        return
+    pos = np.empty(K, np.int64)
+    pos[perm] = np.arange(K)
+    lanes = np.arange(64)
+    for blk in range(-(-K // 512)):
+        for e in range(8):
+            ks = blk * 512 + lanes * 8 + e
+            real = ks < K
+            banks = (pos[ks[real]] >> 1) & 63
+            assert len(np.unique(banks)) == banks.size, (blk, e)
+            for half in (0, 1):
+                b = banks[(lanes[real] >> 5) == half] & 31
+                assert len(np.unique(b)) == b.size, (blk, e, half)

@@ -152,3 +152,26 @@ def test_bias_patterns_are_the_stated_values():
         assert np.uint16(0x6400 + v).view(np.float16) == 1024 + v          # fp16 magic: 0x64vv
     for v in range(0, 128):
         assert np.float32(np.uint32((0x4300 + v) << 16).view(np.float32)) == 128 + v   # bf16 magic: 0x43vv
+
+
+def test_runtime_perm_checker_rejects_wrong_orders():
+    """The GPU tests' check of the decoded load-time order (gpu_util.check_runtime_perm) fails a
+    permutation that breaks a group, and, for an act-order layer staged whole in LDS, the stable
+    order (whose scatter instructions hit repeated banks); it passes the stable order where the
+    library keeps it."""
+    import numpy as np
+    import oracle as o
+    from gpu_util import check_runtime_perm
+    rng = np.random.default_rng(5)
+    K, gs = 1024, 128
+    g = np.empty(K, np.int64)
+    g[rng.permutation(K)] = np.arange(K) // gs
+    stable = o.runtime_perm(g)
+    with pytest.raises(AssertionError):
+        check_runtime_perm(stable, g, gs)          # the staged act-order layer must spread banks
+    broken = stable.copy()
+    broken[[0, gs]] = broken[[gs, 0]]              # two inputs of different groups swapped
+    with pytest.raises(AssertionError):
+        check_runtime_perm(broken, g, 32)
+    check_runtime_perm(stable, g, 32)              # 32-input groups keep the stable order
+    check_runtime_perm(np.arange(K), np.arange(K) // gs, gs)   # identity order

@@ -12,7 +12,7 @@ import pytest
 
 import oracle as o
 import gptq_inputs as gi
-from gpu_util import bits_to_device, check, run_gemm
+from gpu_util import bits_to_device, check, check_runtime_perm, run_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,7 @@ def test_repack_decodes_to_the_formats_codes_and_zeros(fmt, bits, gs, desc, sdt)
     assert np.array_equal(d["zeros"], zeros.astype(np.int32))
     want_sc = L.scales.view(np.uint32) if sdt == "f32" else L.scales.astype(np.uint32)
     assert np.array_equal(d["scales"], want_sc)
-    assert np.array_equal(d["perm"], o.runtime_perm(L.g_idx))
+    check_runtime_perm(d["perm"], L.g_idx, gs)
     assert h.info()["bits"] == bits
     h.close()
 

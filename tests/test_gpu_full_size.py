@@ -9,7 +9,7 @@ import pytest
 
 import oracle as o
 import gptq_inputs as gi
-from gpu_util import check, repack_layer, run_gemm
+from gpu_util import check, check_runtime_perm, repack_layer, run_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _decode_check(h, L, cols):
     assert np.array_equal(d["codes"][:, cols], o.unpack_codes(L.qweight[:, cols], L.bits))
     assert np.array_equal(d["zeros"], o.unpack_zeros(L.qzeros, L.bits))
     assert np.array_equal(d["scales"], L.scales.astype(np.uint32))
-    assert np.array_equal(d["perm"], o.runtime_perm(L.g_idx))
+    check_runtime_perm(d["perm"], L.g_idx, L.group_size)
 
 
 def _workload(i):

@@ -12,7 +12,7 @@ import pytest
 
 import oracle as o
 import gptq_inputs as gi
-from gpu_util import TOL, bits_to_device, check, device_to_bits, repack_layer, run_gemm, torch_dtype
+from gpu_util import TOL, bits_to_device, check, check_runtime_perm, device_to_bits, repack_layer, run_gemm, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_repack_decodes_to_oracle_unpack(K, N, bits, gs, desc, sdt):
     assert np.array_equal(d["zeros"], o.unpack_zeros(L.qzeros, bits))
     want_sc = L.scales.view(np.uint32) if sdt == "f32" else L.scales.astype(np.uint32)
     assert np.array_equal(d["scales"], want_sc)
-    assert np.array_equal(d["perm"], o.runtime_perm(L.g_idx))
+    check_runtime_perm(d["perm"], L.g_idx, gs)
     assert h.info()["has_perm"] == int(not np.array_equal(o.runtime_perm(L.g_idx), np.arange(K)))
     h.close()
 
@@ -134,8 +134,13 @@ M1_RULE = [(9216, 4, "bf16", "f16"), (9216, 3, "f16", "bf16"), (11008, 4, "f16",
            (4000, 4, "bf16", "f16"), (9024, 8, "f16", "f16"), (4096, 4, "f16", "f16"), (8192, 4, "bf16", "f16")]
 # act-order layers at the same K values (x scattered into sorted order in LDS, or a sorted copy of
 # x past 8192 inputs)
+# act-order at M = 1: the staged form up to 8192 inputs (T = 4 up to 32 chunks, else 16 at 4-bit
+# and 8 otherwise; padding chunks at 7936 / 8064 / 1152 / 6144; K = 4000 keeps the stable order),
+# the mid kernel beyond
 M1_RULE_ACT = [(8192, 2, "f16", "f16"), (8192, 4, "bf16", "f16"), (8192, 8, "f16", "bf16"), (11008, 3, "bf16", "f16"),
-               (16384, 4, "f16", "f32"), (1152, 4, "bf16", "bf16"), (4000, 8, "bf16", "f16"), (4096, 4, "f16", "f16")]
+               (16384, 4, "f16", "f32"), (1152, 4, "bf16", "bf16"), (4000, 8, "bf16", "f16"), (4096, 4, "f16", "f16"),
+               (8192, 3, "bf16", "f32"), (6144, 3, "f16", "f32"), (8064, 2, "bf16", "f16"), (7936, 4, "f16", "bf16"),
+               (256, 8, "f16", "f16"), (2048, 2, "f16", "f16"), (7936, 8, "bf16", "f16")]
 
 
 @pytest.mark.parametrize("K,bits,xdt,sdt,desc", [c + (False,) for c in M1_RULE] + [c + (True,) for c in M1_RULE_ACT])
@@ -153,6 +158,8 @@ def test_m1_rule_any_k(K, bits, xdt, sdt, desc):
     for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
         check(run_gemm(h, x, xdt, path=p), xdt, y_ref, label=(K, bits, xdt, sdt, desc, p))
     assert h.info()["has_perm"] == int(desc)
+    if desc:
+        check_runtime_perm(h.decode()["perm"], L.g_idx, 128)
     h.close()
 
 

@@ -50,6 +50,7 @@ namespace gq {
 constexpr int kChunkK = 128;   // sorted-K chunk of one unit
 constexpr int kTileN = 16;     // columns per tile
 constexpr int kLanes = 64;
+constexpr int kIpermMaxKp = 8192;   // 16-bit inverse permutation kept up to this padded K
 
 GQ_HD int words_per_lane(int bits) { return bits; }
 GQ_HD int64_t unit_words(int bits) { return (int64_t)kLanes * bits; }

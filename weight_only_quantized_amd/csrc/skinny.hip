@@ -5,7 +5,9 @@
 
 namespace gq {
 
-bool skinny_needs_xsorted(const gptq_layer* L, int64_t M) { return L->has_perm && !x_fits_lds(M, L->Kp); }
+bool skinny_needs_xsorted(const gptq_layer* L, int64_t M) {
+  return L->has_perm && (!x_fits_lds(M, L->Kp) || !L->iperm);
+}
 
 hipError_t launch_skinny(const GemmCall& c) {
   const gptq_layer* L = c.L;

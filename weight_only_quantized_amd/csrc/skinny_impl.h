@@ -29,7 +29,7 @@ struct SkinnyArgs {
   const uint32_t* meta;   // per (tile, group, column): scale bits | stored zero << 16
   const uint32_t* scale32;  // f32 scale bits (scale_kind == 2 only)
   const uint16_t* x;      // [M, ld] activations (original order when perm is set, else sorted)
-  const int32_t* iperm;   // input index -> sorted position, or NULL (identity); LDS staging only
+  const uint16_t* iperm;  // input index -> sorted position (16-bit), or NULL (identity); LDS staging only
   uint16_t* y;            // [M, N]
   int64_t ld;             // row stride of x in elements
   int M, K, Kp, N, KC, CT, G, scale_kind;
@@ -74,7 +74,8 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // their weight loads fall outside the tile's buffer resource and read zeros, their x is staged as
 // zeros (the staged row holds Kx inputs), so they add exactly nothing.
 // XLDS == 2: an act-order layer; the workgroup scatters all of x into sorted order in LDS through
-// the inverse permutation, then meets at a barrier.
+// the 16-bit inverse permutation, then meets at a barrier (with KSPLIT == 0, M = 1 only: each
+// thread then holds TCH / 4 pieces of the padded row).
 // At least two waves per SIMD: the kernel needs about 60-130 VGPRs, and without the hint the
 // compiler spreads a one-wave-per-SIMD schedule over all 512, so a compute unit held one workgroup.
 // ONE (M = 1, whole-chunk segments, x staged per wave, straight-line ranges): the B operand is
@@ -92,7 +93,7 @@ skinny_kernel(const SkinnyArgs a) {
   static_assert(!ONE || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
                 "the M = 1 form needs whole-chunk segments, per-wave staging and an exact offset operand");
   constexpr bool RTK = KSPLIT == 0;             // waves per tile set at launch
-  static_assert(!RTK || (TCH > 0 && TW == 1 && XLDS == 1), "launch-set K split: per-wave ranges");
+  static_assert(!RTK || (TCH >= 4 && XLDS != 0), "launch-set K split: per-wave ranges, staged x");
   constexpr int NWV = NWV0 ? NWV0 : (RTK ? 16 : (KSPLIT > 4 ? KSPLIT : 4));  // waves per workgroup (at most)
   static_assert(RTK || NWV % KSPLIT == 0, "whole column groups per workgroup");
   constexpr int NT = 64 * NWV;
@@ -245,11 +246,13 @@ skinny_kernel(const SkinnyArgs a) {
   // x staging loads go out before the weight ring (loads complete in issue order).  Act-order
   // layers scatter x into sorted order in LDS through the inverse permutation: both global reads
   // stay coalesced and independent, and the scatter is eight 2-byte LDS writes per piece.
-  constexpr int XPT = 4 * 256 / NT;               // 16-byte x pieces per thread held in registers
+  // (the launch-set form holds one row of Kx = waves * TCH * 128 inputs over 64 * waves threads)
+  constexpr int XPT = RTK ? TCH / 4 : 4 * 256 / NT;   // 16-byte x pieces per thread held in registers
   constexpr bool PERMUTE = XLDS == 2;
+  const int nthr = RTK ? (int)blockDim.x : NT;
   u32x4 xreg[PERMUTE ? XPT : 1];
-  u32x4 ipreg[PERMUTE ? XPT : 1][2];
-  const int per_row = a.Kp / 8;
+  u32x4 ipreg[PERMUTE ? XPT : 1];                 // eight 16-bit sorted positions per piece
+  const int per_row = a.Kx / 8;
   const int n8 = XLDS ? a.M * per_row : 0;        // 16-byte pieces of x (original order if iperm)
   // Without act-order each wave stages only the inputs of its own K range (rows 0..M-1), so no wave
   // waits for another before its first chunk.  x_fits_lds bounds a wave's M * wpr row pieces by
@@ -270,17 +273,14 @@ skinny_kernel(const SkinnyArgs a) {
     }
   }
   if constexpr (XLDS == 2) {
+    const rsrc_t rip = make_rsrc(a.iperm, (uint32_t)a.K * 2u);
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
-      const int idx = threadIdx.x + NT * r;
+      const int idx = threadIdx.x + nthr * r;
       const int m = idx / per_row, j0 = (idx % per_row) * 8;
       const bool real = idx < n8 && j0 < a.K;
       xreg[r] = load_b128(rx, real ? (uint32_t)(m * a.ld + j0) * 2u : kOob, 0u);
-      if constexpr (PERMUTE) {
-        const rsrc_t rip = make_rsrc(a.iperm, (uint32_t)a.K * 4u);
-        ipreg[r][0] = load_b128(rip, real ? (uint32_t)j0 * 4u : kOob, 0u);
-        ipreg[r][1] = load_b128(rip, real ? (uint32_t)j0 * 4u + 16u : kOob, 0u);
-      }
+      ipreg[r] = load_b128(rip, real ? (uint32_t)j0 * 2u : kOob, 0u);
     }
   }
   // With TCH > 0 the waves of neighbouring column tiles walk their K ranges from different
@@ -333,21 +333,31 @@ skinny_kernel(const SkinnyArgs a) {
   if constexpr (XLDS == 2) {
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
-      const int idx = threadIdx.x + NT * r;
+      const int idx = threadIdx.x + nthr * r;
       if (idx < n8) {
         const int m = idx / per_row, j0 = (idx % per_row) * 8;
-        if (PERMUTE && j0 < a.K) {
+        if (j0 < a.K) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint16_t h = (uint16_t)(xreg[r][e >> 1] >> (16 * (e & 1)));
-            xlds[m * xrow + (int)ipreg[PERMUTE ? r : 0][e >> 2][e & 3]] = h;
+            const uint32_t sh = 16u * (e & 1);
+            const uint16_t h = (uint16_t)(xreg[r][e >> 1] >> sh);
+            const int pos = (int)((ipreg[r][e >> 1] >> sh) & 0xFFFFu);
+            xlds[m * xrow + pos] = h;
           }
         } else {
-          *reinterpret_cast<u32x4*>(&xlds[m * xrow + j0]) = xreg[r];   // zeros past K
+          *reinterpret_cast<u32x4*>(&xlds[m * xrow + j0]) = xreg[r];   // zeros past K (and padding)
         }
       }
     }
-    __syncthreads();
+    // LDS-only fences around the barrier: the weight loads already in flight are not waited for
+    // (a workgroup fence on all memory would wait for every load of the ring), and no instruction
+    // crosses it (the scheduler would otherwise start the first chunk's dequantisation above it,
+    // which waits for that chunk's weights before the wave reaches the barrier)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- main loop: compute chunk kc from the ring slot, then refill the slot with kc + DEPTH ---
@@ -455,6 +465,19 @@ inline bool skinny_m1_rule(int64_t M, int KC, int seg_steps, bool has_perm) {
   return M == 1 && !has_perm && seg_steps == 4 && KC <= kM1MaxChunks;
 }
 inline int skinny_m1_chunks(int KC) { return KC <= 32 ? 4 : (KC <= 72 || KC % 16 != 0 ? 8 : 16); }
+// M = 1 with act-order, whole-chunk groups and x staged whole (Kp <= 8192): the same launch-set
+// waves, the workgroup scattering x into sorted order through the 16-bit inverse permutation (whose
+// within-group order the repack chose so that each scatter instruction hits distinct LDS banks)
+// and meeting at one barrier; four chunks in flight per wave.  T = 4 up to 32 chunks, else 16 for
+// 4-bit codes and 8 otherwise.  Measured on MI355X, 8192 x 8192, fp16 x, us (the identity-order
+// gs = -1 layer of the same width in parentheses): 2-bit 8.6 -> 7.49 (7.10), 3-bit 9.2 -> 8.13
+// (7.57), 4-bit 8.9 -> 8.34 (8.01), 8-bit 13.2 -> 12.7 (12.2); before, four waves of 16 chunks
+// scattered through a 32-bit inverse permutation in the stable order (about 13 bank-conflict cycles
+// per 2-byte LDS write instruction, rocprofv3 SQ_LDS_BANK_CONFLICT) and met at a barrier that also
+// waited for every weight load in flight.
+inline bool skinny_m1_act_rule(int64_t M, int Kp, int seg_steps, bool has_iperm) {
+  return M == 1 && has_iperm && seg_steps == 4 && Kp <= kIpermMaxKp;
+}
 // 2 <= M <= 16 on the same layers: the same waves of 16 chunks with x read from L2 per chunk, one
 // column tile per wave below 512 column tiles and two from 512 (enough workgroups either way).
 // Measured on MI355X against the mid kernel / the tiled family (us): 14336 x 4096, M = 2 / 4 / 8 /
@@ -527,6 +550,17 @@ static hipError_t run_m1(const SkinnyArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BITS, int XT, int TCH, int F32S>
+static hipError_t run_m1_act(const SkinnyArgs& a0, hipStream_t s) {
+  SkinnyArgs a = a0;
+  const int waves = (a.KC + TCH - 1) / TCH;   // at most 8 (KC <= 64, T = 8 or 16; KC <= 32, T = 4)
+  a.Kx = waves * TCH * kChunkK;
+  const size_t lds = (size_t)(a.Kx + 8) * 2;
+  hipLaunchKernelGGL((skinny_kernel<BITS, XT, 1, 1, 0, 4, 2, 4, TCH, 0, F32S, 2, 8>), dim3(a.CT), dim3(64 * waves),
+                     lds, s, a);
+  return hipGetLastError();
+}
+
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int F32S>
 static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
   // Straight-line variants for the whole-chunk-segment case; ring depths measured best on
@@ -548,6 +582,11 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     if (t == 4) return run_m1<BITS, XT, 4, F32S>(a, s);
     if (t == 8) return run_m1<BITS, XT, 8, F32S>(a, s);
     return run_m1<BITS, XT, 16, F32S>(a, s);
+  }
+  if (skinny_m1_act_rule(a.M, a.Kp, seg, a.iperm != nullptr)) {
+    if (a.KC <= 32) return run_m1_act<BITS, XT, 4, F32S>(a, s);
+    if constexpr (BITS == 4) return run_m1_act<BITS, XT, 16, F32S>(a, s);
+    else return run_m1_act<BITS, XT, 8, F32S>(a, s);
   }
   if (x_fits_lds(a.M, a.Kp)) {
     if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, 4, F32S>(a, seg, s);
