@@ -14,11 +14,12 @@ Timing.  Every timed region starts with a short device-side wait kernel queued a
 calls are already queued when the start event is reached and the region holds device time only
 (not the host's launch latency before the first call).  The headline `value`: W warm-up calls, then
 exactly K calls between two HIP events on the launch stream, with torch.cuda.synchronize() on both
-sides, measured after the other records.  A region still holds one dispatch latency that no earlier
-call overlaps (the start event waits for the wait kernel), so a short region reads a little above
-the batches' steady state.  Every record (the headline's too, in `headline_batches`) also reports the median and the
-10th / 90th percentiles of the per-call time over 7 batches of at least 50 calls (20 for M >= 1024)
-after at least 10 warm-up calls, with its own counts.
+sides, measured after the decode-sized records and before the compute-bound ones.  A region still
+holds one dispatch latency that no earlier call overlaps (the start event waits for the wait
+kernel), so a short region reads a little above the batches' steady state.  Every record (the
+headline's too, in `headline_batches`) also reports the median and the 10th / 90th percentiles of
+the per-call time over 7 batches of at least 50 calls (20 for M >= 1024) after at least 10 warm-up
+calls, with its own counts.
 
 Prints ONE JSON line.  `value` is microseconds per call (lower is better); `roofline` reports the
 dominant kernel's algorithmic bytes per launch / its average launch time against 8 TB/s; `extra`
@@ -441,11 +442,16 @@ def main():
 
     w = HEADLINE
     extra = []
+    light = [e for e in extra_workloads() if e.M < 1024]
+    heavy = [e for e in extra_workloads() if e.M >= 1024]
+
+    def record(rec):
+        extra.append(rec)
+        print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
+
     if not args.no_extra:
-        for e in extra_workloads():
-            rec = layer_record(e, time_layer(e, timer, xw, 50 if e.M < 1024 else 20))
-            extra.append(rec)
-            print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
+        for e in light:
+            record(layer_record(e, time_layer(e, timer, xw, 50)))
         # the device's own read rate at the decode layers' byte counts (rotated buffers)
         for name, fw in (("llama3_8b_up_proj_M1", HEADLINE),
                          ("llama3_70b_gate_proj_M1", Workload("g", 8192, 28672, 1, 4, 128, False, "f16", "bf16", 0))):
@@ -455,8 +461,15 @@ def main():
             rec["TB_per_s"] = round(nb / (rec["us_per_call"] * 1e-6) / 1e12, 3)
             rec["frac_hbm"] = round(rec["TB_per_s"] * 1e3 / HBM_PEAK_GBS, 4)
             rec["note"] = "gptq_read_floor: a plain read of the same byte count, nothing else (context)"
-            extra.append(rec)
-            print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
+            record(rec)
+    # the headline: W warm-up calls, then exactly K timed calls, on a device the decode records above
+    # have brought to its working clocks and before the compute-bound records below (timed after
+    # them, the same call measured 8.2 us, batch median 8.8, against 7.6 - 7.75 us for the same
+    # kernel earlier in that run)
+    head = time_layer(w, timer, args.warmup, max(50, min(args.steps, 500)), steps=args.steps)
+    if not args.no_extra:
+        for e in heavy:
+            record(layer_record(e, time_layer(e, timer, xw, 20)))
         # dense bf16 matmul of the prefill shape (hipBLASLt through torch): context for the MFMA path
         t = time_dense_mm(4096, 8192, 28672, timer, 10, 20)
         fl = 2.0 * 4096 * 8192 * 28672
@@ -464,15 +477,9 @@ def main():
         rec["TFLOP_per_s"] = round(fl / (rec["us_per_call"] * 1e-6) / 1e12, 1)
         rec["frac_mfma_bf16"] = round(rec["TFLOP_per_s"] / BF16_PEAK_TFLOPS, 4)
         rec["note"] = "torch.mm on dense bf16 operands of the prefill shape (context, not this method)"
-        extra.append(rec)
-        print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
+        record(rec)
         # the step before the path: GPTQ on the GPU for the same 4096 x 14336 layer
-        rec = time_quantize(4096, 14336, 512, 4, 128, True)
-        extra.append(rec)
-        print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
-    # the headline last: W warm-up calls, then exactly K timed calls on a device the records above
-    # have already brought to its working clocks
-    head = time_layer(w, timer, args.warmup, max(50, min(args.steps, 500)), steps=args.steps)
+        record(time_quantize(4096, 14336, 512, 4, 128, True))
     us = head["timed_us"]
     abytes = algorithmic_bytes(w.K, w.N, w.M, w.bits, w.gs, w.desc_act)
     achieved = abytes / (us * 1e-6) / 1e9
