@@ -163,6 +163,35 @@ def test_m1_rule_any_k(K, bits, xdt, sdt, desc):
     h.close()
 
 
+# 2 <= M <= 16 through the copy form (x[0:M] copied into LDS once per workgroup, column groups and
+# launch-set waves of T chunks, padding chunks past the layer; bf16 x in the offset form): the
+# shapes pick T = 16 or 32, one or several column groups, one or two workgroups per compute unit,
+# padding (24 and 9 chunks), whole-layer and 256-input groups, every scale dtype, 2/3/4-bit codes
+COPY_FORM = [(8192, 2048, 4, 128, "bf16", "f16", (2, 3, 5, 8)), (8192, 3072, 2, 128, "bf16", "bf16", (4, 7)),
+             (8192, 2048, 3, 256, "bf16", "f32", (2, 6)), (4096, 1024, 4, 128, "f16", "f16", (4, 9, 16)),
+             (4096, 2048, 3, -1, "bf16", "f16", (12, 16)), (14336, 512, 4, 128, "f16", "bf16", (2, 4)),
+             (3072, 512, 4, 128, "f16", "f16", (8, 13)), (1152, 768, 2, 128, "bf16", "f16", (6, 16)),
+             (16384, 512, 4, 128, "bf16", "f16", (3, 4))]
+
+
+@pytest.mark.parametrize("K,N,bits,gs,xdt,sdt,Ms", COPY_FORM)
+def test_copy_form(K, N, bits, gs, xdt, sdt, Ms):
+    """The copy form against the oracle at each M, on PATH_AUTO and PATH_SKINNY, and with a bias."""
+    import weight_only_quantized_amd as wq
+    say("copy-form", K, N, bits, gs, xdt, sdt, Ms)
+    L = gi.make_layer(K, N, bits, gs, desc_act=False, scales_dtype=sdt, seed=K + N + bits)
+    h = repack_layer(L)
+    x = gi.make_x(max(Ms), K, xdt, seed=K + 5)
+    y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, sdt, L.g_idx, bits)
+    bias = gi.make_bias(N, sdt, seed=N + 1)
+    y_ref_b = y_ref + o.decode_float_bits(bias, sdt)[None, :]
+    for M in Ms:
+        for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
+            check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=(K, N, bits, gs, xdt, sdt, M, p))
+        check(run_gemm(h, x[:M], xdt, bias=bias, bias_tag=sdt), xdt, y_ref_b[:M], label=("bias", K, N, M))
+    h.close()
+
+
 @pytest.mark.parametrize("K,bits,xdt", [(10240, 4, "bf16"), (10240, 3, "f16"), (10240, 8, "bf16"),
                                          (5120, 4, "f16"), (7168, 2, "bf16")])
 def test_long_rows_wide_layer(K, bits, xdt):

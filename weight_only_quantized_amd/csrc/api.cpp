@@ -402,7 +402,8 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
 }
 
 // PATH_AUTO: the skinny family (skinny kernel, or the mid kernel's split K) up to 8 rows; from 9
-// to 32 rows the skinny kernel where it reads x from L2 (skinny_reads_x_from_l2), else the tiled
+// to 32 rows the skinny kernel where one of its one-launch forms takes the call (x read from L2,
+// or the workgroup's copy of x in LDS: skinny_one_launch), else the tiled
 // family when its K slices are long (8 chunks or more) while the mid kernel would cut K into more
 // than 4 slices shorter than 16 chunks (of 4 chunks up to 16 rows), else the mid kernel; the tiled
 // family (split K up to ~450 workgroups) above 32 rows.  Measured on MI355X with 4-bit g128 layers, fp16 x, mid vs tiled (two chunks in flight):
@@ -415,7 +416,7 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
 static int32_t auto_path(const gptq_layer* L, int64_t M) {
   if (M <= 8) return GPTQ_PATH_SKINNY;
   if (M <= 32) {
-    if (skinny_x_from_l2(L, M)) return GPTQ_PATH_SKINNY;
+    if (skinny_one_launch(L, M)) return GPTQ_PATH_SKINNY;
     // up to 16 rows only 4-chunk mid slices lose; from 17 rows any shorter than 16 chunks
     const int mid_cpw = mid_slice_chunks(L, M);
     return (tiled_slice_chunks(L, M) >= 8 && mid_slices(L, M) > 4 && (M > 16 ? mid_cpw < 16 : mid_cpw <= 4))

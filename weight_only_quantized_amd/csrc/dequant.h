@@ -142,6 +142,14 @@ __device__ __forceinline__ float scale_of(uint32_t rec, uint32_t s32, int kind) 
   const float f32v = __builtin_bit_cast(float, s32);
   return kind == 0 ? f16v : (kind == 1 ? bf16v : f32v);
 }
+// The same picked through masks (no branch: see group_of_segment_nb), for chunk code with loads in
+// flight.
+__device__ __forceinline__ float scale_of_nb(uint32_t rec, uint32_t s32, int kind) {
+  const uint32_t f16v = __builtin_bit_cast(uint32_t, (float)__builtin_bit_cast(_Float16, (uint16_t)(rec & 0xFFFFu)));
+  const uint32_t bf16v = rec << 16;
+  const uint32_t m1 = 0u - (uint32_t)(kind == 1), m2 = 0u - (uint32_t)(kind == 2);
+  return __builtin_bit_cast(float, (((f16v & ~m1) | (bf16v & m1)) & ~m2) | (s32 & m2));
+}
 // The zero of a metadata record: its high half holds zero - 1 mod 2^16 (layout.h), which is the
 // GPTQ v1 stored field as it is and 0xFFFF for an AWQ zero of 0.
 __device__ __forceinline__ uint32_t zero_of(uint32_t rec) { return ((rec >> 16) + 1u) & 0xFFFFu; }

@@ -62,11 +62,12 @@ bool tiled_needs_xsorted(const gptq_layer* L, int x_bf16);
 // large to gather into LDS).
 bool skinny_needs_xsorted(const gptq_layer* L, int64_t M);
 
-// The SKINNY path (M <= 64) runs the skinny kernel when x fits one workgroup's LDS whole and the
+// The SKINNY path (M <= 64) runs the skinny kernel when one of its forms takes the call and the
 // mid kernel (split K, mid.hip) otherwise; the mid kernel's partial sums need workspace.
 bool uses_mid(const gptq_layer* L, int64_t M);
-// The skinny kernel reads x from L2 for this M (mid.hip; the rule is skinny_impl.h's).
-bool skinny_x_from_l2(const gptq_layer* L, int64_t M);
+// The skinny kernel takes these M > 1 rows in one launch: x read from L2 per chunk, or the
+// workgroup's copy of x in LDS (mid.hip; the rules are skinny_impl.h's).
+bool skinny_one_launch(const gptq_layer* L, int64_t M);
 // K slices the mid kernel would cut a call into (mid.hip), and chunks per K slice of the tiled
 // plan (tiled.hip): the inputs of PATH_AUTO between 17 and 32 rows.
 int mid_slices(const gptq_layer* L, int64_t M);

@@ -97,6 +97,16 @@ GQ_HD int group_of_segment(int si, uint32_t magic, int shift, int G) {
   const int g = shift >= 0 ? (si >> shift) : (int)(((uint64_t)(uint32_t)si * magic) >> 32);
   return g < G - 1 ? g : G - 1;
 }
+// The same with both forms computed and combined through a mask: the select above, on a
+// wave-uniform value, is compiled into a branch, and a branch join inside chunk code that has loads
+// in flight makes the wave wait for all of them.
+GQ_HD int group_of_segment_nb(int si, uint32_t magic, int shift, int G) {
+  const uint32_t by_shift = (uint32_t)si >> (shift & 31);
+  const uint32_t by_magic = (uint32_t)(((uint64_t)(uint32_t)si * magic) >> 32);
+  const uint32_t m = 0u - (uint32_t)(shift >= 0);
+  const int g = (int)((by_shift & m) | (by_magic & ~m));
+  return g < G - 1 ? g : G - 1;
+}
 
 // Sorted-K offset within the chunk, and column within the tile, of lane code i.
 GQ_HD int code_k_in_chunk(int lane, int i) { return 32 * (i >> 3) + 8 * (lane >> 4) + (i & 7); }

@@ -9,16 +9,17 @@ namespace gq {
 
 static inline size_t align256m(size_t b) { return (b + 255) / 256 * 256; }
 
-bool skinny_x_from_l2(const gptq_layer* L, int64_t M) {
+bool skinny_one_launch(const gptq_layer* L, int64_t M) {
   return skinny_reads_x_from_l2(M, L->KC, L->CT, L->bits, L->seg_steps) ||
-         skinny_mx_long(M, L->KC, L->CT, L->seg_steps, L->has_perm != 0);
+         skinny_mx_long(M, L->KC, L->CT, L->seg_steps, L->has_perm != 0) ||
+         skinny_copy_plan(M, L->KC, L->CT, L->bits, L->seg_steps, L->has_perm != 0).ok;
 }
 
 int mid_slices(const gptq_layer* L, int64_t M) { return mid_plan(L, M).KS; }
 int mid_slice_chunks(const gptq_layer* L, int64_t M) { return mid_plan(L, M).cpw; }
 
 bool uses_mid(const gptq_layer* L, int64_t M) {
-  return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_x_from_l2(L, M) &&
+  return M > 0 && !x_fits_lds(M, L->Kp) && !skinny_one_launch(L, M) &&
          !skinny_m1_rule(M, L->KC, L->seg_steps, L->has_perm != 0);
 }
 

@@ -19,6 +19,7 @@ hipError_t launch_skinny(const GemmCall& c) {
   a.y = reinterpret_cast<uint16_t*>(c.y);
   a.M = (int)c.M; a.K = L->K; a.Kp = L->Kp; a.N = L->N; a.KC = L->KC; a.CT = L->CT; a.G = L->G;
   a.Kx = L->Kp;
+  a.cgs = 1;
   segment_divisor(L, &a.gmagic, &a.gshift);
   a.scale_kind = L->scales_dtype;
   a.bias = c.bias;

@@ -33,11 +33,12 @@ struct SkinnyArgs {
   uint16_t* y;            // [M, N]
   int64_t ld;             // row stride of x in elements
   int M, K, Kp, N, KC, CT, G, scale_kind;
-  int Kx;                 // length of a staged x row in LDS (XLDS = 1): Kp, or the launch's waves
-                          // times their chunks times 128 when the last wave's range runs past Kp
+  int Kx;                 // length of a staged x row in LDS: Kp, or the launch's waves per column
+                          // group times their chunks times 128 when the last wave's range runs past Kp
   uint32_t gmagic;        // segment -> group map (segment_divisor): min(segment / d, G - 1)
   int gshift;
   const void* bias;       // [N] in the scales' dtype (scale_kind), or NULL
+  int cgs;                // column groups per workgroup of the copy form (KSPLIT = 0, XLDS = 3)
 };
 
 // Workgroups are handed to the eight XCDs in turn (workgroup i to XCD i mod 8).  This renumbers
@@ -54,8 +55,9 @@ __device__ __forceinline__ int xcd_contiguous_block() {
 
 // Group of segment `si` (a chunk index when segments are chunks, a 32-input step index when they
 // are steps).  Every operand is wave-uniform, so this runs on the scalar unit.
+template <bool NB = false>
 __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift, int G) {
-  return group_of_segment(si, gmagic, gshift, G);
+  return NB ? group_of_segment_nb(si, gmagic, gshift, G) : group_of_segment(si, gmagic, gshift, G);
 }
 
 // XLDS = 1: each wave first copies the part of x[0:M, 0:Kp] that its own K range multiplies into
@@ -73,6 +75,9 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // each owning TCH chunks; chunks past the layer's last (the tail of the last wave) are padding:
 // their weight loads fall outside the tile's buffer resource and read zeros, their x is staged as
 // zeros (the staged row holds Kx inputs), so they add exactly nothing.
+// XLDS == 3: the workgroup copies all of x[0:M, 0:Kp] into LDS rows (1 KB buffer_load ... lds pieces,
+// Kp a multiple of 512) after issuing its weight ring, and every column group's waves read their A
+// operands there: one copy of x per workgroup, shared by its CGS column groups.
 // XLDS == 2: an act-order layer; the workgroup scatters all of x into sorted order in LDS through
 // the 16-bit inverse permutation, then meets at a barrier (with KSPLIT == 0, M = 1 only: each
 // thread then holds TCH / 4 pieces of the padded row).
@@ -86,32 +91,49 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // sits in the metadata record and no second load is issued per chunk (2 % on the 8192-input M = 1
 // and M = 4 calls on MI355X).
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH, int ONE = 0,
-          int F32S = 1, int WPE = 2, int NWV0 = 0, int XMAP = 1>
+          int F32S = 1, int WPE = 2, int NWV0 = 0, int XMAP = 1, int NBS = 0>
 __global__ void __launch_bounds__(64 * (NWV0 ? NWV0 : (KSPLIT == 0 ? 16 : (KSPLIT > 4 ? KSPLIT : 4))))
 __attribute__((amdgpu_waves_per_eu(WPE)))
 skinny_kernel(const SkinnyArgs a) {
-  static_assert(!ONE || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
+  static_assert(ONE != 1 || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
                 "the M = 1 form needs whole-chunk segments, per-wave staging and an exact offset operand");
+  static_assert(ONE != 2 || (MT == 1 && SEG == 4 && XLDS == 3 && TCH > 0 && XT == 1 && BITS <= 4),
+                "the offset form for up to 16 rows needs whole-chunk segments, the workgroup's copy of x and "
+                "an exact bf16 offset operand");
   constexpr bool RTK = KSPLIT == 0;             // waves per tile set at launch
   static_assert(!RTK || (TCH >= 4 && XLDS != 0), "launch-set K split: per-wave ranges, staged x");
   constexpr int NWV = NWV0 ? NWV0 : (RTK ? 16 : (KSPLIT > 4 ? KSPLIT : 4));  // waves per workgroup (at most)
   static_assert(RTK || NWV % KSPLIT == 0, "whole column groups per workgroup");
   constexpr int NT = 64 * NWV;
-  constexpr int CGS = RTK ? 1 : NWV / KSPLIT;   // column groups per workgroup
+  constexpr int CGS = RTK ? 1 : NWV / KSPLIT;   // column groups per workgroup (launch-set form: a.cgs)
   constexpr int NSEG = 4 / SEG;                 // fixup segments per chunk
   constexpr int PARTS = BITS == 8 ? 2 : 1;      // loads per lane per unit
   constexpr int PW = BITS == 8 ? 4 : BITS;      // words per load
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
-  constexpr int NR = ONE ? 1 : 4;                // accumulator registers carried (ONE: output row 0)
+  constexpr int NR = ONE == 1 ? 1 : 4;           // accumulator registers carried (ONE = 1: output row 0)
+  // Group and scale picked without branches (NB): in the copy form, where the branches around the
+  // scale conversion ran the registers out (spills), and where the caller asks for it (NBS) for x
+  // read from L2 (a branch join waits for the chunk's x loads in flight; measured on MI355X,
+  // 5120 x 13824 M = 4: 14.4 -> 11.5 us; 14336 x 4096 M = 8 measured 12.2 -> 13.0, 4096 x 14336
+  // M = 4 9.4 -> 10.0, and the M = 1 forms 1 - 6 % slower, so those keep the branches)
+  constexpr bool NB = XLDS == 3 || (XLDS == 0 && NBS);
+  auto scale_at = [&](uint32_t rec, uint32_t s32) {
+    return NB ? scale_of_nb(rec, s32, a.scale_kind) : scale_of(rec, s32, a.scale_kind);
+  };
   __shared__ float red[NWV][MT * TW * NR][64];
   extern __shared__ __attribute__((aligned(16))) uint16_t xlds[];
 
   // Chunk and tile bookkeeping is wave-uniform (scalar registers).
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int cg = RTK ? 0 : wave / KSPLIT, ks = RTK ? wave : wave % KSPLIT;
-  const int nks = RTK ? (int)(blockDim.x >> 6) : KSPLIT;   // waves sharing the tile
-  const int ct0 = ((XMAP ? xcd_contiguous_block() : (int)blockIdx.x) * CGS + cg) * TW;
+  // launch-set form: blockDim.x / 64 waves; the copy form (XLDS = 3) splits them into a.cgs column
+  // groups of nks waves, the others have one group (no division on the way to the first load)
+  constexpr bool GROUPS = RTK && XLDS == 3;
+  const int nwaves = RTK ? (int)(blockDim.x >> 6) : NWV;
+  const int nks = RTK ? (GROUPS ? nwaves / a.cgs : nwaves) : KSPLIT;   // waves sharing a group's tiles
+  const int cg = RTK ? (GROUPS ? wave / nks : 0) : wave / KSPLIT;
+  const int ks = RTK ? wave - cg * nks : wave % KSPLIT;
+  const int ct0 = ((XMAP ? xcd_contiguous_block() : (int)blockIdx.x) * (GROUPS ? a.cgs : CGS) + cg) * TW;
   const int cpw = RTK ? TCH : (a.KC + KSPLIT - 1) / KSPLIT;
   const int kc0 = ks * cpw;
   const int kc1 = min(a.KC, kc0 + cpw);
@@ -152,7 +174,7 @@ skinny_kernel(const SkinnyArgs a) {
         load_words<PW, kAuxStream>(rw[i], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &c.w[i][4 * p]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
+      const int g = segment_group<NB>(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
         c.rec[i][s] = load_b32(rm[i], voff_m, (uint32_t)g * 64u);
@@ -199,8 +221,21 @@ skinny_kernel(const SkinnyArgs a) {
 
   // per-chunk sums of x (ONE): TCH floats per wave after the staged rows
   float* const xsum = reinterpret_cast<float*>(xlds + (XLDS ? a.M * xrow : 0)) + wave * TCH;
+  // ONE = 2: per-(chunk, row) sums of the workgroup's copy of x, [KC][16] floats after the rows
+  float* const xs2 = reinterpret_cast<float*>(xlds + (XLDS ? a.M * xrow : 0));
   auto compute_one = [&](const WChunk& c, const XChunk& xc, int kc) {
-    if constexpr (ONE) {
+    if constexpr (ONE == 2) {
+      // rows 4q .. 4q + 3 of this lane's accumulators; rows >= M repeat row 0 and are never stored
+      const f32x4 sx = *reinterpret_cast<const f32x4*>(xs2 + kc * 16 + 4 * q);
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) tmp = mfma16<XT>(xc.xa[0][t], build_b_offset<BITS, XT>(c.w[i], t), tmp);
+        const float off = 128.f + (float)zero_of(c.rec[i][0]);
+        acc[0][i] += scale_at(c.rec[i][0], c.s32[i][0]) * (tmp - off * sx);
+      }
+    } else if constexpr (ONE) {
       const float sx = xsum[kc - kc0];
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
@@ -237,7 +272,7 @@ skinny_kernel(const SkinnyArgs a) {
           f32x4 tmp = c0[m][s];
 #pragma unroll
           for (int t = s * SEG; t < (s + 1) * SEG; ++t) tmp = mfma16<XT>(xc.xa[m][t], b[t], tmp);
-          acc[m][i] += scale_of(c.rec[i][s], c.s32[i][s], a.scale_kind) * tmp;
+          acc[m][i] += scale_at(c.rec[i][s], c.s32[i][s]) * tmp;
         }
     }
   };
@@ -292,6 +327,37 @@ skinny_kernel(const SkinnyArgs a) {
   for (int j = 0; j < DEPTH; ++j)
     if (TCH > 0 || kc0 + j < kc1) load_w(TCH > 0 ? chunk_at(j) : kc0 + j, ring[j]);
 
+  if constexpr (XLDS == 3) {
+    // after the ring, so that the weights' HBM latency overlaps the copy; every wave's share of the
+    // copy (and its ring) has landed before any wave reads x
+    const int per_row = a.Kx >> 9;                     // rows of Kx inputs, zeros past K
+    const int n_inst = a.M * per_row;
+    for (int d = wave; d < n_inst; d += nwaves) {
+      const int r = d / per_row, pc = d - r * per_row;
+      const int k = pc * 512 + lane * 8;
+      const uint32_t vo = k < a.K ? (uint32_t)(r * a.ld + k) * 2u : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(xlds + r * xrow + pc * 512), 16, vo, 0u, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if constexpr (ONE == 2) {
+      // the sums of every chunk's rows once per workgroup, by MFMA against an all-ones operand (the
+      // products are exact, the sums fp32 as in the multiply itself)
+      u32x4 ones;
+      ones[0] = ones[1] = ones[2] = ones[3] = XT == 1 ? 0x3F803F80u : 0x3C003C00u;
+      for (int kc = wave; kc < (a.Kx >> 7); kc += nwaves) {   // padding chunks: sums of zeros
+        XChunk xc;
+        load_x_lds(kc, xc);
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v = mfma16<XT>(xc.xa[0][t], ones, v);
+        if (col == 0) *reinterpret_cast<f32x4*>(xs2 + kc * 16 + 4 * q) = v;
+      }
+      __syncthreads();
+    }
+  }
+
   if constexpr (XLDS == 1) {
 #pragma unroll
     for (int r = 0; r < XLW; ++r) {
@@ -303,7 +369,7 @@ skinny_kernel(const SkinnyArgs a) {
         }
       }
     }
-    if constexpr (ONE) {
+    if constexpr (ONE == 1) {
       // piece r of a lane is 8 inputs of chunk kc0 + lane / 16 + 4 r; its 16 lanes add up
 #pragma unroll
       for (int r = 0; r < XLW; ++r) {
@@ -369,6 +435,9 @@ skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
     for (int j = 0; j < TCH; ++j) {
       const int kc = chunk_at(j);
+      // the workgroup-copy form's LDS reads stay within their chunk (hoisted over long ranges they
+      // ran the registers out)
+      if constexpr (XLDS == 3) __builtin_amdgcn_sched_barrier(0);
       if constexpr (XLDS) {
         load_x_lds(kc, xcur);
       } else {
@@ -410,14 +479,14 @@ skinny_kernel(const SkinnyArgs a) {
     // unrolled to the workgroup's largest wave count, slots of absent waves masked, so that every
     // LDS read is issued before the first add (a loop bounded at run time waited for each in turn)
 #pragma unroll
-    for (int w2 = 1; w2 < (RTK ? NWV : KSPLIT); ++w2)
+    for (int w2 = 1; w2 < (RTK ? NWV : KSPLIT); ++w2)   // (launch-set form: slots past nks masked)
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < TW; ++i)
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
-            const float v = red[wave + w2][(m * TW + i) * NR + r][lane];
+            const float v = red[GROUPS ? min(wave + w2, NWV - 1) : wave + w2][(m * TW + i) * NR + r][lane];
             acc[m][i][r] += (!RTK || w2 < nks) ? v : 0.f;
           }
   }
@@ -478,6 +547,50 @@ inline int skinny_m1_chunks(int KC) { return KC <= 32 ? 4 : (KC <= 72 || KC % 16
 inline bool skinny_m1_act_rule(int64_t M, int Kp, int seg_steps, bool has_iperm) {
   return M == 1 && has_iperm && seg_steps == 4 && Kp <= kIpermMaxKp;
 }
+// 2 <= M <= 16, the copy form (XLDS = 3 with launch-set waves): each workgroup copies x[0:M, 0:Kx]
+// into LDS once (1 KB buffer_load ... lds pieces), cgs column groups of one tile each share it, and
+// a group's nks waves split K in ranges of T chunks (padding chunks past the layer read zeros);
+// bf16 x takes the offset form (128 + code, the -(128 + zero) * sum_k x correction from per-chunk,
+// per-row sums the workgroup takes once by MFMA against an all-ones operand).  Workgroups are sized
+// so that about one round of them fills the chip: one per compute unit when the copy takes more
+// than half of the LDS (up to 16 waves), two otherwise (up to 8); cgs = ceil(CT / (256 x that)),
+// T = 16 while that many waves fit, else 32.  Measured on MI355X against the previous dispatch (the
+// mid kernel's split K with its reduction launch, or x read from L2), us: 8192 x 28672 bf16 M = 2 /
+// 4 / 6 / 8: 26.4 / 27.9 / 28.8 / 30.1 -> 24.2 / 24.9 / 25.5 / 26.2; 4096 x 14336 fp16 M = 8 / 12 /
+// 16: 10.2 / 11.3 / 12.7 -> 9.5 / 9.9 / 10.4; 14336 x 4096 fp16 M = 2 / 4: 11.3 / 11.8 -> 8.7 /
+// 9.7; 8192 x 8192 fp16 M = 4: 11.9 -> 9.4.  Not taken: act-order (x would need
+// sorting), 8-bit codes, 32-input groups, 40 / 48 / 56 chunks at M <= 8 and up to 32 chunks at
+// M <= 4 (x read from L2 measured faster: 5120 x 13824 M = 4 / 5 11.5 against 12.2 / 12.3,
+// 4096 x 14336 M = 4 9.4 against 9.8), and copies that do not fit the LDS (the 8192-input layer
+// above 8 rows).
+struct CopyPlan {
+  bool ok;
+  int T, nks, cgs;
+  size_t lds;              // dynamic LDS: the rows, and the per-(chunk, row) sums of the offset form
+};
+inline CopyPlan skinny_copy_plan(int64_t M, int KC, int CT, int bits, int seg_steps, bool has_perm) {
+  CopyPlan p{false, 0, 0, 0, 0};
+  if (M < 2 || M > 16 || bits > 4 || seg_steps != 4 || has_perm) return p;
+  if ((KC == 40 || KC == 48 || KC == 56) && M <= 8) return p;
+  if (KC <= 32 && M <= 4) return p;
+  constexpr size_t kLds = 160 * 1024, kStatic = 16 * 1024;   // the reduction slots of 16 waves
+  for (int T : {16, 32}) {
+    const int nks = (KC + T - 1) / T;
+    const size_t Kx = (size_t)nks * T * kChunkK;
+    const size_t lds = (size_t)M * (Kx + 8) * 2 + Kx / 2;
+    if (lds + kStatic > kLds) return p;
+    const int wpc = (lds + kStatic) * 2 <= kLds ? 2 : 1;
+    const int W = wpc == 1 ? 16 : 8;
+    int cgs = (CT + 256 * wpc - 1) / (256 * wpc);
+    cgs = cgs < 1 ? 1 : (cgs > W ? W : cgs);
+    const int nks_max = W / cgs > 0 ? W / cgs : 1;
+    if (nks <= nks_max) {
+      p = CopyPlan{true, T, nks, cgs, lds};
+      return p;
+    }
+  }
+  return p;
+}
 // 2 <= M <= 16 on the same layers: the same waves of 16 chunks with x read from L2 per chunk, one
 // column tile per wave below 512 column tiles and two from 512 (enough workgroups either way).
 // Measured on MI355X against the mid kernel / the tiled family (us): 14336 x 4096, M = 2 / 4 / 8 /
@@ -512,7 +625,8 @@ template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int
           int SEG1 = 1,   // SEG1 = 0: whole-chunk groups only (no 32-input-segment kernel is built)
           int WPE = 2,    // minimum waves per SIMD the register allocation must allow
           int NWV0 = 0,   // waves per workgroup (0: max(KSPLIT, 4)); a multiple of KSPLIT
-          int XMAP = 1>   // 1: workgroups renumbered XCD-contiguously (xcd_contiguous_block)
+          int XMAP = 1,   // 1: workgroups renumbered XCD-contiguously (xcd_contiguous_block)
+          int NBS = 0>    // 1: group and scale picked without branches (x read from L2)
 static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   constexpr int NWV = NWV0 ? NWV0 : (KSPLIT > 4 ? KSPLIT : 4);
   constexpr int CGS = NWV / KSPLIT;
@@ -520,7 +634,7 @@ static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
   // staged rows (+ the per-chunk sums of x of every wave, ONE)
   const size_t lds = (XLDS ? (size_t)a.M * (a.Kx + 8) * 2 : 0) + (ONE ? (size_t)NWV * TCH * 4 : 0);
   if (seg == 4)
-    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S, WPE, NWV0, XMAP>), dim3(blocks),
+    hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 4, XLDS, DEPTH, TCH, ONE, F32S, WPE, NWV0, XMAP, NBS>), dim3(blocks),
                        dim3(64 * NWV), lds, s, a);
   else if constexpr (TCH == 0 && SEG1)
     hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, TW, KSPLIT, 1, XLDS, DEPTH, 0, 0, F32S>), dim3(blocks),
@@ -561,6 +675,18 @@ static hipError_t run_m1_act(const SkinnyArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BITS, int XT, int TCH, int F32S>
+static hipError_t run_copy(const SkinnyArgs& a0, const CopyPlan& p, hipStream_t s) {
+  constexpr int ONE = XT == 1 ? 2 : 0;
+  SkinnyArgs a = a0;
+  a.Kx = p.nks * TCH * kChunkK;
+  a.cgs = p.cgs;
+  const int blocks = (a.CT + p.cgs - 1) / p.cgs;
+  hipLaunchKernelGGL((skinny_kernel<BITS, XT, 1, 1, 0, 4, 3, 4, TCH, ONE, F32S, 2, 16>), dim3(blocks),
+                     dim3(64 * p.cgs * p.nks), p.lds, s, a);
+  return hipGetLastError();
+}
+
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int F32S>
 static hipError_t run(const SkinnyArgs& a, int seg, hipStream_t s) {
   // Straight-line variants for the whole-chunk-segment case; ring depths measured best on
@@ -592,16 +718,20 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
     if (a.iperm) return run<BITS, XT, 1, 1, 4, 2, 4, F32S>(a, seg, s);
     return run<BITS, XT, 1, 1, 4, 1, 4, F32S>(a, seg, s);
   }
+  if constexpr (BITS <= 4) {
+    const CopyPlan cp = skinny_copy_plan(a.M, a.KC, a.CT, BITS, seg, a.iperm != nullptr);
+    if (cp.ok) return cp.T == 16 ? run_copy<BITS, XT, 16, F32S>(a, cp, s) : run_copy<BITS, XT, 32, F32S>(a, cp, s);
+  }
   if (skinny_mx_long(a.M, a.KC, a.CT, seg, a.iperm != nullptr)) {
     if (a.KC < 64) {     // 40 / 48 / 56 chunks: five to seven waves of 8
       if (a.CT >= 512) {
-        if (a.KC == 40) return run_tch<BITS, XT, 1, 2, 5, 0, 2, 8, 0, F32S, 0>(a, seg, s);
-        if (a.KC == 48) return run_tch<BITS, XT, 1, 2, 6, 0, 2, 8, 0, F32S, 0>(a, seg, s);
-        return run_tch<BITS, XT, 1, 2, 7, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+        if (a.KC == 40) return run_tch<BITS, XT, 1, 2, 5, 0, 2, 8, 0, F32S, 0, 2, 0, 1, 1>(a, seg, s);
+        if (a.KC == 48) return run_tch<BITS, XT, 1, 2, 6, 0, 2, 8, 0, F32S, 0, 2, 0, 1, 1>(a, seg, s);
+        return run_tch<BITS, XT, 1, 2, 7, 0, 2, 8, 0, F32S, 0, 2, 0, 1, 1>(a, seg, s);
       }
-      if (a.KC == 40) return run_tch<BITS, XT, 1, 1, 5, 0, 2, 8, 0, F32S, 0>(a, seg, s);
-      if (a.KC == 48) return run_tch<BITS, XT, 1, 1, 6, 0, 2, 8, 0, F32S, 0>(a, seg, s);
-      return run_tch<BITS, XT, 1, 1, 7, 0, 2, 8, 0, F32S, 0>(a, seg, s);
+      if (a.KC == 40) return run_tch<BITS, XT, 1, 1, 5, 0, 2, 8, 0, F32S, 0, 2, 0, 1, 1>(a, seg, s);
+      if (a.KC == 48) return run_tch<BITS, XT, 1, 1, 6, 0, 2, 8, 0, F32S, 0, 2, 0, 1, 1>(a, seg, s);
+      return run_tch<BITS, XT, 1, 1, 7, 0, 2, 8, 0, F32S, 0, 2, 0, 1, 1>(a, seg, s);
     }
     if (a.CT >= 512) {
       if (a.KC == 80) return run_tch<BITS, XT, 1, 2, 5, 0, 4, 16, 0, F32S, 0>(a, seg, s);
