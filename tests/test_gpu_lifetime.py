@@ -3,10 +3,11 @@ and validation checklist" item 6: repeated forwards, mutation and lifetime cases
 section "Marlin and caller-owned scratch": a graph caller preallocates the scratch and owns it for
 the graph's lifetime).
 
-- every PATH_AUTO route (skinny with staged x, skinny with x from L2, the mid kernel's split K and
-  its reduction launch, the tiled family's prep + tiles + split-K reduction, act-order staging and
-  act-order prep) captured in a HIP graph and replayed several times, with the program's own eager
-  work and new inputs between replays: every replay bitwise equal to the eager call;
+- every PATH_AUTO route (skinny with staged x, skinny with x from L2, the skinny copy form whole and
+  in two halves, the mid kernel's split K and its reduction launch, the tiled family's prep + tiles
+  + split-K reduction, act-order staging and act-order prep) captured in a HIP graph and replayed
+  several times, with the program's own eager work and new inputs between replays: every replay
+  bitwise equal to the eager call;
 - two handles on two streams, and one handle on two streams, each call with its own workspace:
   bitwise equal to the eager single-stream results;
 - a destroyed handle is refused (no use of freed memory); a device allocation failure during repack
@@ -42,8 +43,10 @@ def say(*a):
 ROUTES = [
     ("skinny staged x", 4096, 2048, 4, 128, False, "f16", 1, 0, False),
     ("skinny staged x bf16 offset form", 8192, 2048, 4, 128, False, "bf16", 1, 0, False),
-    ("skinny x from L2", 4096, 2048, 4, 128, False, "f16", 16, 1, False),
-    ("mid split K + reduction", 8192, 2048, 4, 128, False, "bf16", 12, 1, True),
+    ("skinny x from L2", 4096, 2048, 4, 128, False, "f16", 3, 1, False),
+    ("skinny copy of x", 4096, 2048, 4, 128, False, "f16", 16, 1, False),
+    ("skinny copy of x in two halves, offset form", 8192, 2048, 4, 128, False, "bf16", 12, 1, False),
+    ("mid split K + reduction", 8192, 2048, 8, 128, False, "bf16", 12, 1, True),
     ("tiled prep + split K + reduction", 4096, 2048, 4, 128, False, "bf16", 64, 2, True),
     ("tiled large M", 2048, 1024, 3, 64, False, "f16", 300, 0, None),
     ("act-order staged", 2048, 1024, 4, 128, True, "f16", 3, 0, False),
@@ -127,8 +130,8 @@ def test_two_handles_on_two_streams():
 def test_one_handle_on_two_streams():
     import torch
     say("one handle, two streams")
-    K, N = 8192, 2048
-    L = gi.make_layer(K, N, 4, 128, desc_act=False, scales_dtype="f16", seed=gi.seed_for(9, 40))
+    K, N = 8192, 2048      # 8-bit codes: the mid kernel's split K at 12 rows, the tiled split K at 64
+    L = gi.make_layer(K, N, 8, 128, desc_act=False, scales_dtype="f16", seed=gi.seed_for(9, 40))
     h = repack_layer(L)
     cases = []
     for M, xdt in ((12, "bf16"), (64, "f16")):     # both need workspace (split K / prep)

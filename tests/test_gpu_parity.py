@@ -163,15 +163,20 @@ def test_m1_rule_any_k(K, bits, xdt, sdt, desc):
     h.close()
 
 
-# 2 <= M <= 16 through the copy form (x[0:M] copied into LDS once per workgroup, column groups and
-# launch-set waves of T chunks, padding chunks past the layer; bf16 x in the offset form): the
-# shapes pick T = 16 or 32, one or several column groups, one or two workgroups per compute unit,
-# padding (24 and 9 chunks), whole-layer and 256-input groups, every scale dtype, 2/3/4-bit codes
+# 2 <= M <= 16 through the copy form (x[0:M] copied into LDS once per workgroup, or in two halves
+# of the inputs, column groups and launch-set waves of T chunks, padding chunks past the layer; bf16
+# x in the offset form): the shapes pick T = 16 or 32, one or several column groups, one or two
+# workgroups per compute unit, padding (24, 9 and 63 chunks), whole-layer and 256-input groups,
+# every scale dtype, 2/3/4-bit codes
 COPY_FORM = [(8192, 2048, 4, 128, "bf16", "f16", (2, 3, 5, 8)), (8192, 3072, 2, 128, "bf16", "bf16", (4, 7)),
              (8192, 2048, 3, 256, "bf16", "f32", (2, 6)), (4096, 1024, 4, 128, "f16", "f16", (4, 9, 16)),
              (4096, 2048, 3, -1, "bf16", "f16", (12, 16)), (14336, 512, 4, 128, "f16", "bf16", (2, 4)),
              (3072, 512, 4, 128, "f16", "f16", (8, 13)), (1152, 768, 2, 128, "bf16", "f16", (6, 16)),
-             (16384, 512, 4, 128, "bf16", "f16", (3, 4))]
+             (16384, 512, 4, 128, "bf16", "f16", (3, 4)),
+             # x copied in two halves of the inputs (the whole rows do not fit the LDS)
+             (8192, 2048, 4, 128, "bf16", "f16", (9, 16)), (8192, 1536, 2, 128, "bf16", "bf16", (12,)),
+             (14336, 512, 4, 128, "f16", "f16", (5, 8)), (16384, 512, 3, 256, "bf16", "f32", (8, 11)),
+             (8064, 1024, 4, 128, "f16", "f16", (16,))]
 
 
 @pytest.mark.parametrize("K,N,bits,gs,xdt,sdt,Ms", COPY_FORM)
@@ -262,8 +267,8 @@ def test_bf16_rows_longer_than_the_one_pass_prep():
 
 # ---- the layer's optional bias (gptq_gemm_bias) ---------------------------------------------------
 # Every family adds the bias in its own epilogue: the skinny kernel (x in LDS, the bf16 M = 1 form,
-# x from L2), the mid kernel without and with split K (in-kernel store, reduction kernel), and both
-# tiled tiles.
+# x from L2, the copy form), the mid kernel without and with split K (in-kernel store, reduction
+# kernel), and both tiled tiles.
 
 BIAS_MS = [1, 3, 8, 17, 33, 130, 257]
 

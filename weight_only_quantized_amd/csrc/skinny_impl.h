@@ -91,12 +91,14 @@ __device__ __forceinline__ int segment_group(int si, uint32_t gmagic, int gshift
 // sits in the metadata record and no second load is issued per chunk (2 % on the 8192-input M = 1
 // and M = 4 calls on MI355X).
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int SEG, int XLDS, int DEPTH, int TCH, int ONE = 0,
-          int F32S = 1, int WPE = 2, int NWV0 = 0, int XMAP = 1, int NBS = 0>
+          int F32S = 1, int WPE = 2, int NWV0 = 0, int XMAP = 1, int NBS = 0, int PH = 1>
 __global__ void __launch_bounds__(64 * (NWV0 ? NWV0 : (KSPLIT == 0 ? 16 : (KSPLIT > 4 ? KSPLIT : 4))))
 __attribute__((amdgpu_waves_per_eu(WPE)))
 skinny_kernel(const SkinnyArgs a) {
   static_assert(ONE != 1 || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
                 "the M = 1 form needs whole-chunk segments, per-wave staging and an exact offset operand");
+  static_assert(PH == 1 || (PH == 2 && XLDS == 3 && KSPLIT == 0 && TCH % 16 == 0),
+                "two copy phases: the copy form's launch-set waves");
   static_assert(ONE != 2 || (MT == 1 && SEG == 4 && XLDS == 3 && TCH > 0 && XT == 1 && BITS <= 4),
                 "the offset form for up to 16 rows needs whole-chunk segments, the workgroup's copy of x and "
                 "an exact bf16 offset operand");
@@ -138,7 +140,11 @@ skinny_kernel(const SkinnyArgs a) {
   const int kc0 = ks * cpw;
   const int kc1 = min(a.KC, kc0 + cpw);
   const int col = lane & 15, q = lane >> 4;
-  const int xrow = a.Kx + 8;                    // LDS row stride (halves)
+  // PH = 2 (the copy form when x[0:M, 0:Kx] does not fit the LDS): the workgroup copies the first
+  // half of the inputs, every wave takes the first half of its chunks from there, and after a
+  // barrier the second half replaces it; a wave's chunks are the T / 2 of its slot in each half
+  const int Kxs = a.Kx / PH;                    // staged inputs per row
+  const int xrow = Kxs + 8;                     // LDS row stride (halves)
 
   f32x4 acc[MT][TW];
 #pragma unroll
@@ -320,33 +326,38 @@ skinny_kernel(const SkinnyArgs a) {
   }
   // With TCH > 0 the waves of neighbouring column tiles walk their K ranges from different
   // starting chunks, so at any moment they read different offsets within their units.
-  const int rot = TCH > 0 ? (ct0 * 5) & (TCH - 1) : 0;
-  auto chunk_at = [&](int j) { return kc0 + ((j + rot) & (TCH > 0 ? TCH - 1 : 0)); };
+  const int rot = (TCH > 0 && PH == 1) ? (ct0 * 5) & (TCH - 1) : 0;
+  const int kch = Kxs >> 7;                     // chunks per copy phase
+  auto chunk_at = [&](int j) {
+    if constexpr (PH == 2) return (j < TCH / 2 ? 0 : kch) + ks * (TCH / 2) + (j & (TCH / 2 - 1));
+    return kc0 + ((j + rot) & (TCH > 0 ? TCH - 1 : 0));
+  };
   WChunk ring[DEPTH];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j)
     if (TCH > 0 || kc0 + j < kc1) load_w(TCH > 0 ? chunk_at(j) : kc0 + j, ring[j]);
 
-  if constexpr (XLDS == 3) {
-    // after the ring, so that the weights' HBM latency overlaps the copy; every wave's share of the
-    // copy (and its ring) has landed before any wave reads x
-    const int per_row = a.Kx >> 9;                     // rows of Kx inputs, zeros past K
+  // the copy form's copy of phase h (inputs h * Kxs .. (h + 1) * Kxs - 1 of every row, zeros past
+  // K) and, for the offset form, the sums of each of its chunks' rows, by MFMA against an all-ones
+  // operand (the products are exact, the sums fp32 as in the multiply itself)
+  auto copy_phase = [&](int h) {
+    const int per_row = Kxs >> 9;
     const int n_inst = a.M * per_row;
     for (int d = wave; d < n_inst; d += nwaves) {
       const int r = d / per_row, pc = d - r * per_row;
-      const int k = pc * 512 + lane * 8;
+      const int k = h * Kxs + pc * 512 + lane * 8;
       const uint32_t vo = k < a.K ? (uint32_t)(r * a.ld + k) * 2u : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx, (__attribute__((address_space(3))) void*)(xlds + r * xrow + pc * 512), 16, vo, 0u, 0, 0);
     }
+    // every wave's share of the copy (and its weights in flight, which complete in order before
+    // it) has landed before any wave reads x
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (ONE == 2) {
-      // the sums of every chunk's rows once per workgroup, by MFMA against an all-ones operand (the
-      // products are exact, the sums fp32 as in the multiply itself)
       u32x4 ones;
       ones[0] = ones[1] = ones[2] = ones[3] = XT == 1 ? 0x3F803F80u : 0x3C003C00u;
-      for (int kc = wave; kc < (a.Kx >> 7); kc += nwaves) {   // padding chunks: sums of zeros
+      for (int kc = wave; kc < kch; kc += nwaves) {   // padding chunks: sums of zeros
         XChunk xc;
         load_x_lds(kc, xc);
         f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -356,7 +367,8 @@ skinny_kernel(const SkinnyArgs a) {
       }
       __syncthreads();
     }
-  }
+  };
+  if constexpr (XLDS == 3) copy_phase(0);   // after the ring: the weights' HBM latency overlaps it
 
   if constexpr (XLDS == 1) {
 #pragma unroll
@@ -435,15 +447,31 @@ skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
     for (int j = 0; j < TCH; ++j) {
       const int kc = chunk_at(j);
-      // the workgroup-copy form's LDS reads stay within their chunk (hoisted over long ranges they
-      // ran the registers out)
-      if constexpr (XLDS == 3) __builtin_amdgcn_sched_barrier(0);
+      const int kcl = (PH == 2 && j >= TCH / 2) ? kc - kch : kc;   // chunk within the staged copy
+      if constexpr (PH == 2) {
+        if (j == TCH / 2) {
+          // the first half's sums are complete here (otherwise the compiler sinks them past the
+          // copy below, to their use at the end, and keeps every chunk's partial live until then)
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < TW; ++i) asm volatile("" : "+v"(acc[m][i]));
+          // every wave is done with the first half before the second replaces it (LDS-only fence:
+          // the weights in flight are not waited for here)
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+          copy_phase(1);
+        }
+      }
+      if constexpr (XLDS == 3) __builtin_amdgcn_sched_barrier(0);   // copy form: LDS reads per chunk
       if constexpr (XLDS) {
-        load_x_lds(kc, xcur);
+        load_x_lds(kcl, xcur);
       } else {
         if (j + 1 < TCH) load_x_global(chunk_at(j + 1), xnxt);
       }
-      if constexpr (ONE) compute_one(ring[j % DEPTH], xcur, kc);
+      if constexpr (ONE) compute_one(ring[j % DEPTH], xcur, ONE == 2 ? kcl : kc);
       else compute(ring[j % DEPTH], xcur);
       if (j + DEPTH < TCH) load_w(chunk_at(j + DEPTH), ring[j % DEPTH]);
       if constexpr (!XLDS) xcur = xnxt;
@@ -565,30 +593,28 @@ inline bool skinny_m1_act_rule(int64_t M, int Kp, int seg_steps, bool has_iperm)
 // above 8 rows).
 struct CopyPlan {
   bool ok;
-  int T, nks, cgs;
+  int T, nks, cgs, ph;     // ph = 2: x copied in two halves of the inputs
   size_t lds;              // dynamic LDS: the rows, and the per-(chunk, row) sums of the offset form
 };
 inline CopyPlan skinny_copy_plan(int64_t M, int KC, int CT, int bits, int seg_steps, bool has_perm) {
-  CopyPlan p{false, 0, 0, 0, 0};
+  CopyPlan p{false, 0, 0, 0, 1, 0};
   if (M < 2 || M > 16 || bits > 4 || seg_steps != 4 || has_perm) return p;
   if ((KC == 40 || KC == 48 || KC == 56) && M <= 8) return p;
   if (KC <= 32 && M <= 4) return p;
   constexpr size_t kLds = 160 * 1024, kStatic = 16 * 1024;   // the reduction slots of 16 waves
-  for (int T : {16, 32}) {
-    const int nks = (KC + T - 1) / T;
-    const size_t Kx = (size_t)nks * T * kChunkK;
-    const size_t lds = (size_t)M * (Kx + 8) * 2 + Kx / 2;
-    if (lds + kStatic > kLds) return p;
-    const int wpc = (lds + kStatic) * 2 <= kLds ? 2 : 1;
-    const int W = wpc == 1 ? 16 : 8;
-    int cgs = (CT + 256 * wpc - 1) / (256 * wpc);
-    cgs = cgs < 1 ? 1 : (cgs > W ? W : cgs);
-    const int nks_max = W / cgs > 0 ? W / cgs : 1;
-    if (nks <= nks_max) {
-      p = CopyPlan{true, T, nks, cgs, lds};
-      return p;
+  for (int ph : {1, 2})
+    for (int T : {16, 32}) {
+      const int nks = (KC + T - 1) / T;
+      const size_t Kxs = (size_t)nks * T * kChunkK / ph;      // inputs per staged row
+      const size_t lds = (size_t)M * (Kxs + 8) * 2 + Kxs / 2;
+      if (lds + kStatic > kLds) continue;
+      const int wpc = (lds + kStatic) * 2 <= kLds ? 2 : 1;
+      const int W = wpc == 1 ? 16 : 8;
+      int cgs = (CT + 256 * wpc - 1) / (256 * wpc);
+      cgs = cgs < 1 ? 1 : (cgs > W ? W : cgs);
+      const int nks_max = W / cgs > 0 ? W / cgs : 1;
+      if (nks <= nks_max) return CopyPlan{true, T, nks, cgs, ph, lds};
     }
-  }
   return p;
 }
 // 2 <= M <= 16 on the same layers: the same waves of 16 chunks with x read from L2 per chunk, one
@@ -675,14 +701,14 @@ static hipError_t run_m1_act(const SkinnyArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BITS, int XT, int TCH, int F32S>
+template <int BITS, int XT, int TCH, int F32S, int PH>
 static hipError_t run_copy(const SkinnyArgs& a0, const CopyPlan& p, hipStream_t s) {
   constexpr int ONE = XT == 1 ? 2 : 0;
   SkinnyArgs a = a0;
   a.Kx = p.nks * TCH * kChunkK;
   a.cgs = p.cgs;
   const int blocks = (a.CT + p.cgs - 1) / p.cgs;
-  hipLaunchKernelGGL((skinny_kernel<BITS, XT, 1, 1, 0, 4, 3, 4, TCH, ONE, F32S, 2, 16>), dim3(blocks),
+  hipLaunchKernelGGL((skinny_kernel<BITS, XT, 1, 1, 0, 4, 3, 4, TCH, ONE, F32S, 2, 16, 1, 0, PH>), dim3(blocks),
                      dim3(64 * p.cgs * p.nks), p.lds, s, a);
   return hipGetLastError();
 }
@@ -720,7 +746,11 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
   }
   if constexpr (BITS <= 4) {
     const CopyPlan cp = skinny_copy_plan(a.M, a.KC, a.CT, BITS, seg, a.iperm != nullptr);
-    if (cp.ok) return cp.T == 16 ? run_copy<BITS, XT, 16, F32S>(a, cp, s) : run_copy<BITS, XT, 32, F32S>(a, cp, s);
+    if (cp.ok) {
+      if (cp.ph == 1)
+        return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 1>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 1>(a, cp, s);
+      return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 2>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 2>(a, cp, s);
+    }
   }
   if (skinny_mx_long(a.M, a.KC, a.CT, seg, a.iperm != nullptr)) {
     if (a.KC < 64) {     // 40 / 48 / 56 chunks: five to seven waves of 8
