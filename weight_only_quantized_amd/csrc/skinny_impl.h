@@ -332,15 +332,10 @@ skinny_kernel(const SkinnyArgs a) {
     if constexpr (PH == 2) return (j < TCH / 2 ? 0 : kch) + ks * (TCH / 2) + (j & (TCH / 2 - 1));
     return kc0 + ((j + rot) & (TCH > 0 ? TCH - 1 : 0));
   };
-  WChunk ring[DEPTH];
-#pragma unroll
-  for (int j = 0; j < DEPTH; ++j)
-    if (TCH > 0 || kc0 + j < kc1) load_w(TCH > 0 ? chunk_at(j) : kc0 + j, ring[j]);
-
   // the copy form's copy of phase h (inputs h * Kxs .. (h + 1) * Kxs - 1 of every row, zeros past
   // K) and, for the offset form, the sums of each of its chunks' rows, by MFMA against an all-ones
   // operand (the products are exact, the sums fp32 as in the multiply itself)
-  auto copy_phase = [&](int h) {
+  auto copy_issue = [&](int h) {
     const int per_row = Kxs >> 9;
     const int n_inst = a.M * per_row;
     for (int d = wave; d < n_inst; d += nwaves) {
@@ -350,10 +345,20 @@ skinny_kernel(const SkinnyArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx, (__attribute__((address_space(3))) void*)(xlds + r * xrow + pc * 512), 16, vo, 0u, 0, 0);
     }
-    // every wave's share of the copy (and its weights in flight, which complete in order before
-    // it) has landed before any wave reads x
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+  // ring_after: the weight ring was issued after the copy, and stays in flight (its loads complete
+  // in order after the copy's); otherwise everything this wave has in flight is waited for
+  constexpr int NRING = XLDS == 3 ? DEPTH * TW * (PARTS + NSEG * (1 + F32S)) : 0;   // loads of the ring
+  auto copy_finish = [&](bool ring_after) {
+    if (ring_after) wait_vmcnt<NRING>();
+    else __builtin_amdgcn_s_waitcnt(0);
+    // every wave's share of the copy has landed before any wave reads x (LDS-only fences: the
+    // weights in flight are not waited for)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (ONE == 2) {
       u32x4 ones;
       ones[0] = ones[1] = ones[2] = ones[3] = XT == 1 ? 0x3F803F80u : 0x3C003C00u;
@@ -365,10 +370,25 @@ skinny_kernel(const SkinnyArgs a) {
         for (int t = 0; t < 4; ++t) v = mfma16<XT>(xc.xa[0][t], ones, v);
         if (col == 0) *reinterpret_cast<f32x4*>(xs2 + kc * 16 + 4 * q) = v;
       }
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  if constexpr (XLDS == 3) copy_phase(0);   // after the ring: the weights' HBM latency overlaps it
+  // the copy form's copy goes out first (L2 hits, done long before the ring's HBM loads), so that
+  // the wait for it leaves the ring in flight
+  if constexpr (XLDS == 3) {
+    copy_issue(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  WChunk ring[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j)
+    if (TCH > 0 || kc0 + j < kc1) load_w(TCH > 0 ? chunk_at(j) : kc0 + j, ring[j]);
+
+  if constexpr (XLDS == 3) copy_finish(true);
 
   if constexpr (XLDS == 1) {
 #pragma unroll
@@ -462,7 +482,8 @@ skinny_kernel(const SkinnyArgs a) {
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-          copy_phase(1);
+          copy_issue(1);
+          copy_finish(false);
         }
       }
       if constexpr (XLDS == 3) __builtin_amdgcn_sched_barrier(0);   // copy form: LDS reads per chunk
