@@ -176,7 +176,10 @@ COPY_FORM = [(8192, 2048, 4, 128, "bf16", "f16", (2, 3, 5, 8)), (8192, 3072, 2, 
              # x copied in two halves of the inputs (the whole rows do not fit the LDS)
              (8192, 2048, 4, 128, "bf16", "f16", (9, 16)), (8192, 1536, 2, 128, "bf16", "bf16", (12,)),
              (14336, 512, 4, 128, "f16", "f16", (5, 8)), (16384, 512, 3, 256, "bf16", "f32", (8, 11)),
-             (8064, 1024, 4, 128, "f16", "f16", (16,))]
+             (8064, 1024, 4, 128, "f16", "f16", (16,)),
+             # two 16-row blocks (17 <= M <= 32) in one, two or four copy phases
+             (8192, 2048, 4, 128, "bf16", "f16", (17, 24, 32)), (4096, 1024, 3, 128, "f16", "bf16", (20, 32)),
+             (2048, 768, 2, 128, "bf16", "f32", (32,)), (8192, 1024, 3, -1, "bf16", "f16", (29,))]
 
 
 @pytest.mark.parametrize("K,N,bits,gs,xdt,sdt,Ms", COPY_FORM)
@@ -194,6 +197,24 @@ def test_copy_form(K, N, bits, gs, xdt, sdt, Ms):
         for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
             check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=(K, N, bits, gs, xdt, sdt, M, p))
         check(run_gemm(h, x[:M], xdt, bias=bias, bias_tag=sdt), xdt, y_ref_b[:M], label=("bias", K, N, M))
+    h.close()
+
+
+@pytest.mark.parametrize("K,N,bits,xdt,Ms", [(8192, 1024, 2, "f16", (2, 8, 16, 32)), (8192, 768, 4, "bf16", (5, 12, 24)),
+                                              (4096, 1024, 3, "bf16", (3, 17, 32))])
+def test_copy_form_act_order(K, N, bits, xdt, Ms):
+    """Act-order at 2 <= M <= 32: x sorted into the workspace, then the copy form; the oracle
+    multiplies x as given against the act-order layer."""
+    import weight_only_quantized_amd as wq
+    say("copy-form act-order", K, N, bits, xdt, Ms)
+    L = gi.make_layer(K, N, bits, 128, desc_act=True, scales_dtype="f16", seed=K + N + 7 * bits)
+    h = repack_layer(L)
+    assert h.info()["has_perm"] == 1
+    x = gi.make_x(max(Ms), K, xdt, seed=K + 9)
+    y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, "f16", L.g_idx, bits)
+    for M in Ms:
+        for p in (wq.PATH_AUTO, wq.PATH_SKINNY):
+            check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=("act", K, N, bits, xdt, M, p))
     h.close()
 
 

@@ -12,7 +12,8 @@ static inline size_t align256m(size_t b) { return (b + 255) / 256 * 256; }
 bool skinny_one_launch(const gptq_layer* L, int64_t M) {
   return skinny_reads_x_from_l2(M, L->KC, L->CT, L->bits, L->seg_steps) ||
          skinny_mx_long(M, L->KC, L->CT, L->seg_steps, L->has_perm != 0) ||
-         skinny_copy_plan(M, L->KC, L->CT, L->bits, L->seg_steps, L->has_perm != 0).ok;
+         // (act-order layers: the skinny path sorts x into the workspace first, skinny_needs_xsorted)
+         skinny_copy_plan(M, L->KC, L->CT, L->bits, L->seg_steps, false).ok;
 }
 
 int mid_slices(const gptq_layer* L, int64_t M) { return mid_plan(L, M).KS; }

@@ -97,9 +97,9 @@ __attribute__((amdgpu_waves_per_eu(WPE)))
 skinny_kernel(const SkinnyArgs a) {
   static_assert(ONE != 1 || (MT == 1 && SEG == 4 && XLDS == 1 && TCH > 0 && (XT == 0 || BITS <= 4)),
                 "the M = 1 form needs whole-chunk segments, per-wave staging and an exact offset operand");
-  static_assert(PH == 1 || (PH == 2 && XLDS == 3 && KSPLIT == 0 && TCH % 16 == 0),
-                "two copy phases: the copy form's launch-set waves");
-  static_assert(ONE != 2 || (MT == 1 && SEG == 4 && XLDS == 3 && TCH > 0 && XT == 1 && BITS <= 4),
+  static_assert(PH == 1 || ((PH == 2 || PH == 4) && XLDS == 3 && KSPLIT == 0 && TCH % (4 * PH) == 0),
+                "copy phases: the copy form's launch-set waves, at least four chunks per phase");
+  static_assert(ONE != 2 || (MT <= 2 && SEG == 4 && XLDS == 3 && TCH > 0 && XT == 1 && BITS <= 4),
                 "the offset form for up to 16 rows needs whole-chunk segments, the workgroup's copy of x and "
                 "an exact bf16 offset operand");
   constexpr bool RTK = KSPLIT == 0;             // waves per tile set at launch
@@ -122,8 +122,12 @@ skinny_kernel(const SkinnyArgs a) {
   auto scale_at = [&](uint32_t rec, uint32_t s32) {
     return NB ? scale_of_nb(rec, s32, a.scale_kind) : scale_of(rec, s32, a.scale_kind);
   };
-  __shared__ float red[NWV][MT * TW * NR][64];
+  // reduction slots; the copy form reuses its copy of x for them (after a barrier), which leaves
+  // its whole LDS to the copy
+  __shared__ float red_s[XLDS == 3 ? 1 : NWV][MT * TW * NR][64];
   extern __shared__ __attribute__((aligned(16))) uint16_t xlds[];
+  float (*const red)[MT * TW * NR][64] =
+      XLDS == 3 ? reinterpret_cast<float (*)[MT * TW * NR][64]>(xlds) : red_s;
 
   // Chunk and tile bookkeeping is wave-uniform (scalar registers).
   const int lane = threadIdx.x & 63;
@@ -140,9 +144,9 @@ skinny_kernel(const SkinnyArgs a) {
   const int kc0 = ks * cpw;
   const int kc1 = min(a.KC, kc0 + cpw);
   const int col = lane & 15, q = lane >> 4;
-  // PH = 2 (the copy form when x[0:M, 0:Kx] does not fit the LDS): the workgroup copies the first
-  // half of the inputs, every wave takes the first half of its chunks from there, and after a
-  // barrier the second half replaces it; a wave's chunks are the T / 2 of its slot in each half
+  // PH = 2 or 4 (the copy form when x[0:M, 0:Kx] does not fit the LDS): the workgroup copies the
+  // first PH-th of the inputs, every wave takes the first T / PH of its chunks from there, and after
+  // a barrier the next part replaces it; a wave's chunks are the T / PH of its slot in each part
   const int Kxs = a.Kx / PH;                    // staged inputs per row
   const int xrow = Kxs + 8;                     // LDS row stride (halves)
 
@@ -231,15 +235,23 @@ skinny_kernel(const SkinnyArgs a) {
   float* const xs2 = reinterpret_cast<float*>(xlds + (XLDS ? a.M * xrow : 0));
   auto compute_one = [&](const WChunk& c, const XChunk& xc, int kc) {
     if constexpr (ONE == 2) {
-      // rows 4q .. 4q + 3 of this lane's accumulators; rows >= M repeat row 0 and are never stored
-      const f32x4 sx = *reinterpret_cast<const f32x4*>(xs2 + kc * 16 + 4 * q);
+      // rows m * 16 + 4q .. + 3 of this lane's accumulators; rows >= M repeat row 0 and are never
+      // stored; each B operand serves every row block
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
-        f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 b[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) tmp = mfma16<XT>(xc.xa[0][t], build_b_offset<BITS, XT>(c.w[i], t), tmp);
+        for (int t = 0; t < 4; ++t) b[t] = build_b_offset<BITS, XT>(c.w[i], t);
         const float off = 128.f + (float)zero_of(c.rec[i][0]);
-        acc[0][i] += scale_at(c.rec[i][0], c.s32[i][0]) * (tmp - off * sx);
+        const float sc = scale_at(c.rec[i][0], c.s32[i][0]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const f32x4 sx = *reinterpret_cast<const f32x4*>(xs2 + (kc * MT + m) * 16 + 4 * q);
+          f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) tmp = mfma16<XT>(xc.xa[m][t], b[t], tmp);
+          acc[m][i] += sc * (tmp - off * sx);
+        }
       }
     } else if constexpr (ONE) {
       const float sx = xsum[kc - kc0];
@@ -329,7 +341,7 @@ skinny_kernel(const SkinnyArgs a) {
   const int rot = (TCH > 0 && PH == 1) ? (ct0 * 5) & (TCH - 1) : 0;
   const int kch = Kxs >> 7;                     // chunks per copy phase
   auto chunk_at = [&](int j) {
-    if constexpr (PH == 2) return (j < TCH / 2 ? 0 : kch) + ks * (TCH / 2) + (j & (TCH / 2 - 1));
+    if constexpr (PH > 1) return (j / (TCH / PH)) * kch + ks * (TCH / PH) + (j % (TCH / PH));
     return kc0 + ((j + rot) & (TCH > 0 ? TCH - 1 : 0));
   };
   // the copy form's copy of phase h (inputs h * Kxs .. (h + 1) * Kxs - 1 of every row, zeros past
@@ -365,10 +377,13 @@ skinny_kernel(const SkinnyArgs a) {
       for (int kc = wave; kc < kch; kc += nwaves) {   // padding chunks: sums of zeros
         XChunk xc;
         load_x_lds(kc, xc);
-        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v = mfma16<XT>(xc.xa[0][t], ones, v);
-        if (col == 0) *reinterpret_cast<f32x4*>(xs2 + kc * 16 + 4 * q) = v;
+        for (int m = 0; m < MT; ++m) {
+          f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v = mfma16<XT>(xc.xa[m][t], ones, v);
+          if (col == 0) *reinterpret_cast<f32x4*>(xs2 + (kc * MT + m) * 16 + 4 * q) = v;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -467,22 +482,22 @@ skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
     for (int j = 0; j < TCH; ++j) {
       const int kc = chunk_at(j);
-      const int kcl = (PH == 2 && j >= TCH / 2) ? kc - kch : kc;   // chunk within the staged copy
-      if constexpr (PH == 2) {
-        if (j == TCH / 2) {
-          // the first half's sums are complete here (otherwise the compiler sinks them past the
-          // copy below, to their use at the end, and keeps every chunk's partial live until then)
+      const int kcl = PH > 1 ? kc - (j / (TCH / PH)) * kch : kc;   // chunk within the staged copy
+      if constexpr (PH > 1) {
+        if (j > 0 && j % (TCH / PH) == 0) {
+          // the sums so far are complete here (otherwise the compiler sinks them past the copy
+          // below, to their use at the end, and keeps every chunk's partial live until then)
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int i = 0; i < TW; ++i) asm volatile("" : "+v"(acc[m][i]));
-          // every wave is done with the first half before the second replaces it (LDS-only fence:
-          // the weights in flight are not waited for here)
+          // every wave is done with this part before the next replaces it (LDS-only fence: the
+          // weights in flight are not waited for here)
           __builtin_amdgcn_sched_barrier(0);
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-          copy_issue(1);
+          copy_issue(j / (TCH / PH));
           copy_finish(false);
         }
       }
@@ -517,6 +532,7 @@ skinny_kernel(const SkinnyArgs a) {
 
   // ---- reduce the KSPLIT partial sums of each column group, then store ---------------------
   if constexpr (RTK || KSPLIT > 1) {
+    if constexpr (XLDS == 3) __syncthreads();   // every wave is done with the copy the slots reuse
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -614,28 +630,42 @@ inline bool skinny_m1_act_rule(int64_t M, int Kp, int seg_steps, bool has_iperm)
 // above 8 rows).
 struct CopyPlan {
   bool ok;
-  int T, nks, cgs, ph;     // ph = 2: x copied in two halves of the inputs
-  size_t lds;              // dynamic LDS: the rows, and the per-(chunk, row) sums of the offset form
+  int T, nks, cgs, ph, mt;   // ph: copy phases (parts of the inputs); mt: 16-row blocks
+  size_t lds;                // dynamic LDS: the rows and the per-(chunk, row) sums of the offset
+                             // form, or the reduction slots that reuse them, whichever is larger
 };
-inline CopyPlan skinny_copy_plan(int64_t M, int KC, int CT, int bits, int seg_steps, bool has_perm) {
-  CopyPlan p{false, 0, 0, 0, 1, 0};
-  if (M < 2 || M > 16 || bits > 4 || seg_steps != 4 || has_perm) return p;
+inline CopyPlan skinny_copy_plan(int64_t M, int KC, int CT, int bits, int seg_steps, bool x_unsorted) {
+  CopyPlan p{false, 0, 0, 0, 1, 1, 0};
+  if (M < 2 || M > 32 || bits > 4 || seg_steps != 4 || x_unsorted) return p;
   if ((KC == 40 || KC == 48 || KC == 56) && M <= 8) return p;
   if (KC <= 32 && M <= 4) return p;
-  constexpr size_t kLds = 160 * 1024, kStatic = 16 * 1024;   // the reduction slots of 16 waves
-  for (int ph : {1, 2})
+  constexpr size_t kLds = 160 * 1024;
+  const int mt = M <= 16 ? 1 : 2;
+  for (int ph : {1, 2, 4}) {
+    if (mt == 1 && ph == 4) break;
     for (int T : {16, 32}) {
+      if (T < 4 * ph) continue;
       const int nks = (KC + T - 1) / T;
       const size_t Kxs = (size_t)nks * T * kChunkK / ph;      // inputs per staged row
-      const size_t lds = (size_t)M * (Kxs + 8) * 2 + Kxs / 2;
-      if (lds + kStatic > kLds) continue;
-      const int wpc = (lds + kStatic) * 2 <= kLds ? 2 : 1;
-      const int W = wpc == 1 ? 16 : 8;
-      int cgs = (CT + 256 * wpc - 1) / (256 * wpc);
-      cgs = cgs < 1 ? 1 : (cgs > W ? W : cgs);
-      const int nks_max = W / cgs > 0 ? W / cgs : 1;
-      if (nks <= nks_max) return CopyPlan{true, T, nks, cgs, ph, lds};
+      size_t lds = (size_t)M * (Kxs + 8) * 2 + (Kxs / kChunkK) * 16 * mt * 4;
+      const size_t red = (size_t)16 * mt * 4 * 64 * 4;         // 16 waves' slots, the worst case
+      if (lds < red) lds = red;
+      if (lds > kLds) continue;
+      // two workgroups per compute unit when two copies fit, else (or when that leaves fewer than
+      // four waves a workgroup) one
+      for (int wpc = lds * 2 <= kLds ? 2 : 1; wpc >= 1; --wpc) {
+        // (two row blocks: at most 8 waves, which leaves each of them 256 VGPRs)
+        const int W = mt == 2 ? 8 : (wpc == 1 ? 16 : 8);
+        int cgs = (CT + 256 * wpc - 1) / (256 * wpc);
+        cgs = cgs < 1 ? 1 : (cgs > W ? W : cgs);
+        const int nks_max = W / cgs > 0 ? W / cgs : 1;
+        // at least four waves a workgroup, and fewer padding chunks than real ones (2048 x 14336
+        // at M = 17: two waves of one 16-chunk range measured 12.3 us, four of 32 chunks half
+        // padding 13.5, against 9.6 for x read from L2)
+        if (nks <= nks_max && nks * cgs >= 4 && nks * T < 2 * KC) return CopyPlan{true, T, nks, cgs, ph, mt, lds};
+      }
     }
+  }
   return p;
 }
 // 2 <= M <= 16 on the same layers: the same waves of 16 chunks with x read from L2 per chunk, one
@@ -722,14 +752,14 @@ static hipError_t run_m1_act(const SkinnyArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BITS, int XT, int TCH, int F32S, int PH>
+template <int BITS, int XT, int TCH, int F32S, int PH, int MT>
 static hipError_t run_copy(const SkinnyArgs& a0, const CopyPlan& p, hipStream_t s) {
   constexpr int ONE = XT == 1 ? 2 : 0;
   SkinnyArgs a = a0;
   a.Kx = p.nks * TCH * kChunkK;
   a.cgs = p.cgs;
   const int blocks = (a.CT + p.cgs - 1) / p.cgs;
-  hipLaunchKernelGGL((skinny_kernel<BITS, XT, 1, 1, 0, 4, 3, 4, TCH, ONE, F32S, 2, 16, 1, 0, PH>), dim3(blocks),
+  hipLaunchKernelGGL((skinny_kernel<BITS, XT, MT, 1, 0, 4, 3, 4, TCH, ONE, F32S, 2, (MT == 1 ? 16 : 8), 1, 0, PH>), dim3(blocks),
                      dim3(64 * p.cgs * p.nks), p.lds, s, a);
   return hipGetLastError();
 }
@@ -768,9 +798,16 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
   if constexpr (BITS <= 4) {
     const CopyPlan cp = skinny_copy_plan(a.M, a.KC, a.CT, BITS, seg, a.iperm != nullptr);
     if (cp.ok) {
+      if (cp.mt == 1) {
+        if (cp.ph == 1)
+          return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 1, 1>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 1, 1>(a, cp, s);
+        return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 2, 1>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 2, 1>(a, cp, s);
+      }
       if (cp.ph == 1)
-        return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 1>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 1>(a, cp, s);
-      return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 2>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 2>(a, cp, s);
+        return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 1, 2>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 1, 2>(a, cp, s);
+      if (cp.ph == 2)
+        return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 2, 2>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 2, 2>(a, cp, s);
+      return cp.T == 16 ? run_copy<BITS, XT, 16, F32S, 4, 2>(a, cp, s) : run_copy<BITS, XT, 32, F32S, 4, 2>(a, cp, s);
     }
   }
   if (skinny_mx_long(a.M, a.KC, a.CT, seg, a.iperm != nullptr)) {
