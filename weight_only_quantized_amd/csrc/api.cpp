@@ -379,8 +379,9 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
     (void)hipFree(L->perm);
     L->perm = nullptr;
   } else if (Kp <= kIpermMaxKp) {
-    // 16-bit sorted positions for the one kernel that scatters x through them (LDS staging of a
-    // whole row, Kp <= 8192): half the bytes every workgroup reads before its first chunk
+    // 16-bit sorted positions for the kernels that scatter x through them (the skinny kernel's
+    // LDS staging of a whole row, where they halve the bytes every workgroup reads before its
+    // first chunk, and the prep's sorted copy); Kp <= 8192
     std::vector<uint16_t> ip(K);
     for (int j = 0; j < Kp; ++j)
       if (perm_host[j] >= 0) ip[perm_host[j]] = (uint16_t)j;

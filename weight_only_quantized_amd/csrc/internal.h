@@ -19,7 +19,8 @@ struct gptq_layer {
   uint32_t* scale32;  // [CT][G][16] f32 scale bits when scales_dtype is F32, else NULL
   int32_t* perm;      // [Kp]: original input index at each sorted position (-1 = padding)
   uint16_t* iperm;    // [K]: sorted position of each original input (act-order with Kp <= 8192
-                      // only: the skinny kernel's LDS staging, which holds x whole, is its one user)
+                      // only): the skinny kernel scatters x through it into LDS, the prep into
+                      // the workspace copy
   int64_t bytes;
 };
 
