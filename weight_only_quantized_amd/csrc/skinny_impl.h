@@ -100,7 +100,7 @@ skinny_kernel(const SkinnyArgs a) {
   static_assert(PH == 1 || ((PH == 2 || PH == 4) && XLDS == 3 && KSPLIT == 0 && TCH % (4 * PH) == 0),
                 "copy phases: the copy form's launch-set waves, at least four chunks per phase");
   static_assert(ONE != 2 || (MT <= 2 && SEG == 4 && XLDS == 3 && TCH > 0 && XT == 1 && BITS <= 4),
-                "the offset form for up to 16 rows needs whole-chunk segments, the workgroup's copy of x and "
+                "the offset form for up to 32 rows needs whole-chunk segments, the workgroup's copy of x and "
                 "an exact bf16 offset operand");
   constexpr bool RTK = KSPLIT == 0;             // waves per tile set at launch
   static_assert(!RTK || (TCH >= 4 && XLDS != 0), "launch-set K split: per-wave ranges, staged x");
@@ -612,22 +612,28 @@ inline int skinny_m1_chunks(int KC) { return KC <= 32 ? 4 : (KC <= 72 || KC % 16
 inline bool skinny_m1_act_rule(int64_t M, int Kp, int seg_steps, bool has_iperm) {
   return M == 1 && has_iperm && seg_steps == 4 && Kp <= kIpermMaxKp;
 }
-// 2 <= M <= 16, the copy form (XLDS = 3 with launch-set waves): each workgroup copies x[0:M, 0:Kx]
-// into LDS once (1 KB buffer_load ... lds pieces), cgs column groups of one tile each share it, and
-// a group's nks waves split K in ranges of T chunks (padding chunks past the layer read zeros);
-// bf16 x takes the offset form (128 + code, the -(128 + zero) * sum_k x correction from per-chunk,
-// per-row sums the workgroup takes once by MFMA against an all-ones operand).  Workgroups are sized
-// so that about one round of them fills the chip: one per compute unit when the copy takes more
-// than half of the LDS (up to 16 waves), two otherwise (up to 8); cgs = ceil(CT / (256 x that)),
-// T = 16 while that many waves fit, else 32.  Measured on MI355X against the previous dispatch (the
-// mid kernel's split K with its reduction launch, or x read from L2), us: 8192 x 28672 bf16 M = 2 /
-// 4 / 6 / 8: 26.4 / 27.9 / 28.8 / 30.1 -> 24.2 / 24.9 / 25.5 / 26.2; 4096 x 14336 fp16 M = 8 / 12 /
-// 16: 10.2 / 11.3 / 12.7 -> 9.5 / 9.9 / 10.4; 14336 x 4096 fp16 M = 2 / 4: 11.3 / 11.8 -> 8.7 /
-// 9.7; 8192 x 8192 fp16 M = 4: 11.9 -> 9.4.  Not taken: act-order (x would need
-// sorting), 8-bit codes, 32-input groups, 40 / 48 / 56 chunks at M <= 8 and up to 32 chunks at
-// M <= 4 (x read from L2 measured faster: 5120 x 13824 M = 4 / 5 11.5 against 12.2 / 12.3,
-// 4096 x 14336 M = 4 9.4 against 9.8), and copies that do not fit the LDS (the 8192-input layer
-// above 8 rows).
+// 2 <= M <= 32, the copy form (XLDS = 3 with launch-set waves): each workgroup copies x[0:M, 0:Kx]
+// into LDS (1 KB buffer_load ... lds pieces), in PH = 2 or 4 parts of the inputs when the whole rows
+// do not fit (each part replaces the previous one after a barrier); cgs column groups of one tile
+// each share it, and a group's nks waves split K in ranges of T chunks (padding chunks past the
+// layer read zeros).  17 to 32 rows are two 16-row blocks sharing every B operand (at most 8 waves:
+// the 16-wave bound leaves 128 VGPRs, which two blocks exceed).  bf16 x takes the offset form (128 +
+// code, the -(128 + zero) * sum_k x correction from per-chunk, per-row sums the workgroup takes
+// once per part by MFMA against an all-ones operand).  Workgroups are sized so that about one round
+// of them fills the chip: one per compute unit when the copy takes more than half of the LDS (up to
+// 16 waves, 8 with two row blocks), two otherwise (up to 8), and one when two would leave fewer than
+// four waves a workgroup; cgs = ceil(CT / (256 x workgroups per compute unit)), T = 16 while that
+// many waves fit, else 32; fewer padding chunks than real ones.  Measured on MI355X against the
+// previous dispatch (the mid kernel's split K with its reduction launch, or x read from L2), us:
+// 8192 x 28672 bf16 M = 2 / 4 / 6 / 8: 26.4 / 27.9 / 28.8 / 30.1 -> 24.2 / 24.9 / 25.5 / 26.2;
+// 4096 x 14336 fp16 M = 8 / 12 / 16: 10.2 / 11.3 / 12.7 -> 9.5 / 9.9 / 10.4, M = 17 / 32 (against
+// the tiled family) 15.0 / 16.7 -> 11.7 / 13.9; 14336 x 4096 fp16 M = 2 / 4: 11.3 / 11.8 -> 8.7 /
+// 9.7; 8192 x 8192 fp16 M = 4: 11.9 -> 9.4.  Act-order layers take it once their x is sorted into
+// the workspace (x_unsorted then false).  Not taken: 8-bit codes, 32-input groups, 40 / 48 / 56
+// chunks at M <= 8 and up to 32 chunks at M <= 4 (x read from L2 measured faster: 5120 x 13824
+// M = 4 / 5 11.5 against 12.2 / 12.3, 4096 x 14336 M = 4 9.4 against 9.8), and shapes for which
+// no part count fits the LDS with enough waves (the 8192-input layer at 20 to 32 rows over 1792
+// column tiles).
 struct CopyPlan {
   bool ok;
   int T, nks, cgs, ph, mt;   // ph: copy phases (parts of the inputs); mt: 16-row blocks
