@@ -140,6 +140,21 @@ def test_runtime_layout_map_is_a_bijection():
         os.remove(exe)
 
 
+def test_dispatch_plans_fit_their_kernels():
+    """Every form the skinny dispatch rules pick fits its kernel's LDS, wave bound, copy pieces and
+    instantiated chunk and part counts (tests/plan_check.cpp over rows 0..64, chunks 1..160 and a
+    spread of column-tile counts)."""
+    exe = os.path.join("/tmp", f"gq_plan_check_{os.getpid()}")
+    src = os.path.join(ROOT, "tests", "plan_check.cpp")
+    inc = os.path.join(ROOT, "weight_only_quantized_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", inc, src, "-o", exe], check=True)
+    try:
+        out = subprocess.run([exe], capture_output=True, text=True)
+        assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+    finally:
+        os.remove(exe)
+
+
 def test_bias_patterns_are_the_stated_values():
     # dequant.h feeds -bias as raw 16-bit patterns; check them against numpy's conversions
     text = open(os.path.join(ROOT, "weight_only_quantized_amd", "csrc", "dequant.h")).read()

@@ -1,0 +1,142 @@
+// Rules of the skinny family's dispatch (skinny_impl.h launches what they pick): plain host C++
+// over the layer's shape, so that a host build can check them (tests/plan_check.cpp).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace gq {
+
+constexpr int kXLdsMax = 64 * 1024;   // dynamic LDS budget for staged x
+
+// True when x for this call can be staged in LDS (small M): the call then needs no workspace.
+// The staging holds at most 4 pieces of 8 inputs per thread (M * Kp <= 8192).
+inline bool x_fits_lds(int64_t M, int Kp) {
+  // (with M * Kp <= 8192, a wave's share (M + 1) * 16 * ceil(Kp / 512) is at most 512 pieces)
+  return M <= 4 && M * (int64_t)Kp <= 4 * 8 * 256 && (M + 1) * (int64_t)(Kp + 8) * 2 <= kXLdsMax &&
+         (M + 1) * 16 * ((Kp / 128 + 3) / 4) <= 512;
+}
+
+// M = 1 without act-order, whole-chunk groups, up to 128 chunks (16384 inputs): one column tile per
+// workgroup, whose ceil(KC / T) waves each stage their own T chunks of x in LDS and stream those
+// chunks' weights (T = 4 or 8: every load in flight at once; T = 16: four chunks in flight); the
+// last wave's chunks past the layer are padding (zeros).  A rule, not a table: any K in range takes
+// it.  T = 4 up to 32 chunks, 8 up to 72 chunks or when the chunk count is not a multiple of 16,
+// else 16.  Measured on MI355X (us, interleaved on one device): 4096 x 14336 7.69 -> 7.44 against two
+// waves of 16 chunks; 8192 x 28672 bf16 22.2 -> 20.46 against four waves of 16; T = 8 vs 16:
+// 9216 x 8192 9.38 / 9.71, 11008 x 4096 6.82 / 7.43, 12288 x 8192 10.68 / 11.07 (the one layer the
+// rule gives away), 10240 x 8192 9.90 / 9.32, 14336 x 4096 7.94 / 7.73, 16384 x 8192 15.0 / 13.9;
+// layers between the exact sizes the previous dispatch knew no longer fall to the split-K mid
+// kernel (9216 x 8192: 14.1 -> 9.4; 11008 x 4096: 10.7 -> 6.9).
+constexpr int kM1MaxChunks = 128;
+inline bool skinny_m1_rule(int64_t M, int KC, int seg_steps, bool has_perm) {
+  return M == 1 && !has_perm && seg_steps == 4 && KC <= kM1MaxChunks;
+}
+inline int skinny_m1_chunks(int KC) { return KC <= 32 ? 4 : (KC <= 72 || KC % 16 != 0 ? 8 : 16); }
+// M = 1 with act-order, whole-chunk groups and x staged whole (Kp <= 8192): the same launch-set
+// waves, the workgroup scattering x into sorted order through the 16-bit inverse permutation (whose
+// within-group order the repack chose so that each scatter instruction hits distinct LDS banks)
+// and meeting at one barrier; four chunks in flight per wave.  T = 4 up to 32 chunks, else 16 for
+// 4-bit codes and 8 otherwise.  Measured on MI355X, 8192 x 8192, fp16 x, us (the identity-order
+// gs = -1 layer of the same width in parentheses): 2-bit 8.6 -> 7.49 (7.10), 3-bit 9.2 -> 8.13
+// (7.57), 4-bit 8.9 -> 8.34 (8.01), 8-bit 13.2 -> 12.7 (12.2); before, four waves of 16 chunks
+// scattered through a 32-bit inverse permutation in the stable order (about 13 bank-conflict cycles
+// per 2-byte LDS write instruction, rocprofv3 SQ_LDS_BANK_CONFLICT) and met at a barrier that also
+// waited for every weight load in flight.
+inline bool skinny_m1_act_rule(int64_t M, int Kp, int seg_steps, bool has_iperm) {
+  return M == 1 && has_iperm && seg_steps == 4 && Kp <= kIpermMaxKp;
+}
+// 2 <= M <= 32, the copy form (XLDS = 3 with launch-set waves): each workgroup copies x[0:M, 0:Kx]
+// into LDS (1 KB buffer_load ... lds pieces), in PH = 2 or 4 parts of the inputs when the whole rows
+// do not fit (each part replaces the previous one after a barrier); cgs column groups of one tile
+// each share it, and a group's nks waves split K in ranges of T chunks (padding chunks past the
+// layer read zeros).  17 to 32 rows are two 16-row blocks sharing every B operand (at most 8 waves:
+// the 16-wave bound leaves 128 VGPRs, which two blocks exceed).  bf16 x takes the offset form (128 +
+// code, the -(128 + zero) * sum_k x correction from per-chunk, per-row sums the workgroup takes
+// once per part by MFMA against an all-ones operand).  Workgroups are sized so that about one round
+// of them fills the chip: one per compute unit when the copy takes more than half of the LDS (up to
+// 16 waves, 8 with two row blocks), two otherwise (up to 8), and one when two would leave fewer than
+// four waves a workgroup; cgs = ceil(CT / (256 x workgroups per compute unit)), T = 16 while that
+// many waves fit, else 32; fewer padding chunks than real ones.  Measured on MI355X against the
+// previous dispatch (the mid kernel's split K with its reduction launch, or x read from L2), us:
+// 8192 x 28672 bf16 M = 2 / 4 / 6 / 8: 26.4 / 27.9 / 28.8 / 30.1 -> 24.2 / 24.9 / 25.5 / 26.2;
+// 4096 x 14336 fp16 M = 8 / 12 / 16: 10.2 / 11.3 / 12.7 -> 9.5 / 9.9 / 10.4, M = 17 / 32 (against
+// the tiled family) 15.0 / 16.7 -> 11.7 / 13.9; 14336 x 4096 fp16 M = 2 / 4: 11.3 / 11.8 -> 8.7 /
+// 9.7; 8192 x 8192 fp16 M = 4: 11.9 -> 9.4.  Act-order layers take it once their x is sorted into
+// the workspace (x_unsorted then false).  Not taken: 8-bit codes, 32-input groups, 40 / 48 / 56
+// chunks at M <= 8 and up to 32 chunks at M <= 4 (x read from L2 measured faster: 5120 x 13824
+// M = 4 / 5 11.5 against 12.2 / 12.3, 4096 x 14336 M = 4 9.4 against 9.8), and shapes for which
+// no part count fits the LDS with enough waves (the 8192-input layer at 20 to 32 rows over 1792
+// column tiles).
+struct CopyPlan {
+  bool ok;
+  int T, nks, cgs, ph, mt;   // ph: copy phases (parts of the inputs); mt: 16-row blocks
+  size_t lds;                // dynamic LDS: the rows and the per-(chunk, row) sums of the offset
+                             // form, or the reduction slots that reuse them, whichever is larger
+};
+inline CopyPlan skinny_copy_plan(int64_t M, int KC, int CT, int bits, int seg_steps, bool x_unsorted) {
+  CopyPlan p{false, 0, 0, 0, 1, 1, 0};
+  if (M < 2 || M > 32 || bits > 4 || seg_steps != 4 || x_unsorted) return p;
+  if ((KC == 40 || KC == 48 || KC == 56) && M <= 8) return p;
+  if (KC <= 32 && M <= 4) return p;
+  constexpr size_t kLds = 160 * 1024;
+  const int mt = M <= 16 ? 1 : 2;
+  for (int ph : {1, 2, 4}) {
+    if (mt == 1 && ph == 4) break;
+    for (int T : {16, 32}) {
+      if (T < 4 * ph) continue;
+      const int nks = (KC + T - 1) / T;
+      const size_t Kxs = (size_t)nks * T * kChunkK / ph;      // inputs per staged row
+      size_t lds = (size_t)M * (Kxs + 8) * 2 + (Kxs / kChunkK) * 16 * mt * 4;
+      const size_t red = (size_t)16 * mt * 4 * 64 * 4;         // 16 waves' slots, the worst case
+      if (lds < red) lds = red;
+      if (lds > kLds) continue;
+      // two workgroups per compute unit when two copies fit, else (or when that leaves fewer than
+      // four waves a workgroup) one
+      for (int wpc = lds * 2 <= kLds ? 2 : 1; wpc >= 1; --wpc) {
+        // (two row blocks: at most 8 waves, which leaves each of them 256 VGPRs)
+        const int W = mt == 2 ? 8 : (wpc == 1 ? 16 : 8);
+        int cgs = (CT + 256 * wpc - 1) / (256 * wpc);
+        cgs = cgs < 1 ? 1 : (cgs > W ? W : cgs);
+        const int nks_max = W / cgs > 0 ? W / cgs : 1;
+        // at least four waves a workgroup, and fewer padding chunks than real ones (2048 x 14336
+        // at M = 17: two waves of one 16-chunk range measured 12.3 us, four of 32 chunks half
+        // padding 13.5, against 9.6 for x read from L2)
+        if (nks <= nks_max && nks * cgs >= 4 && nks * T < 2 * KC) return CopyPlan{true, T, nks, cgs, ph, mt, lds};
+      }
+    }
+  }
+  return p;
+}
+// 2 <= M <= 16 on the same layers: the same waves of 16 chunks with x read from L2 per chunk, one
+// column tile per wave below 512 column tiles and two from 512 (enough workgroups either way).
+// Measured on MI355X against the mid kernel / the tiled family (us): 14336 x 4096, M = 2 / 4 / 8 /
+// 12: 9.7 / 10.3 / 12.0 / 14.5 against 14.4 / 14.4 / 14.8 / 15.3; 12288 x 8192, M = 2 / 8 / 16:
+// 13.4 / 14.6 / 18.2 against 16.0 / 19.3 / 20.5.  (At 13 to 16 rows on fewer than 512 column tiles
+// the tiled family measured faster.)
+// 5120 / 6144 / 7168 inputs (40 / 48 / 56 chunks): five to seven waves of 8 chunks, up to M = 8
+// (5120 x 5120 M = 2 / 4 / 8: 8.8 / 9.6 / 9.8 -> 7.5 / 8.0 / 9.4 us; 7168 x 20480 M = 8: 24.5 ->
+// 23.1 us; slower than the mid kernel from 12 rows).
+inline bool skinny_mx_long(int64_t M, int KC, int CT, int seg_steps, bool has_perm) {
+  if (M < 2 || has_perm || seg_steps != 4) return false;
+  if (KC == 40 || KC == 48 || KC == 56) return M <= 8;
+  return M <= (CT >= 512 ? 16 : 12) && (KC == 80 || KC == 96 || KC == 112);
+}
+
+// The other case the skinny kernel keeps: x read from L2 per chunk, for M <= 16 over at most 32
+// chunks of K, for M <= 4 at any K when the layer has at least 1024 column tiles (enough workgroups
+// for its long per-wave ranges), and for 17 <= M <= 32 (two 16-row blocks) while M * KC <= 640.
+// Measured on MI355X: faster there than the mid family's split K (8192 x 28672, M = 2 / 3 / 4:
+// 28.3 / 29.5 / 30.7 us against 30.1 / 30.5 / 31.2) and than the tiled family (2048 x 14336,
+// M = 17 / 32: 9.5 / 12.6 us against 15.0 / 17.3; 4096 x 14336, M = 17 / 20: 15.6 / 16.9 against
+// 17.4 / 17.1); slower beyond (14336 x 4096, 256 column tiles, M = 1: 29.3 us against the mid
+// kernel's 13.4).
+// (The two-block form is built for whole-chunk groups and 3/4/8-bit codes: with 2-bit codes or
+// 32-input groups it does not fit its registers.)
+inline bool skinny_reads_x_from_l2(int64_t M, int KC, int CT, int bits, int seg_steps) {
+  return (M <= 16 && (KC <= 32 || (M <= 4 && CT >= 1024))) ||
+         (M > 16 && M <= 32 && M * KC <= 640 && bits != 2 && seg_steps == 4);
+}
+
+}  // namespace gq
