@@ -60,8 +60,8 @@ def algorithmic_bytes(K, N, M, bits, gs, desc_act, scale_bytes=2, act_bytes=2):
 
 # Sources that make up each measured kernel family (its own files plus the shared headers).
 SHARED_SOURCES = ["bufmem.h", "dequant.h", "internal.h", "layout.h"]
-FAMILY_SOURCES = {"skinny": ["skinny_impl.h", "skinny_plan.h", "skinny.hip", "skinny_b4.hip"],
-                  "tiled": ["tiled.hip"]}
+FAMILY_SOURCES = {"skinny": ["skinny_impl.h", "plans.h", "skinny.hip", "skinny_b4.hip"],
+                  "tiled": ["tiled.hip", "plans.h"]}
 
 
 def csrc_digest(family):

@@ -1,13 +1,17 @@
-// Host check of the skinny family's dispatch rules (weight_only_quantized_amd/csrc/skinny_plan.h):
-// over every row count up to 64, every chunk count up to 160 and a spread of column-tile counts,
-// every form a rule picks must fit what its kernel assumes -- the LDS of one workgroup, the wave
-// bound it was built for, whole 1 KB copy pieces, every wave holding at least one real chunk, and
-// the part counts and chunk counts the kernels are instantiated with.  Built with g++ by
-// tests/test_boundary_cpu.py; prints "ok" on success.
+// Host check of the launch plans (weight_only_quantized_amd/csrc/plans.h).  Skinny family, over
+// every row count up to 64, every chunk count up to 160 and a spread of column-tile counts: every
+// form a rule picks must fit what its kernel assumes -- the LDS of one workgroup, the wave bound it
+// was built for, whole 1 KB copy pieces, every wave holding at least one real chunk, and the part
+// and chunk counts the kernels are instantiated with.  Mid kernel: an instantiated (row blocks,
+// chunks per slice) pair, slices covering K exactly once, the slice's x within 64 KB of LDS.
+// Tiled family, up to 65536 rows: a tile of the table, slices covering K exactly once with at
+// least four chunks each when K is split, split partial sums addressable by 32-bit offsets, and a
+// grid within the launch limit.  Built with g++ by tests/test_boundary_cpu.py; prints "ok" on
+// success.
 #include <cstdio>
 #include <initializer_list>
 
-#include "skinny_plan.h"
+#include "plans.h"
 
 static int fail(const char* what, long M, int KC, int CT, int bits, int seg, int uns) {
   printf("%s: M=%ld KC=%d CT=%d bits=%d seg=%d unsorted=%d\n", what, M, KC, CT, bits, seg, uns);
@@ -65,6 +69,40 @@ int main() {
                 if (M > 4 || (M + 1) * (long)(Kp + 8) * 2 > gq::kXLdsMax) return fail("staged x", M, KC, CT, bits, seg, uns);
               }
             }
+  // mid kernel
+  for (long M = 1; M <= 64; ++M)
+    for (int KC = 1; KC <= 512; KC += (KC < 160 ? 1 : 7))
+      for (int CT : cts)
+        for (int seg : {1, 4}) {
+          const gq::MidPlan p = gq::mid_plan_of(M, KC, CT, seg);
+          const long rows = M < gq::mid_rows_per_pass_of(seg) ? M : gq::mid_rows_per_pass_of(seg);
+          const bool built = seg == 4 ? ((p.MT == 1 && (p.cpw == 16 || p.cpw == 8 || p.cpw == 4)) ||
+                                          (p.MT == 2 && (p.cpw == 8 || p.cpw == 4)) || (p.MT == 4 && p.cpw == 4))
+                                       : (p.cpw == 4 && (p.MT == 1 || p.MT == 2));
+          if (!built) return fail("mid: configuration not built", M, KC, CT, 0, seg, 0);
+          if (16L * p.MT < rows || (p.MT > 1 && 16L * (p.MT / 2) >= rows)) return fail("mid: row blocks", M, KC, CT, 0, seg, 0);
+          if ((long)p.KS * p.cpw < KC || (long)(p.KS - 1) * p.cpw >= KC) return fail("mid: slices", M, KC, CT, 0, seg, 0);
+          if ((long)p.cpw * 16 * p.MT * 256 > 64 * 1024) return fail("mid: LDS", M, KC, CT, 0, seg, 0);
+          if (p.KS > 65535) return fail("mid: grid", M, KC, CT, 0, seg, 0);
+        }
+  // tiled family
+  const long tms[] = {1, 2, 16, 17, 33, 64, 65, 100, 128, 129, 256, 257, 512, 513, 768, 1024, 2048, 4096, 8192, 65536};
+  const int tns[] = {32, 96, 256, 1024, 4096, 6144, 14336, 28672, 65536};
+  for (long M : tms)
+    for (int KC = 1; KC <= 512; KC += (KC < 40 ? 1 : 13))
+      for (int N : tns)
+        for (int bits : {2, 3, 4, 8})
+          for (int seg : {1, 4}) {
+            const int Kp = KC * gq::kChunkK, CT = N / 16;
+            const gq::TiledPlan p = gq::tiled_plan_of(M, Kp, N, bits, KC, CT, seg);
+            if (p.tile < 0 || p.tile >= gq::kNumTiles || (seg != 4 && p.tile != 1)) return fail("tiled: tile", M, KC, CT, bits, seg, 0);
+            if (p.KS < 1 || p.kcs < 1 || (long)p.KS * p.kcs < KC || (long)(p.KS - 1) * p.kcs >= KC) return fail("tiled: slices", M, KC, CT, bits, seg, 0);
+            if (p.KS > 1 && p.kcs < 4) return fail("tiled: slice shorter than four chunks", M, KC, CT, bits, seg, 0);
+            if (p.KS > 1 && M * (long)N * 4 > 2147483647L) return fail("tiled: partial sums past 32-bit offsets", M, KC, CT, bits, seg, 0);
+            const gq::TileShape& ts = gq::kTiles[p.tile];
+            const long blocks = ((M + 16 * ts.WM - 1) / (16 * ts.WM)) * ((CT + ts.NW * ts.WN - 1) / (ts.NW * ts.WN)) * p.KS;
+            if (blocks < 1 || blocks > 2147483647L) return fail("tiled: grid", M, KC, CT, bits, seg, 0);
+          }
   if (plans == 0 || m1 == 0) { printf("no plans\n"); return 1; }
   printf("ok\n");
   return 0;

@@ -24,6 +24,7 @@
 #include "bufmem.h"
 #include "dequant.h"
 #include "internal.h"
+#include "plans.h"
 
 namespace gq {
 
@@ -221,37 +222,9 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   }
 }
 
-// Shape of one mid call: row blocks, K slices and chunks per slice.
-struct MidPlan {
-  int MT;       // 16-row blocks held (1, 2 or 4)
-  int KS;       // K slices (workgroups along K)
-  int cpw;      // chunks per slice: 4, 8 or 16
-};
-constexpr int kMidNW = 4, kMidWN = 2;          // four waves of two column tiles: 128 columns
-
-// Slices of 16, 8 or 4 chunks (x of one slice: cpw * MT * 4 KB <= 64 KB of LDS), the longest that
-// still gives two workgroups per compute unit (longer slices stream behind a 2-chunk ring; at four
-// workgroups per compute unit the 4-chunk slices loaded everything before computing, 13-16 %
-// slower on the act-order 8192 x 8192, M = 32 layer).
-// Rows per pass: all of M, except 32 for 32-input segments (whose four-row-block variant would
-// not fit in registers).
-inline int64_t mid_rows_per_pass(const gptq_layer* L) { return L->seg_steps == 4 ? 64 : 32; }
-
-inline MidPlan mid_plan(const gptq_layer* L, int64_t M) {
-  MidPlan p;
-  if (M > mid_rows_per_pass(L)) M = mid_rows_per_pass(L);
-  p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const int nbk = (L->CT + kMidNW * kMidWN - 1) / (kMidNW * kMidWN);
-  // one row block starts from 8-chunk slices while that keeps K in at most 8 slices, else from 16
-  // (MI355X, bf16 x, M = 8 / 16: the 8192 x 28672 layer 33.4 / 35.1 us with 16-chunk slices,
-  // 30.8 / 32.6 with 8; the 28672 x 8192 layer 30.8 / 33.2 with 16, 32.5 / 33.8 with 8, whose 28
-  // slices the reduction then adds)
-  int cpw = L->seg_steps == 4 ? (p.MT == 1 ? (L->KC > 64 ? 16 : 8) : 8 / (p.MT / 2)) : 4;
-  while (cpw > 4 && (int64_t)nbk * ((L->KC + cpw - 1) / cpw) < 2 * 256) cpw /= 2;
-  p.cpw = cpw;
-  p.KS = (L->KC + cpw - 1) / cpw;
-  return p;
-}
+// (the mid plan: plans.h)
+inline int64_t mid_rows_per_pass(const gptq_layer* L) { return mid_rows_per_pass_of(L->seg_steps); }
+inline MidPlan mid_plan(const gptq_layer* L, int64_t M) { return mid_plan_of(M, L->KC, L->CT, L->seg_steps); }
 
 template <int BITS, int XT, int MT, int SEG, int TCH, int F32S>
 static hipError_t run_mid_cfg(const MidArgs& a, int KS, hipStream_t s) {

@@ -1,5 +1,7 @@
-// Rules of the skinny family's dispatch (skinny_impl.h launches what they pick): plain host C++
-// over the layer's shape, so that a host build can check them (tests/plan_check.cpp).
+// Launch plans of the three kernel families, as functions of the layer's shape and the row count:
+// the skinny family's forms (skinny_impl.h launches what they pick), the mid kernel's K slices
+// (mid_impl.h) and the tiled family's tile and K split (tiled.hip).  Plain host C++, so that a host
+// build can check them (tests/plan_check.cpp).
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -137,6 +139,110 @@ inline bool skinny_mx_long(int64_t M, int KC, int CT, int seg_steps, bool has_pe
 inline bool skinny_reads_x_from_l2(int64_t M, int KC, int CT, int bits, int seg_steps) {
   return (M <= 16 && (KC <= 32 || (M <= 4 && CT >= 1024))) ||
          (M > 16 && M <= 32 && M * KC <= 640 && bits != 2 && seg_steps == 4);
+}
+
+
+// ---- mid family ------------------------------------------------------------------------------
+// Shape of one mid call: row blocks, K slices and chunks per slice.
+struct MidPlan {
+  int MT;       // 16-row blocks held (1, 2 or 4)
+  int KS;       // K slices (workgroups along K)
+  int cpw;      // chunks per slice: 4, 8 or 16
+};
+constexpr int kMidNW = 4, kMidWN = 2;          // four waves of two column tiles: 128 columns
+
+// Slices of 16, 8 or 4 chunks (x of one slice: cpw * MT * 4 KB <= 64 KB of LDS), the longest that
+// still gives two workgroups per compute unit (longer slices stream behind a 2-chunk ring; at four
+// workgroups per compute unit the 4-chunk slices loaded everything before computing, 13-16 %
+// slower on the act-order 8192 x 8192, M = 32 layer).
+// Rows per pass: all of M, except 32 for 32-input segments (whose four-row-block variant would
+// not fit in registers).
+inline int64_t mid_rows_per_pass_of(int seg_steps) { return seg_steps == 4 ? 64 : 32; }
+
+inline MidPlan mid_plan_of(int64_t M, int KC, int CT, int seg_steps) {
+  MidPlan p;
+  if (M > mid_rows_per_pass_of(seg_steps)) M = mid_rows_per_pass_of(seg_steps);
+  p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int nbk = (CT + kMidNW * kMidWN - 1) / (kMidNW * kMidWN);
+  // one row block starts from 8-chunk slices while that keeps K in at most 8 slices, else from 16
+  // (MI355X, bf16 x, M = 8 / 16: the 8192 x 28672 layer 33.4 / 35.1 us with 16-chunk slices,
+  // 30.8 / 32.6 with 8; the 28672 x 8192 layer 30.8 / 33.2 with 16, 32.5 / 33.8 with 8, whose 28
+  // slices the reduction then adds)
+  int cpw = seg_steps == 4 ? (p.MT == 1 ? (KC > 64 ? 16 : 8) : 8 / (p.MT / 2)) : 4;
+  while (cpw > 4 && (int64_t)nbk * ((KC + cpw - 1) / cpw) < 2 * 256) cpw /= 2;
+  p.cpw = cpw;
+  p.KS = (KC + cpw - 1) / cpw;
+  return p;
+}
+
+
+// ---- tiled family ----------------------------------------------------------------------------
+// Tile table: (rows, columns) of a workgroup tile, its wave tile and wave count.
+struct TileShape { int WM, WN, NW; };
+constexpr TileShape kTiles[] = {
+  {16, 2, 8},   // 0: 256 x 256, wave 256 x 32
+  {8, 1, 8},    // 1: 128 x 128, wave 128 x 16 (also every 32-input-segment layer)
+  {8, 2, 4},    // 2: 128 x 128, wave 128 x 32
+  {4, 2, 4},    // 3:  64 x 128, wave  64 x 32
+  {8, 2, 8},    // 4: 128 x 256, wave 128 x 32
+  {4, 2, 4},    // 5:  64 x 128 as 3, two chunks in flight
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+struct TiledPlan { int tile, KS, kcs; };
+
+inline int64_t tiles_of(int64_t M, int CT, int t) {
+  const TileShape& ts = kTiles[t];
+  return ((M + 16 * ts.WM - 1) / (16 * ts.WM)) * ((CT + ts.NW * ts.WN - 1) / (ts.NW * ts.WN));
+}
+
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Tile and K split of a call: an M-bucketed tile table as in "Formats and kernels ...", section
+// "Tile tables, and what happens when your shape does not fit", re-derived for gfx950 from a sweep
+// of every tile and split on MI355X (4-bit g128, 4096 x 14336 and 8192 x 28672 layers, M = 4 ..
+// 1024): a call runs best with about one eight-wave workgroup (or two four-wave ones) per compute
+// unit, from the largest tile that gets there, and splits K only as far as needed to get there:
+//   * M <= 64: the 64 x 128 tile, K split up to ~448 workgroups;
+//   * M <= 512 on layers of at most 4096 inputs whose 64-row blocks together read at most 128 MB
+//     of packed weights (the repeated passes then come from the Infinity Cache): the 64 x 128
+//     tile too, K split in two below ~192 tiles (4096 x 6144, M = 128 / 512: 24.3 / 52.7 us with
+//     the tiles below against 19.1 / 36.7; 4096 x 14336, M = 256: 43.3 against 39.5; longer K or
+//     more weight passes measured slower: 14336 x 4096 M = 128 31.2 against 45.3, 8192 x 28672
+//     M = 256 120.4 against 148.7);
+//   * larger M: the 256 x 256 tile once it alone gives ~192 workgroups, else the 128 x 256 tile,
+//     K split up to ~224 workgroups when it gives fewer than ~150;
+//   * 32-input segments: the 128 x 128 tile (wave 128 x 16), split the same way.
+// Split K only while one slice of partial sums stays addressable by 32-bit offsets and the rows
+// are one launch (14336 x 4096 at M = 1024, the 128 x 256 tile unsplit: 179 us; an earlier fixed
+// 768-row limit had kept such calls unsplit).
+inline TiledPlan tiled_plan_of(int64_t M, int Kp, int N, int bits, int KC, int CT, int seg_steps) {
+  TiledPlan p;
+  p.KS = 1;
+  const int64_t wbytes = (int64_t)Kp * N * bits / 8;     // packed codes of the layer
+  const int64_t mb64 = (M + 63) / 64;                            // 64-row blocks
+  if (seg_steps != 4) {
+    p.tile = 1;
+  } else if (M <= 64) {
+    p.tile = 5;
+  } else if (M <= 512 && KC <= 32 && mb64 * wbytes <= (int64_t(128) << 20)) {
+    p.tile = 5;       // short K, and every 64-row block's pass over the weights fits the MALL
+  } else if (tiles_of(M, CT, 0) >= 192) {
+    p.tile = 0;
+  } else {
+    p.tile = 4;
+  }
+  const int64_t t = tiles_of(M, CT, p.tile);
+  if (p.tile == 5 && M > 64) p.KS = t >= 192 ? 1 : 2;
+  else if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
+  else if (t < 150) p.KS = ceil_div(224, t);
+  // one row slice of launch_tiled (x and y offsets below 2^31) must hold all M rows
+  const int64_t row_slice = ((int64_t(1) << 31) - 1) / (2 * (int64_t)(Kp > N ? Kp : N)) / 256 * 256;
+  if (p.KS > 1 && (M * (int64_t)N * 4 > (int64_t)INT32_MAX || M > row_slice)) p.KS = 1;
+  if (p.KS > KC / 4) p.KS = KC / 4 > 1 ? KC / 4 : 1;     // at least four chunks per slice
+  p.kcs = (KC + p.KS - 1) / p.KS;
+  p.KS = (KC + p.kcs - 1) / p.kcs;
+  return p;
 }
 
 }  // namespace gq

@@ -21,7 +21,7 @@
 #include "bufmem.h"
 #include "dequant.h"
 #include "internal.h"
-#include "skinny_plan.h"
+#include "plans.h"
 
 namespace gq {
 
@@ -574,7 +574,7 @@ skinny_kernel(const SkinnyArgs a) {
 // ------------------------------------------------------------------------------------------------
 // Dispatch of one bit width (instantiated in skinny_b<bits>.hip)
 // ------------------------------------------------------------------------------------------------
-// (the rules that pick a form: skinny_plan.h)
+// (the rules that pick a form: plans.h)
 
 template <int BITS, int XT, int MT, int TW, int KSPLIT, int XLDS, int DEPTH, int TCH, int ONE, int F32S,
           int SEG1 = 1,   // SEG1 = 0: whole-chunk groups only (no 32-input-segment kernel is built)

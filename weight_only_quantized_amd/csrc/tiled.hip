@@ -38,6 +38,7 @@
 #include "bufmem.h"
 #include "dequant.h"
 #include "internal.h"
+#include "plans.h"
 #include "skinny_impl.h"
 
 namespace gq {
@@ -563,72 +564,9 @@ static hipError_t run_tiled(const TiledArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile table: (rows, columns) of a workgroup tile, its wave tile and wave count.
-struct TileShape { int WM, WN, NW; };
-constexpr TileShape kTiles[] = {
-  {16, 2, 8},   // 0: 256 x 256, wave 256 x 32
-  {8, 1, 8},    // 1: 128 x 128, wave 128 x 16 (also every 32-input-segment layer)
-  {8, 2, 4},    // 2: 128 x 128, wave 128 x 32
-  {4, 2, 4},    // 3:  64 x 128, wave  64 x 32
-  {8, 2, 8},    // 4: 128 x 256, wave 128 x 32
-  {4, 2, 4},    // 5:  64 x 128 as 3, two chunks in flight
-};
-constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
-
-struct TiledPlan { int tile, KS, kcs; };
-
-static int64_t tiles_of(const gptq_layer* L, int64_t M, int t) {
-  const TileShape& ts = kTiles[t];
-  return ((M + 16 * ts.WM - 1) / (16 * ts.WM)) * ((L->CT + ts.NW * ts.WN - 1) / (ts.NW * ts.WN));
-}
-
-static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
-// Tile and K split of a call: an M-bucketed tile table as in "Formats and kernels ...", section
-// "Tile tables, and what happens when your shape does not fit", re-derived for gfx950 from a sweep
-// of every tile and split on MI355X (4-bit g128, 4096 x 14336 and 8192 x 28672 layers, M = 4 ..
-// 1024): a call runs best with about one eight-wave workgroup (or two four-wave ones) per compute
-// unit, from the largest tile that gets there, and splits K only as far as needed to get there:
-//   * M <= 64: the 64 x 128 tile, K split up to ~448 workgroups;
-//   * M <= 512 on layers of at most 4096 inputs whose 64-row blocks together read at most 128 MB
-//     of packed weights (the repeated passes then come from the Infinity Cache): the 64 x 128
-//     tile too, K split in two below ~192 tiles (4096 x 6144, M = 128 / 512: 24.3 / 52.7 us with
-//     the tiles below against 19.1 / 36.7; 4096 x 14336, M = 256: 43.3 against 39.5; longer K or
-//     more weight passes measured slower: 14336 x 4096 M = 128 31.2 against 45.3, 8192 x 28672
-//     M = 256 120.4 against 148.7);
-//   * larger M: the 256 x 256 tile once it alone gives ~192 workgroups, else the 128 x 256 tile,
-//     K split up to ~224 workgroups when it gives fewer than ~150;
-//   * 32-input segments: the 128 x 128 tile (wave 128 x 16), split the same way.
-// Split K only while one slice of partial sums stays addressable by 32-bit offsets and the rows
-// are one launch (14336 x 4096 at M = 1024, the 128 x 256 tile unsplit: 179 us; an earlier fixed
-// 768-row limit had kept such calls unsplit).
+// (tile table and plan: plans.h)
 static TiledPlan tiled_plan(const gptq_layer* L, int64_t M) {
-  TiledPlan p;
-  p.KS = 1;
-  const int64_t wbytes = (int64_t)L->Kp * L->N * L->bits / 8;     // packed codes of the layer
-  const int64_t mb64 = (M + 63) / 64;                            // 64-row blocks
-  if (L->seg_steps != 4) {
-    p.tile = 1;
-  } else if (M <= 64) {
-    p.tile = 5;
-  } else if (M <= 512 && L->KC <= 32 && mb64 * wbytes <= (int64_t(128) << 20)) {
-    p.tile = 5;       // short K, and every 64-row block's pass over the weights fits the MALL
-  } else if (tiles_of(L, M, 0) >= 192) {
-    p.tile = 0;
-  } else {
-    p.tile = 4;
-  }
-  const int64_t t = tiles_of(L, M, p.tile);
-  if (p.tile == 5 && M > 64) p.KS = t >= 192 ? 1 : 2;
-  else if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
-  else if (t < 150) p.KS = ceil_div(224, t);
-  // one row slice of launch_tiled (x and y offsets below 2^31) must hold all M rows
-  const int64_t row_slice = ((int64_t(1) << 31) - 1) / (2 * (int64_t)(L->Kp > L->N ? L->Kp : L->N)) / 256 * 256;
-  if (p.KS > 1 && (M * (int64_t)L->N * 4 > (int64_t)INT32_MAX || M > row_slice)) p.KS = 1;
-  if (p.KS > L->KC / 4) p.KS = L->KC / 4 > 1 ? L->KC / 4 : 1;     // at least four chunks per slice
-  p.kcs = (L->KC + p.KS - 1) / p.KS;
-  p.KS = (L->KC + p.kcs - 1) / p.kcs;
-  return p;
+  return tiled_plan_of(M, L->Kp, L->N, L->bits, L->KC, L->CT, L->seg_steps);
 }
 
 int tiled_slice_chunks(const gptq_layer* L, int64_t M) { return tiled_plan(L, M).kcs; }
