@@ -155,6 +155,22 @@ def test_dispatch_plans_fit_their_kernels():
         os.remove(exe)
 
 
+def test_act_order_bank_spread():
+    """The within-group order of act-order layers (csrc/bank_spread.h): for seeded act-order maps
+    over K = 128 .. 8192 and groups of 128 / 256 / 512 / all inputs it succeeds and gives a
+    permutation that keeps every group on its positions with distinct LDS banks per staging write
+    instruction (tests/spread_check.cpp, checked independently of the function's own check)."""
+    exe = os.path.join("/tmp", f"gq_spread_check_{os.getpid()}")
+    src = os.path.join(ROOT, "tests", "spread_check.cpp")
+    inc = os.path.join(ROOT, "weight_only_quantized_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-I", inc, src, "-o", exe], check=True)
+    try:
+        out = subprocess.run([exe], capture_output=True, text=True)
+        assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+    finally:
+        os.remove(exe)
+
+
 def test_bias_patterns_are_the_stated_values():
     # dequant.h feeds -bias as raw 16-bit patterns; check them against numpy's conversions
     text = open(os.path.join(ROOT, "weight_only_quantized_amd", "csrc", "dequant.h")).read()
