@@ -331,8 +331,8 @@ def extra_workloads():
                         bias=True))
     out.append(Workload("bias_prefill_4096x8192x28672", 8192, 28672, 4096, 4, 128, False, "bf16", "bf16",
                         gi.seed_for(4), bias=True))
-    # GPTQ_P planar checkpoints: 3-bit (its own runtime width) and 5-bit (run as 8-bit codes)
-    for bits in (3, 5):
+    # GPTQ_P planar checkpoints, each in the runtime layout of its own width
+    for bits in (3, 5, 6, 7):
         out.append(Workload(f"gptq_p_llama3_8b_up_proj", 4096, 14336, 1, bits, 128, False, "f16", "f16",
                             gi.seed_for(6, bits), fmt="gptq_p"))
     # the same shapes repacked from AutoAWQ GEMM tensors (same runtime layout and kernels)

@@ -83,8 +83,8 @@ typedef enum {
    * 32 codes take `bits` consecutive words (qweight rows, qzeros columns), one group of words per
    * plane of widths 2 | 2+1 | 4 | 4+1 | 4+2 | 4+2+1 | 8, low bits first; inside a plane the
    * fields are packed continuously, low bits first.  Zeros keep the v1 "minus one".  Shapes as
-   * GPTQ.  5/6/7-bit codes are widened to the 8-bit runtime layout (exact; 8 / bits of the
-   * checkpoint's bytes per call). */
+   * GPTQ.  Every width runs in a runtime layout of its own width (5/6/7-bit codes included), so
+   * a call reads bits / 8 bytes per weight. */
   GPTQ_FORMAT_GPTQ_P = 4
 } gptq_format;
 

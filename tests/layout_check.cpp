@@ -1,6 +1,7 @@
 // Host check of the runtime layout map (weight_only_quantized_amd/csrc/layout.h): for every bit
-// width, the 32 codes of a lane must cover every bit of the lane's words exactly once, and every
-// lane word must land at a distinct offset inside its unit; the division-free segment -> group map
+// width 2..8, the 32 codes of a lane must cover every bit of the lane's words exactly once, every
+// lane word must land at a distinct offset inside its unit, and each part's words of a lane must
+// be consecutive (one load); the division-free segment -> group map
 // must equal integer division for every divisor and segment a layer can have.  Built with g++ by
 // tests/test_boundary_cpu.py; prints "ok" on success.
 #include <cstdio>
@@ -8,12 +9,12 @@
 #include "layout.h"
 
 int main() {
-  const int widths[4] = {2, 3, 4, 8};
+  const int widths[7] = {2, 3, 4, 5, 6, 7, 8};
   for (int bits : widths) {
     unsigned used[8] = {0};
     int code_bits = 0;
     for (int i = 0; i < 32; ++i) {
-      gq::Piece p[2];
+      gq::Piece p[gq::kMaxPieces];
       int np = gq::code_pieces(bits, i, p);
       int cb = 0;
       for (int k = 0; k < np; ++k) {
@@ -28,6 +29,12 @@ int main() {
       code_bits += cb;
     }
     for (int w = 0; w < bits; ++w) if (used[w] != 0xFFFFFFFFu) { printf("hole bits=%d word=%d %08x\n", bits, w, used[w]); return 1; }
+    // every word of a part is read by one load of 1..4 consecutive words at the lane's base
+    for (int lane = 0; lane < 64; ++lane)
+      for (int w = 1; w < bits; ++w)
+        if ((w & 3) != 0 && gq::unit_word_offset(bits, lane, w) != gq::unit_word_offset(bits, lane, w - 1) + 1) {
+          printf("part not contiguous bits=%d lane=%d w=%d\n", bits, lane, w); return 1;
+        }
     std::set<int> offs;
     for (int lane = 0; lane < 64; ++lane)
       for (int w = 0; w < bits; ++w) offs.insert(gq::unit_word_offset(bits, lane, w));

@@ -94,6 +94,31 @@ def test_gemm_formats_every_family(fmt, bits, K, gs, desc, sdt, xdt):
     h.close()
 
 
+# 5/6/7-bit planar layers in their own runtime widths, on every form the dispatcher has for them:
+# the M = 1 rule at 4 / 8 chunks a wave (and 8 where 4-bit codes would take 16), act-order M = 1,
+# staged x, x from L2, two row blocks, the 40-chunk waves, 32-input groups, the mid kernel and
+# both tiled tiles.
+@pytest.mark.parametrize("bits,K,gs,desc,sdt,xdt", [
+    (5, 4096, 128, False, "f16", "bf16"), (6, 8192, 128, True, "f16", "f16"), (7, 8192, 128, False, "bf16", "bf16"),
+    (6, 10240, 128, False, "f16", "f16"), (7, 14336, -1, False, "f32", "f16"), (5, 5120, 128, False, "bf16", "f16"),
+    (7, 2048, 32, True, "f16", "bf16"), (6, 16384, 128, False, "f16", "bf16"), (5, 8192, 256, True, "bf16", "bf16"),
+])
+def test_native_wide_codes_every_form(bits, K, gs, desc, sdt, xdt):
+    import weight_only_quantized_amd as wq
+    N = 256
+    say("wide-codes", bits, K, gs, desc, sdt, xdt)
+    L = gi.make_layer(K, N, bits, gs, desc_act=desc, scales_dtype=sdt, seed=7 * K + bits)
+    h = repack_fmt(L, "gptq_p")
+    assert h.info()["bits"] == bits
+    rows = [1, 2, 3, 5, 8, 12, 16, 17, 24, 33, 64, 65, 130]
+    x = gi.make_x(max(rows), K, xdt, seed=K + 3 * bits)
+    y_ref = o.gemm_fmt("gptq_p", x, xdt, L.qweight, L.qzeros, L.scales, sdt, L.g_idx, bits)
+    for M in rows:
+        for p in [wq.PATH_AUTO, wq.PATH_TILED] + ([wq.PATH_SKINNY] if M <= 64 else []):
+            check(run_gemm(h, x[:M], xdt, path=p), xdt, y_ref[:M], label=("wide", bits, K, M, p))
+    h.close()
+
+
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 def test_v2_zero_of_zero(xdt):
     """A v2 zero of 0 (which v1 cannot store) on every family: W = code * scale there."""

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
 SOURCES = ["api.cpp", "repack.hip", "skinny.hip", "skinny_b2.hip", "skinny_b3.hip", "skinny_b4.hip",
-           "skinny_b8.hip", "mid.hip", "mid_b2.hip", "mid_b3.hip", "mid_b4.hip", "mid_b8.hip", "tiled.hip", "quantize.hip",
+           "skinny_b5.hip", "skinny_b6.hip", "skinny_b7.hip", "skinny_b8.hip", "mid.hip", "mid_b2.hip", "mid_b3.hip",
+           "mid_b4.hip", "mid_b5.hip", "mid_b6.hip", "mid_b7.hip", "mid_b8.hip", "tiled.hip", "quantize.hip",
            "read_floor.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -233,7 +233,7 @@ gptq_status gptq_repack(const gptq_layer_desc* desc, const int32_t* qweight, con
   L->device = dev;
   L->K = K; L->N = N; L->group_size = desc->group_size;
   L->ckpt_bits = desc->bits;
-  L->bits = desc->bits >= 5 && desc->bits <= 7 ? 8 : desc->bits;   // 5/6/7-bit codes run as 8-bit
+  L->bits = desc->bits;   // 2..8-bit runtime widths (layout.h)
   L->gs_eff = desc->group_size == -1 ? K : desc->group_size;
   L->G = groups_of(K, desc->group_size);
   L->Kp = Kp; L->KC = Kp / kChunkK; L->CT = N / kTileN;
@@ -460,7 +460,7 @@ gptq_status gptq_decode_runtime(gptq_handle_t h, uint8_t* codes_kn_host, int32_t
         const uint32_t* u = w.data() + ((size_t)ct * h->KC + kc) * unit_words(bits);
         for (int lane = 0; lane < kLanes; ++lane)
           for (int i = 0; i < 32; ++i) {
-            Piece p[2];
+            Piece p[kMaxPieces];
             int np = code_pieces(bits, i, p);
             uint32_t code = 0;
             for (int q = 0; q < np; ++q) {

@@ -51,6 +51,25 @@ __device__ __forceinline__ void load_words(rsrc_t r, uint32_t voff, uint32_t sof
   }
 }
 
+// A lane's `BITS` words of one unit (layout.h, unit_word_offset) at byte offset soff of resource
+// r: one load of BITS words up to 4 bits; above, words 0-3 and then words 4 .. BITS - 1.  The two
+// lane offsets come from unit_voff0 / unit_voff1, computed once per kernel.
+template <int BITS>
+__device__ __forceinline__ uint32_t unit_voff0(int lane) { return (uint32_t)lane * (BITS < 4 ? BITS : 4) * 4u; }
+template <int BITS>
+__device__ __forceinline__ uint32_t unit_voff1(int lane) {
+  return BITS == 8 ? unit_voff0<BITS>(lane) + 1024u : 1024u + (uint32_t)lane * (BITS > 4 ? BITS - 4 : 0) * 4u;
+}
+template <int BITS, int AUX>
+__device__ __forceinline__ void load_unit(rsrc_t r, uint32_t voff0, uint32_t voff1, uint32_t soff, uint32_t* out) {
+  if constexpr (BITS <= 4) {
+    load_words<BITS, AUX>(r, voff0, soff, out);
+  } else {
+    load_words<4, AUX>(r, voff0, soff, out);
+    load_words<BITS - 4, AUX>(r, voff1, soff, out + 4);
+  }
+}
+
 __device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }

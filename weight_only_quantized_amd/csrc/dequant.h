@@ -15,7 +15,7 @@
 //     v = code + 16 - zero in [0, 30] per byte (one v_add_u32, no carries), so the operand is
 //     144 + (code - zero) exactly, and the kernels remove the constant 144 with one extra term
 //     -144 * sum_k x[m, k] per row and segment, fed in as the MFMA's initial accumulator;
-//     8-bit bf16 codes go through fp32 (c - z is exact in bf16, no bias);
+//     5..8-bit bf16 codes go through fp32 (c - z is exact in bf16, no bias);
 //   * the group scale multiplies each segment's fp32 partial sum (a group, or a 128-input chunk
 //     of a larger group) -- it is never folded into the 16-bit operand, so no weight is rounded.
 #pragma once
@@ -60,10 +60,27 @@ template <int BITS>
 __device__ __forceinline__ uint32_t byte_vector(const uint32_t* w, int j) {
   if constexpr (BITS == 4) return (w[j >> 1] >> (4 * (j & 1))) & 0x0F0F0F0Fu;
   else if constexpr (BITS == 2) return (w[j >> 2] >> (2 * (j & 3))) & 0x03030303u;
-  else {  // 3-bit
+  else if constexpr (BITS == 3) {
     if (j < 6) return (w[j >> 1] >> (3 * (j & 1))) & 0x07070707u;
     const uint32_t comb = ((w[0] >> 6) & 0x03030303u) | ((w[1] >> 4) & 0x0C0C0C0Cu) | ((w[2] >> 2) & 0x30303030u);
     return j == 6 ? (comb & 0x07070707u) : ((comb >> 3) & 0x07070707u);
+  } else {  // 5/6/7-bit: j < BITS in the low bits of word j's bytes, the rest from the spare bits
+    static_assert(BITS >= 5 && BITS <= 7, "byte vectors of 2..7-bit codes");
+    constexpr uint32_t ones = 0x01010101u;
+    if (j < BITS) return w[j] & (ones * ((1u << BITS) - 1u));
+    constexpr int sp = 8 - BITS;
+    uint32_t r = 0;
+    int pos = BITS * (j - BITS), cbit = 0;
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) {      // at most BITS pieces, one per word
+      if (cbit < BITS) {
+        const int u = pos / sp, o = pos % sp, take = sp - o < BITS - cbit ? sp - o : BITS - cbit;
+        r |= (w[u] >> (BITS + o - cbit)) & (ones * (((1u << take) - 1u) << cbit));
+        pos += take;
+        cbit += take;
+      }
+    }
+    return r;
   }
 }
 
@@ -72,11 +89,21 @@ __device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
 }
 
 // B operand of MFMA step t (8 consecutive k of the lane's column): code - zero (fp16), or
-// 144 + code - zero (bf16, 2/3/4-bit), or code - zero (bf16, 8-bit).
+// 144 + code - zero (bf16, 2/3/4-bit), or code - zero (bf16, 5..8-bit).
 template <int BITS, int XT>
 __device__ __forceinline__ u32x4 build_b(const uint32_t* w, int t, uint32_t zt) {
   u32x4 r;
-  if constexpr (BITS <= 4) {
+  if constexpr (BITS >= 5 && BITS <= 7 && XT == 1) {
+    // bf16 through fp32 (c - z is exact: |c - z| <= 128), bytes 0..3 of two byte vectors
+    const float zf = (float)zt;
+    const uint32_t bv[2] = {byte_vector<BITS>(w, 2 * t), byte_vector<BITS>(w, 2 * t + 1)};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t v = bv[p >> 1] >> (16 * (p & 1));     // bytes {0, 1} or {2, 3}
+      const float lo = (float)(v & 0xFFu) - zf, hi2 = (float)((v >> 8) & 0xFFu) - zf;
+      r[p] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi2) & 0xFFFF0000u);
+    }
+  } else if constexpr (BITS <= 7) {
     if constexpr (XT == 0) {
       const uint32_t b0 = byte_vector<BITS>(w, 2 * t), b1 = byte_vector<BITS>(w, 2 * t + 1);
       r[0] = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, b0, 0x04010400u), zt);

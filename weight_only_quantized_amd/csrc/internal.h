@@ -9,8 +9,8 @@
 
 struct gptq_layer {
   int device;
-  int K, N, bits, group_size, gs_eff, G, Kp, KC, CT;   // bits: runtime code width (2/3/4/8)
-  int ckpt_bits;      // the checkpoint's code width (bits, or 5/6/7 for planar layers run as 8)
+  int K, N, bits, group_size, gs_eff, G, Kp, KC, CT;   // bits: runtime code width (2..8)
+  int ckpt_bits;      // the checkpoint's code width (equal to bits: every width has its runtime layout)
   int scales_dtype;   // gptq_dtype of the stored scales
   int has_perm;       // 1 when the sorted order is not the identity
   int seg_steps;      // MFMA K steps (of 32) per scale-fixup segment: 4 or 1

@@ -29,6 +29,11 @@
 //   8-bit: code i = 8t + 4h + c  at word 2t + h, byte {0, 2, 1, 3}[c]
 //          ((w & 0x00FF00FF) holds codes c = 0, 1 in its two 16-bit halves, (w >> 8) & 0x00FF00FF
 //          codes c = 2, 3)
+//   5/6/7-bit (b bits, s = 8 - b spare bits per byte): code i < 4b at word i / 4, byte i % 4, its
+//          low b bits (BV_j = w_j & mask for j < b); the s spare bits of byte position p of the
+//          b words, taken word by word, form a stream of b * s bits that holds the s remaining
+//          codes of that byte position, 4b + 4e + p for e = 0 .. s - 1, b bits each, low bits
+//          first (a code's bits come from up to b words; 7-bit: one spare bit per word)
 //
 // Group metadata is re-tiled the same way, one 32-bit record per (tile, group, column):
 //   meta[(ct * G + g) * 16 + j] = scale bits (fp16/bf16, bits 0-15; 0 for f32 scales)
@@ -55,15 +60,19 @@ constexpr int kIpermMaxKp = 8192;   // 16-bit inverse permutation kept up to thi
 GQ_HD int words_per_lane(int bits) { return bits; }
 GQ_HD int64_t unit_words(int bits) { return (int64_t)kLanes * bits; }
 
-// Word offset (within a unit) of lane `lane`'s word `w`.
+// Word offset (within a unit) of lane `lane`'s word `w`: up to four words a lane, lane-major;
+// wider codes in two parts, words 0-3 (lane-major, 4 words a lane) then words 4 .. bits - 1.
 GQ_HD int unit_word_offset(int bits, int lane, int w) {
   if (bits <= 4) return lane * bits + w;
-  return (w >> 2) * (kLanes * 4) + lane * 4 + (w & 3);
+  const int part = w >> 2, pw = part == 0 ? 4 : bits - 4;
+  return part * (kLanes * 4) + lane * pw + (w & 3);
 }
 
 // A piece of a code: `nb` bits of word `word` starting at bit `bit` hold code bits
-// [cbit, cbit + nb).  Every code has one or two pieces.
+// [cbit, cbit + nb).  Every code has at most kMaxPieces pieces (one or two up to 4 bits and for
+// 8 bits; up to `bits` for the spare-bit codes of 5/6/7 bits).
 struct Piece { int word, bit, nb, cbit; };
+constexpr int kMaxPieces = 8;
 
 GQ_HD int code_pieces(int bits, int i, Piece* p) {
   if (bits == 4) { int t = i >> 3, h = (i >> 2) & 1, b = i & 3; p[0] = {t, 8 * b + 4 * h, 4, 0}; return 1; }
@@ -73,6 +82,18 @@ GQ_HD int code_pieces(int bits, int i, Piece* p) {
     const int byte_of[4] = {0, 2, 1, 3};
     p[0] = {2 * t + h, 8 * byte_of[c], 8, 0};
     return 1;
+  }
+  if (bits >= 5) {
+    if (i < 4 * bits) { p[0] = {i >> 2, 8 * (i & 3), bits, 0}; return 1; }
+    const int x = i - 4 * bits, pos_byte = x & 3, e = x >> 2, sp = 8 - bits;
+    int np = 0, pos = bits * e, cbit = 0;
+    while (cbit < bits) {
+      const int u = pos / sp, o = pos % sp, take = (sp - o < bits - cbit) ? sp - o : bits - cbit;
+      p[np++] = {u, 8 * pos_byte + bits + o, take, cbit};
+      pos += take;
+      cbit += take;
+    }
+    return np;
   }
   // bits == 3
   if (i < 24) { int u = i >> 3, h = (i >> 2) & 1, b = i & 3; p[0] = {u, 8 * b + 3 * h, 3, 0}; return 1; }

@@ -81,6 +81,9 @@ static hipError_t mid_pass(const GemmCall& c, const uint16_t* x, int ld, float* 
     case 2: e = mid_b2(a, p, c.x_bf16, L->seg_steps, c.stream); break;
     case 3: e = mid_b3(a, p, c.x_bf16, L->seg_steps, c.stream); break;
     case 4: e = mid_b4(a, p, c.x_bf16, L->seg_steps, c.stream); break;
+    case 5: e = mid_b5(a, p, c.x_bf16, L->seg_steps, c.stream); break;
+    case 6: e = mid_b6(a, p, c.x_bf16, L->seg_steps, c.stream); break;
+    case 7: e = mid_b7(a, p, c.x_bf16, L->seg_steps, c.stream); break;
     default: e = mid_b8(a, p, c.x_bf16, L->seg_steps, c.stream); break;
   }
   if (e != hipSuccess || p.KS == 1) return e;

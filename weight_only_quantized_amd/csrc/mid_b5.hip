@@ -1,0 +1,8 @@
+// Instantiation unit of the mid family for 5-bit codes (kernel in mid_impl.h).
+#include "mid_impl.h"
+
+namespace gq {
+hipError_t mid_b5(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s) {
+  return mid_bits<5>(a, p, x_bf16, seg, s);
+}
+}  // namespace gq

@@ -59,8 +59,7 @@ template <int BITS, int XT, int MT, int WN, int NW, int SEG, int DEPTH, int TCH,
 __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   constexpr int BMR = 16 * MT;                  // rows held in LDS (rows >= M are zero)
   constexpr int NSEG = 4 / SEG;
-  constexpr int PARTS = BITS == 8 ? 2 : 1;
-  constexpr int PW = BITS == 8 ? 4 : BITS;
+  constexpr int PARTS = BITS > 4 ? 2 : 1;      // loads per lane per unit (load_unit)
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
   constexpr bool BIAS = Bias<BITS, XT>::any;
   extern __shared__ __attribute__((aligned(1024))) uint8_t slab[];   // [chunk][row][16 pieces]
@@ -89,7 +88,7 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
     rm[j] = make_rsrc(a.meta + ctj * a.G * 16, (uint32_t)a.G * 64u);
     rs[j] = make_rsrc(a.scale32 ? a.scale32 + ctj * a.G * 16 : a.meta, a.scale32 ? (uint32_t)a.G * 64u : 0u);
   }
-  const uint32_t voff_w = (uint32_t)lane * PW * 4u;
+  const uint32_t voff_w = unit_voff0<BITS>(lane), voff_w1 = unit_voff1<BITS>(lane);
   const uint32_t voff_m = (uint32_t)col * 4u;
   struct WChunk {
     uint32_t w[WN][BITS];
@@ -99,9 +98,7 @@ __global__ void __launch_bounds__(64 * NW) mid_kernel(const MidArgs a) {
   auto load_w = [&](int kc, WChunk& c) {
 #pragma unroll
     for (int j = 0; j < WN; ++j)
-#pragma unroll
-      for (int p = 0; p < PARTS; ++p)
-        load_words<PW, kAuxStream>(rw[j], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &c.w[j][4 * p]);
+      load_unit<BITS, kAuxStream>(rw[j], voff_w, voff_w1, (uint32_t)kc * UNIT_BYTES, c.w[j]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
       const int g = mid_segment_group(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
@@ -267,6 +264,9 @@ hipError_t mid_bits(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hip
 hipError_t mid_b2(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
 hipError_t mid_b3(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
 hipError_t mid_b4(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
+hipError_t mid_b5(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
+hipError_t mid_b6(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
+hipError_t mid_b7(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
 hipError_t mid_b8(const MidArgs& a, const MidPlan& p, int x_bf16, int seg, hipStream_t s);
 
 }  // namespace gq

@@ -6,7 +6,7 @@
 // "10 / split / 10" layout).  qzeros uses the same rule along the output dimension.  Inputs are
 // visited in the load-time sorted order ("39. Quantized checkpoints ...", "The format").  The
 // same kernels read the other accepted encodings of the same W (RepackSource): GPTQ v2 zeros,
-// GPTQ_P planar words (5/6/7-bit codes go into the 8-bit runtime layout) and AutoAWQ GEMM.
+// GPTQ_P planar words (every width 2..8 into the runtime layout of its own width) and AutoAWQ GEMM.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) repack_words_kernel(
         code = packed_field(qweight, N, src_bits, k, n);
       }
     }
-    Piece p[2];
+    Piece p[kMaxPieces];
     const int np = code_pieces(bits, i, p);
     for (int q = 0; q < np; ++q) {
       const uint32_t part = (code >> p[q].cbit) & ((1u << p[q].nb) - 1u);

@@ -38,6 +38,9 @@ hipError_t launch_skinny(const GemmCall& c) {
     case 2: return skinny_b2(a, c.x_bf16, L->seg_steps, c.stream);
     case 3: return skinny_b3(a, c.x_bf16, L->seg_steps, c.stream);
     case 4: return skinny_b4(a, c.x_bf16, L->seg_steps, c.stream);
+    case 5: return skinny_b5(a, c.x_bf16, L->seg_steps, c.stream);
+    case 6: return skinny_b6(a, c.x_bf16, L->seg_steps, c.stream);
+    case 7: return skinny_b7(a, c.x_bf16, L->seg_steps, c.stream);
     default: return skinny_b8(a, c.x_bf16, L->seg_steps, c.stream);
   }
 }

@@ -1,0 +1,6 @@
+// Instantiation unit of the skinny family for 5-bit codes (kernels are in skinny_impl.h).
+#include "skinny_impl.h"
+
+namespace gq {
+hipError_t skinny_b5(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s) { return skinny_bits<5>(a, x_bf16, seg, s); }
+}  // namespace gq

@@ -110,8 +110,7 @@ skinny_kernel(const SkinnyArgs a) {
   constexpr int NT = 64 * NWV;
   constexpr int CGS = RTK ? 1 : NWV / KSPLIT;   // column groups per workgroup (launch-set form: a.cgs)
   constexpr int NSEG = 4 / SEG;                 // fixup segments per chunk
-  constexpr int PARTS = BITS == 8 ? 2 : 1;      // loads per lane per unit
-  constexpr int PW = BITS == 8 ? 4 : BITS;      // words per load
+  constexpr int PARTS = BITS > 4 ? 2 : 1;      // loads per lane per unit (load_unit)
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
   constexpr int NR = ONE == 1 ? 1 : 4;           // accumulator registers carried (ONE = 1: output row 0)
   // Group and scale picked without branches (NB): in the copy form, where the branches around the
@@ -169,7 +168,7 @@ skinny_kernel(const SkinnyArgs a) {
     rm[i] = make_rsrc(a.meta + cti * a.G * 16, (uint32_t)a.G * 64u);
     rs[i] = make_rsrc(a.scale32 ? a.scale32 + cti * a.G * 16 : a.meta, a.scale32 ? (uint32_t)a.G * 64u : 0u);
   }
-  const uint32_t voff_w = (uint32_t)lane * PW * 4u;
+  const uint32_t voff_w = unit_voff0<BITS>(lane), voff_w1 = unit_voff1<BITS>(lane);
   const uint32_t voff_m = (uint32_t)col * 4u;
 
   struct WChunk {
@@ -180,9 +179,7 @@ skinny_kernel(const SkinnyArgs a) {
   auto load_w = [&](int kc, WChunk& c) {
 #pragma unroll
     for (int i = 0; i < TW; ++i)
-#pragma unroll
-      for (int p = 0; p < PARTS; ++p)
-        load_words<PW, kAuxStream>(rw[i], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &c.w[i][4 * p]);
+      load_unit<BITS, kAuxStream>(rw[i], voff_w, voff_w1, (uint32_t)kc * UNIT_BYTES, c.w[i]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
       const int g = segment_group<NB>(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
@@ -605,7 +602,7 @@ static hipError_t run_tch(const SkinnyArgs& a, int seg, hipStream_t s) {
 template <int BITS, int XT, int TCH, int F32S>
 static hipError_t run_m1(const SkinnyArgs& a0, hipStream_t s) {
   constexpr int ONE = XT == 1 && BITS <= 4;
-  constexpr int DEPTH = TCH == 16 || (BITS == 8 && TCH > 4) ? 4 : TCH;
+  constexpr int DEPTH = TCH == 16 || (BITS > 4 && TCH > 4) ? 4 : TCH;
   SkinnyArgs a = a0;
   const int waves = (a.KC + TCH - 1) / TCH;
   a.Kx = waves * TCH * kChunkK;
@@ -661,8 +658,11 @@ static hipError_t run_m(const SkinnyArgs& a, int seg, hipStream_t s) {
   if (skinny_m1_rule(a.M, a.KC, seg, a.iperm != nullptr)) {
     const int t = skinny_m1_chunks(a.KC);
     if (t == 4) return run_m1<BITS, XT, 4, F32S>(a, s);
-    if (t == 8) return run_m1<BITS, XT, 8, F32S>(a, s);
-    return run_m1<BITS, XT, 16, F32S>(a, s);
+    // (5/6/7-bit codes keep to 8 chunks a wave: 16 with their spare-bit codes exceed the 128
+    // VGPRs of a 16-wave workgroup)
+    if (t == 8 || (BITS > 4 && BITS < 8)) return run_m1<BITS, XT, 8, F32S>(a, s);
+    if constexpr (BITS <= 4 || BITS == 8) return run_m1<BITS, XT, 16, F32S>(a, s);
+    return hipErrorInvalidValue;   // (not reached)
   }
   if (skinny_m1_act_rule(a.M, a.Kp, seg, a.iperm != nullptr)) {
     if (a.KC <= 32) return run_m1_act<BITS, XT, 4, F32S>(a, s);
@@ -728,6 +728,9 @@ hipError_t skinny_bits(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s) 
 hipError_t skinny_b2(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
 hipError_t skinny_b3(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
 hipError_t skinny_b4(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
+hipError_t skinny_b5(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
+hipError_t skinny_b6(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
+hipError_t skinny_b7(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
 hipError_t skinny_b8(const SkinnyArgs& a, int x_bf16, int seg, hipStream_t s);
 
 }  // namespace gq

@@ -312,8 +312,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(DE
 tiled_kernel(const TiledArgs a) {
   constexpr int BM = 16 * WM;
   constexpr int NSEG = 4 / SEG;
-  constexpr int PARTS = BITS == 8 ? 2 : 1;
-  constexpr int PW = BITS == 8 ? 4 : BITS;
+  constexpr int PARTS = BITS > 4 ? 2 : 1;      // loads per lane per unit (load_unit)
   constexpr uint32_t UNIT_BYTES = 256u * BITS;
   constexpr int A_BYTES = BM * 256;            // one chunk of x for the tile
   constexpr int A_INST = BM / (4 * NW);        // 1 KB LDS loads per wave per chunk
@@ -365,7 +364,7 @@ tiled_kernel(const TiledArgs a) {
     rm[j] = make_rsrc(a.meta + ctj * a.G * 16, (uint32_t)a.G * 64u);
     rs[j] = make_rsrc(a.scale32 ? a.scale32 + ctj * a.G * 16 : a.meta, a.scale32 ? (uint32_t)a.G * 64u : 0u);
   }
-  const uint32_t voff_w = (uint32_t)lane * PW * 4u;
+  const uint32_t voff_w = unit_voff0<BITS>(lane), voff_w1 = unit_voff1<BITS>(lane);
   const uint32_t voff_m = (uint32_t)col * 4u;
   // A operand reads: row i*16 + col, piece 4t + q  ->  byte (col * 16 + ((4t + q) ^ col)) * 16 + i * 4096
   uint32_t a_off[4];
@@ -391,9 +390,7 @@ tiled_kernel(const TiledArgs a) {
   auto issue = [&](int kc, uint8_t* xb, Stage& st, bool with_x) {
 #pragma unroll
     for (int j = 0; j < WN; ++j)
-#pragma unroll
-      for (int p = 0; p < PARTS; ++p)
-        load_words<PW, 0>(rw[j], voff_w + p * 1024u, (uint32_t)kc * UNIT_BYTES, &st.w[j][4 * p]);
+      load_unit<BITS, 0>(rw[j], voff_w, voff_w1, (uint32_t)kc * UNIT_BYTES, st.w[j]);
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
       const int g = segment_group(SEG == 4 ? kc : kc * 4 + s, a.gmagic, a.gshift, a.G);
@@ -595,6 +592,9 @@ static hipError_t run_tiled_bits(const TiledArgs& a, int bits, int tile, int seg
     case 2: return run_tiled_m<2, OB>(a, tile, seg, s);
     case 3: return run_tiled_m<3, OB>(a, tile, seg, s);
     case 4: return run_tiled_m<4, OB>(a, tile, seg, s);
+    case 5: return run_tiled_m<5, OB>(a, tile, seg, s);
+    case 6: return run_tiled_m<6, OB>(a, tile, seg, s);
+    case 7: return run_tiled_m<7, OB>(a, tile, seg, s);
     default: return run_tiled_m<8, OB>(a, tile, seg, s);
   }
 }
