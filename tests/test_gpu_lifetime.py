@@ -18,7 +18,8 @@ import numpy as np
 import pytest
 
 import gptq_inputs as gi
-from gpu_util import bits_to_device, device_to_bits, repack_layer, torch_dtype
+import oracle as o
+from gpu_util import bits_to_device, check, device_to_bits, repack_layer, run_gemm, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -174,6 +175,49 @@ def test_destroyed_handle_is_refused():
     assert lib.gptq_destroy(None) == 0
     # a pointer never issued by the library
     assert wq.STATUS[lib.gptq_info(ctypes.c_void_p(x.data_ptr()), ctypes.byref(info))] == "E_INVALID_ARG"
+
+
+def test_hip_runtime_error_is_reported_with_its_code():
+    """A HIP runtime failure surfaces as GPTQ_E_HIP, with the runtime's own error code behind it in
+    gptq_last_hip_error: gptq_repack reads g_idx back to the host and synchronises its stream, which
+    a stream under graph capture refuses.  No kernel is launched.  The library works as before
+    once the capture has ended."""
+    import ctypes
+    import torch
+    import weight_only_quantized_amd as wq
+    say("HIP error")
+    hip = ctypes.CDLL("libamdhip64.so")
+    lib = wq.load_library()
+    K, N = 256, 64
+    L = gi.make_layer(K, N, 4, 128, desc_act=True, scales_dtype="f16", seed=gi.seed_for(9, 61))
+    qw = torch.from_numpy(L.qweight).cuda()
+    qz = torch.from_numpy(L.qzeros).cuda()
+    sc = bits_to_device(L.scales, "f16")
+    gx = torch.from_numpy(L.g_idx).cuda()
+    d = wq.make_desc(K, N, 4, 128, wq.F16, qw.shape, qz.shape, sc.shape, K, True)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    sp = ctypes.c_void_p(s.cuda_stream)
+    assert hip.hipStreamBeginCapture(sp, 2) == 0          # hipStreamCaptureModeRelaxed
+    out = ctypes.c_void_p()
+    try:
+        st = lib.gptq_repack(ctypes.byref(d), qw.data_ptr(), qz.data_ptr(), sc.data_ptr(), gx.data_ptr(), sp,
+                             ctypes.byref(out))
+        code = lib.gptq_last_hip_error()
+    finally:
+        graph = ctypes.c_void_p()
+        hip.hipStreamEndCapture(sp, ctypes.byref(graph))    # the capture is invalidated
+        if graph.value:
+            hip.hipGraphDestroy(graph)
+        hip.hipGetLastError()
+    assert wq.STATUS[st] == "E_HIP", st
+    assert code != 0
+    assert not out.value
+    h = wq.repack(qw, qz, sc, gx, bits=4, group_size=128, desc_act=True)
+    x = gi.make_x(3, K, "f16", seed=7)
+    y_ref = o.gemm(x, "f16", L.qweight, L.qzeros, L.scales, "f16", L.g_idx, 4)
+    check(run_gemm(h, x, "f16"), "f16", y_ref, label="after a HIP error")
+    h.close()
 
 
 def test_out_of_device_memory_is_reported():
