@@ -82,6 +82,13 @@ inline CopyPlan skinny_copy_plan(int64_t M, int KC, int CT, int bits, int seg_st
   if (M < 2 || M > 32 || bits > 4 || seg_steps != 4 || x_unsorted) return p;
   if ((KC == 40 || KC == 48 || KC == 56) && M <= 8) return p;
   if (KC <= 32 && M <= 4) return p;
+  // 17..32 rows over 64 or more chunks go to the tiled family's 32-row tile instead (MI355X, us,
+  // copy form -> 32 x 128 tile, whole calls: 8192 x 28672 bf16 M = 17 / 19 38.9 / 39.2 -> 35.2 /
+  // 35.7; 8192 x 8192 bf16 4-bit M = 32 20.8 -> 18.1, fp16 M = 20 15.6 -> 14.2, act-order M = 32
+  // 2 / 4-bit 20.9 / 21.9 -> 19.3 / 18.5), except 2-bit codes below 20 rows (act-order M = 17
+  // 16.5 against 17.7); over 32 chunks the copy form stays ahead (4096 x 14336 M = 24 / 32: 12.6 /
+  // 13.5 against 13.8 / 14.4)
+  if (M > 16 && KC >= 64 && (bits > 2 || M >= 20)) return p;
   constexpr size_t kLds = 160 * 1024;
   const int mt = M <= 16 ? 1 : 2;
   for (int ph : {1, 2, 4}) {
@@ -186,6 +193,7 @@ constexpr TileShape kTiles[] = {
   {4, 2, 4},    // 3:  64 x 128, wave  64 x 32
   {8, 2, 8},    // 4: 128 x 256, wave 128 x 32
   {4, 2, 4},    // 5:  64 x 128 as 3, two chunks in flight
+  {2, 2, 4},    // 6:  32 x 128, wave  32 x 32, two chunks in flight
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -203,6 +211,10 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // of every tile and split on MI355X (4-bit g128, 4096 x 14336 and 8192 x 28672 layers, M = 4 ..
 // 1024): a call runs best with about one eight-wave workgroup (or two four-wave ones) per compute
 // unit, from the largest tile that gets there, and splits K only as far as needed to get there:
+//   * M <= 32: the 32 x 128 tile (four waves of 32 x 32, two chunks in flight), K split up to
+//     ~256 workgroups (MI355X, fp16 x, us, against the 64 x 128 tile at its split: 8192 x 28672
+//     M = 24 / 32 37.3 / 38.5 -> 30.5 / 32.2; 8192 x 8192 4-bit M = 32 27.5 -> 14.8; 14336 x 4096
+//     M = 16 / 32 -> 13.1 / 14.2 against the dispatch's 15.3 / 16.7);
 //   * M <= 64: the 64 x 128 tile, K split up to ~448 workgroups;
 //   * M <= 512 on layers of at most 4096 inputs whose 64-row blocks together read at most 128 MB
 //     of packed weights (the repeated passes then come from the Infinity Cache): the 64 x 128
@@ -223,6 +235,8 @@ inline TiledPlan tiled_plan_of(int64_t M, int Kp, int N, int bits, int KC, int C
   const int64_t mb64 = (M + 63) / 64;                            // 64-row blocks
   if (seg_steps != 4) {
     p.tile = 1;
+  } else if (M <= 32) {
+    p.tile = 6;
   } else if (M <= 64) {
     p.tile = 5;
   } else if (M <= 512 && KC <= 32 && mb64 * wbytes <= (int64_t(128) << 20)) {
@@ -234,6 +248,7 @@ inline TiledPlan tiled_plan_of(int64_t M, int Kp, int N, int bits, int KC, int C
   }
   const int64_t t = tiles_of(M, CT, p.tile);
   if (p.tile == 5 && M > 64) p.KS = t >= 192 ? 1 : 2;
+  else if (p.tile == 6) p.KS = ceil_div(256, t);
   else if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
   else if (t < 150) p.KS = ceil_div(224, t);
   // one row slice of launch_tiled (x and y offsets below 2^31) must hold all M rows

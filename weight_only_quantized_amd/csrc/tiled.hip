@@ -317,7 +317,8 @@ tiled_kernel(const TiledArgs a) {
   constexpr int A_BYTES = BM * 256;            // one chunk of x for the tile
   constexpr int A_INST = BM / (4 * NW);        // 1 KB LDS loads per wave per chunk
   static_assert(A_INST * NW * 64 == BM * 16, "x tile must split evenly over the waves");
-  static_assert(A_INST <= WM && WM > 2, "one x piece per row block; units after the third");
+  static_assert(A_INST <= WM && WM >= 2, "one x piece per row block");
+  constexpr int UNITS_AT = WM > 2 ? 2 : WM - 1;   // row block after which a chunk's units go out
   static_assert(DEPTH == 1 || DEPTH == 2, "one or two chunks in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t xs[DEPTH == 1 ? 2 : 1][A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t xs_b[DEPTH == 2 ? A_BYTES : 16];
@@ -504,7 +505,7 @@ tiled_kernel(const TiledArgs a) {
       const int kn = kc_lo + min(c + 2, n - 1);
       compute(xb, st, [&](int i) {
         if (i < A_INST) issue_x(kn, xbn, i);
-        if (i == 2) issue(kn, xbn, stn, false);
+        if (i == UNITS_AT) issue(kn, xbn, stn, false);
       });
     };
     auto last_step = [&](const Stage& st, const uint8_t* xb) {
@@ -539,7 +540,7 @@ tiled_kernel(const TiledArgs a) {
     const int kn = more ? it + 1 : it;
     compute(&xs[buf][0], cur, [&](int i) {
       if (i < A_INST) issue_x(kn, &xs[buf ^ 1][0], i);
-      if (i == 2) issue(kn, &xs[buf ^ 1][0], nxt, false);
+      if (i == UNITS_AT) issue(kn, &xs[buf ^ 1][0], nxt, false);
     });
     // the next chunk's x tile, units and metadata were issued before this chunk's compute
     __builtin_amdgcn_s_waitcnt(0);
@@ -582,6 +583,7 @@ static hipError_t run_tiled_m(const TiledArgs& a, int tile, int seg, hipStream_t
     case 3: return run_tiled<BITS, OB, 4, 2, 4, 4>(a, s);
     case 4: return run_tiled<BITS, OB, 8, 2, 4, 8>(a, s);
     case 5: return run_tiled<BITS, OB, 4, 2, 4, 4, 2>(a, s);
+    case 6: return run_tiled<BITS, OB, 2, 2, 4, 4, 2>(a, s);
     default: return run_tiled<BITS, OB, 8, 1, 4, 8>(a, s);
   }
 }
