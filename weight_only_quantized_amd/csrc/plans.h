@@ -194,6 +194,7 @@ constexpr TileShape kTiles[] = {
   {8, 2, 8},    // 4: 128 x 256, wave 128 x 32
   {4, 2, 4},    // 5:  64 x 128 as 3, two chunks in flight
   {2, 2, 4},    // 6:  32 x 128, wave  32 x 32, two chunks in flight
+  {1, 2, 4},    // 7:  16 x 128, wave  16 x 32, two chunks in flight
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -211,6 +212,8 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // of every tile and split on MI355X (4-bit g128, 4096 x 14336 and 8192 x 28672 layers, M = 4 ..
 // 1024): a call runs best with about one eight-wave workgroup (or two four-wave ones) per compute
 // unit, from the largest tile that gets there, and splits K only as far as needed to get there:
+//   * M <= 16: the 16 x 128 tile, K split the same way (14336 x 4096 M = 16: 13.1 -> 11.8 us,
+//     8192 x 28672 fp16 M = 8 / 16 about 10 % faster than the 32 x 128 tile);
 //   * M <= 32: the 32 x 128 tile (four waves of 32 x 32, two chunks in flight), K split up to
 //     ~256 workgroups (MI355X, fp16 x, us, against the 64 x 128 tile at its split: 8192 x 28672
 //     M = 24 / 32 37.3 / 38.5 -> 30.5 / 32.2; 8192 x 8192 4-bit M = 32 27.5 -> 14.8; 14336 x 4096
@@ -235,6 +238,8 @@ inline TiledPlan tiled_plan_of(int64_t M, int Kp, int N, int bits, int KC, int C
   const int64_t mb64 = (M + 63) / 64;                            // 64-row blocks
   if (seg_steps != 4) {
     p.tile = 1;
+  } else if (M <= 16) {
+    p.tile = 7;
   } else if (M <= 32) {
     p.tile = 6;
   } else if (M <= 64) {
@@ -248,7 +253,7 @@ inline TiledPlan tiled_plan_of(int64_t M, int Kp, int N, int bits, int KC, int C
   }
   const int64_t t = tiles_of(M, CT, p.tile);
   if (p.tile == 5 && M > 64) p.KS = t >= 192 ? 1 : 2;
-  else if (p.tile == 6) p.KS = ceil_div(256, t);
+  else if (p.tile == 6 || p.tile == 7) p.KS = ceil_div(256, t);
   else if (p.tile == 3 || p.tile == 5) p.KS = ceil_div(448, t);
   else if (t < 150) p.KS = ceil_div(224, t);
   // one row slice of launch_tiled (x and y offsets below 2^31) must hold all M rows

@@ -317,7 +317,7 @@ tiled_kernel(const TiledArgs a) {
   constexpr int A_BYTES = BM * 256;            // one chunk of x for the tile
   constexpr int A_INST = BM / (4 * NW);        // 1 KB LDS loads per wave per chunk
   static_assert(A_INST * NW * 64 == BM * 16, "x tile must split evenly over the waves");
-  static_assert(A_INST <= WM && WM >= 2, "one x piece per row block");
+  static_assert(A_INST <= WM && WM >= 1, "one x piece per row block");
   constexpr int UNITS_AT = WM > 2 ? 2 : WM - 1;   // row block after which a chunk's units go out
   static_assert(DEPTH == 1 || DEPTH == 2, "one or two chunks in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t xs[DEPTH == 1 ? 2 : 1][A_BYTES];
@@ -584,6 +584,7 @@ static hipError_t run_tiled_m(const TiledArgs& a, int tile, int seg, hipStream_t
     case 4: return run_tiled<BITS, OB, 8, 2, 4, 8>(a, s);
     case 5: return run_tiled<BITS, OB, 4, 2, 4, 4, 2>(a, s);
     case 6: return run_tiled<BITS, OB, 2, 2, 4, 4, 2>(a, s);
+    case 7: return run_tiled<BITS, OB, 1, 2, 4, 4, 2>(a, s);
     default: return run_tiled<BITS, OB, 8, 1, 4, 8>(a, s);
   }
 }
