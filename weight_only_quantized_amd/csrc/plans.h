@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "layout.h"
 
 namespace gq {
@@ -192,9 +194,10 @@ constexpr TileShape kTiles[] = {
   {8, 2, 4},    // 2: 128 x 128, wave 128 x 32
   {4, 2, 4},    // 3:  64 x 128, wave  64 x 32
   {8, 2, 8},    // 4: 128 x 256, wave 128 x 32
-  {4, 2, 4},    // 5:  64 x 128 as 3, two chunks in flight
-  {2, 2, 4},    // 6:  32 x 128, wave  32 x 32, two chunks in flight
+  {4, 2, 4},    // 5:  64 x 128 as 3, two chunks in flight (7- and 8-bit codes: as 8)
+  {2, 1, 8},    // 6:  32 x 128, wave  32 x 16, two chunks in flight
   {1, 2, 4},    // 7:  16 x 128, wave  16 x 32, two chunks in flight
+  {4, 1, 8},    // 8:  64 x 128, wave  64 x 16, two chunks in flight (grids of at most 256)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -214,10 +217,11 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // unit, from the largest tile that gets there, and splits K only as far as needed to get there:
 //   * M <= 16: the 16 x 128 tile, K split the same way (14336 x 4096 M = 16: 13.1 -> 11.8 us,
 //     8192 x 28672 fp16 M = 8 / 16 about 10 % faster than the 32 x 128 tile);
-//   * M <= 32: the 32 x 128 tile (four waves of 32 x 32, two chunks in flight), K split up to
-//     ~256 workgroups (MI355X, fp16 x, us, against the 64 x 128 tile at its split: 8192 x 28672
-//     M = 24 / 32 37.3 / 38.5 -> 30.5 / 32.2; 8192 x 8192 4-bit M = 32 27.5 -> 14.8; 14336 x 4096
-//     M = 16 / 32 -> 13.1 / 14.2 against the dispatch's 15.3 / 16.7);
+//   * M <= 32: the 32 x 128 tile, K split up to ~256 workgroups (MI355X, fp16 x, us, against the
+//     64 x 128 tile at its split: 8192 x 28672 M = 24 / 32 37.3 / 38.5 -> 30.5 / 32.2; 8192 x 8192
+//     4-bit M = 32 27.5 -> 14.8; 14336 x 4096 M = 16 / 32 -> 13.1 / 14.2 against the dispatch's
+//     15.3 / 16.7), in eight waves of 32 x 16 rather than four of 32 x 32 (within 2 % either way
+//     on those calls, in about half the registers);
 //   * M <= 64: the 64 x 128 tile, K split up to ~448 workgroups;
 //   * M <= 512 on layers of at most 4096 inputs whose 64-row blocks together read at most 128 MB
 //     of packed weights (the repeated passes then come from the Infinity Cache): the 64 x 128
@@ -225,6 +229,11 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 //     the tiles below against 19.1 / 36.7; 4096 x 14336, M = 256: 43.3 against 39.5; longer K or
 //     more weight passes measured slower: 14336 x 4096 M = 128 31.2 against 45.3, 8192 x 28672
 //     M = 256 120.4 against 148.7);
+//   * the 64 x 128 tile in eight waves of 64 x 16 when its grid has at most 256 workgroups
+//     (one per compute unit, so four waves would leave every SIMD one wave): 4096 x 14336 M = 128
+//     30.5 -> 27.5 us, 4096 x 6144 M = 256 29.4 -> 25.5; on larger grids four waves stay
+//     (4096 x 6144 M = 512: 43.3 against 47.9; 8192 x 28672 M = 48 / 64: 51.8 / 54.4 against
+//     57.3 / 60.2, where eight waves read every x tile from LDS twice as often);
 //   * larger M: the 256 x 256 tile once it alone gives ~192 workgroups, else the 128 x 256 tile,
 //     K split up to ~224 workgroups when it gives fewer than ~150;
 //   * 32-input segments: the 128 x 128 tile (wave 128 x 16), split the same way.
@@ -262,6 +271,7 @@ inline TiledPlan tiled_plan_of(int64_t M, int Kp, int N, int bits, int KC, int C
   if (p.KS > KC / 4) p.KS = KC / 4 > 1 ? KC / 4 : 1;     // at least four chunks per slice
   p.kcs = (KC + p.KS - 1) / p.KS;
   p.KS = (KC + p.kcs - 1) / p.kcs;
+  if (p.tile == 5 && t * p.KS <= 256) p.tile = 8;       // same tiles and slices, twice the waves
   return p;
 }
 

@@ -356,14 +356,12 @@ skinny_kernel(const SkinnyArgs a) {
           rx, (__attribute__((address_space(3))) void*)(xlds + r * xrow + pc * 512), 16, vo, 0u, 0, 0);
     }
   };
-  // ring_after: the weight ring was issued after the copy, and stays in flight (its loads complete
-  // in order after the copy's); otherwise everything this wave has in flight is waited for
-  constexpr int NRING = XLDS == 3 ? DEPTH * TW * (PARTS + NSEG * (1 + F32S)) : 0;   // loads of the ring
-  auto copy_finish = [&](bool ring_after) {
-    if (ring_after) wait_vmcnt<NRING>();
-    else __builtin_amdgcn_s_waitcnt(0);
-    // every wave's share of the copy has landed before any wave reads x (LDS-only fences: the
-    // weights in flight are not waited for)
+  // Everything this wave has in flight is waited for: a count of outstanding loads tells nothing
+  // about LDS DMA (buffer_load ... lds), whose completion is not ordered with register loads
+  // (MI355X: a tiled kernel whose counted wait relied on that order read stale rows of x).
+  auto copy_finish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    // every wave's share of the copy has landed before any wave reads x (LDS-only fences)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -390,8 +388,8 @@ skinny_kernel(const SkinnyArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // the copy form's copy goes out first (L2 hits, done long before the ring's HBM loads), so that
-  // the wait for it leaves the ring in flight
+  // the copy form's copy goes out first (L2 hits) and the weight ring right behind it, so that the
+  // wait for both takes about one HBM latency
   if constexpr (XLDS == 3) {
     copy_issue(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -401,7 +399,7 @@ skinny_kernel(const SkinnyArgs a) {
   for (int j = 0; j < DEPTH; ++j)
     if (TCH > 0 || kc0 + j < kc1) load_w(TCH > 0 ? chunk_at(j) : kc0 + j, ring[j]);
 
-  if constexpr (XLDS == 3) copy_finish(true);
+  if constexpr (XLDS == 3) copy_finish();
 
   if constexpr (XLDS == 1) {
 #pragma unroll
@@ -496,7 +494,7 @@ skinny_kernel(const SkinnyArgs a) {
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
           copy_issue(j / (TCH / PH));
-          copy_finish(false);
+          copy_finish();
         }
       }
       if constexpr (XLDS == 3) __builtin_amdgcn_sched_barrier(0);   // copy form: LDS reads per chunk

@@ -10,10 +10,11 @@
 //   * workgroup tile BM x BN = (16 WM) x (16 WN NW) with NW waves side by side along N, each
 //     wave owning WM x WN tiles of 16 x 16 (v_mfma_f32_16x16x32); the large-M tile is 256 x 256
 //     (WM = 16, WN = 2, eight waves, two per SIMD, under 256 registers each);
-//   * the x tile of one 128-input chunk goes global -> LDS directly (buffer_load ... lds,
-//     double-buffered, XOR-swizzled so a 16-row A-operand read hits distinct banks); each wave
-//     reads its A operands from LDS one 16-row block ahead of the matrix instructions that use
-//     them, and applies a block's group scales after the next block's MFMAs are issued;
+//   * the x tile of one 128-input chunk goes to LDS (XOR-swizzled so a 16-row A-operand read hits
+//     distinct banks): by buffer_load ... lds and a full wait with one chunk in flight, through
+//     registers with two (see tiled_kernel); each wave reads its A operands from LDS one 16-row
+//     block ahead of the matrix instructions that use them, and applies a block's group scales
+//     after the next block's MFMAs are issued;
 //   * each wave loads its own packed weight units straight into registers (one 16-byte load per
 //     unit per lane, 4-bit) and builds exact B operands (dequant.h) -- nothing dequantised is ever
 //     written to LDS or HBM;
@@ -300,13 +301,19 @@ __device__ __forceinline__ void store_part(const TiledArgs& a, const f32x4 (&acc
 
 // x tile of one chunk in LDS: BM rows x 16 pieces of 16 bytes, no padding, piece c of row r at
 // slot r * 16 + (c ^ (r & 15)).  Sixteen lanes reading the same piece of sixteen consecutive
-// rows (an A operand) then hit sixteen different 16-byte bank groups.  The tile is filled with
-// buffer_load ... lds (lane i of a load writes slot i of its 1 KB destination), so each lane
-// simply fetches the global piece that belongs in its slot.
-// DEPTH = 1: one chunk in flight (two x buffers, the next chunk's loads issued during this chunk's
-// compute, then a full wait); DEPTH = 2: two chunks in flight (three x buffers and three register
-// stages, each step waiting only for its own chunk's loads).  The three buffers are distinct LDS
-// arrays: the compiler then knows that a read of one does not wait for the LDS DMA into another.
+// rows (an A operand) then hit sixteen different 16-byte bank groups.  Lane i of a wave's piece j
+// fills slot (wave * A_INST + j) * 64 + i of the tile, so each lane simply fetches the global
+// piece that belongs in that slot.
+// DEPTH = 1: one chunk in flight (two x buffers filled by buffer_load ... lds, the next chunk's
+// loads issued during this chunk's compute, then a full wait); DEPTH = 2: two chunks in flight
+// (three x buffers and three register stages, each step waiting only for its own chunk's loads).
+// With two chunks in flight the x pieces do not come by LDS DMA: each wave loads them into
+// registers with the chunk's other loads and writes them to LDS itself.  A count of outstanding
+// loads is a sound wait only for register loads, which complete in issue order: on MI355X, with
+// the pieces loaded by DMA and the same counted wait, a 64-row tile in eight waves read 16 stale
+// rows of x in about half of its calls, while a full wait before every barrier was always right
+// and 13-28 % slower.  The buffers are distinct LDS arrays: the compiler then knows that a read of
+// one does not wait on a write to another.
 template <int BITS, int OB, int WM, int WN, int SEG, int NW, int DEPTH>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(DEPTH == 2 ? 2 : 1)))
 tiled_kernel(const TiledArgs a) {
@@ -376,10 +383,10 @@ tiled_kernel(const TiledArgs a) {
     uint32_t w[WN][BITS];
     uint32_t rec[WN][NSEG];
     uint32_t s32[WN][NSEG];
+    u32x4 x[DEPTH == 2 ? A_INST : 1];   // the wave's x pieces (two chunks in flight)
   };
 
-  // Chunk kc: packed units and metadata -> registers, then the x chunk -> LDS buffer xb by DMA.
-  // One 1 KB piece (j) of chunk kc's x tile -> xb by LDS DMA.
+  // One 1 KB piece (j) of chunk kc's x tile -> LDS buffer xb by DMA (one chunk in flight).
   auto issue_x = [&](int kc, uint8_t* xb, int j) {
     // (the offset goes through a local: passed straight from the array, the host pass of this
     // compiler drops the kernel's launch stub)
@@ -388,6 +395,15 @@ tiled_kernel(const TiledArgs a) {
         rx, (__attribute__((address_space(3))) void*)(xb + (wave * A_INST + j) * 1024), 16, vo,
         (uint32_t)kc * 256u, 0, 0);
   };
+  // One piece (j) of chunk kc's x tile -> registers, and a wave's pieces from there -> LDS buffer
+  // xb, the same slots (two chunks in flight).
+  auto load_xr = [&](int kc, Stage& st, int j) { st.x[j] = load_b128(rx, voff_a[j], (uint32_t)kc * 256u); };
+  auto write_x = [&](const Stage& st, uint8_t* xb) {
+#pragma unroll
+    for (int j = 0; j < A_INST; ++j)
+      *reinterpret_cast<u32x4*>(xb + (wave * A_INST + j) * 1024 + lane * 16) = st.x[j];
+  };
+  // Chunk kc: packed units and metadata -> registers, then (with_x) its x pieces.
   auto issue = [&](int kc, uint8_t* xb, Stage& st, bool with_x) {
 #pragma unroll
     for (int j = 0; j < WN; ++j)
@@ -403,7 +419,10 @@ tiled_kernel(const TiledArgs a) {
     }
     if (with_x) {
 #pragma unroll
-      for (int j = 0; j < A_INST; ++j) issue_x(kc, xb, j);
+      for (int j = 0; j < A_INST; ++j) {
+        if constexpr (DEPTH == 2) load_xr(kc, st, j);
+        else issue_x(kc, xb, j);
+      }
     }
   };
 
@@ -484,43 +503,53 @@ tiled_kernel(const TiledArgs a) {
   if constexpr (DEPTH == 2) {
     // Chunk c (c = 0, 1, ... from kc_lo) sits in buffer and register stage c % 3.  The step of
     // chunk c waits until at most one chunk's loads (c + 1) are pending, meets the workgroup at the
-    // barrier (every wave is then done with chunk c - 1, whose buffer and stage are free) and
-    // requests chunk c + 2 into them while it computes.  Requests past the slice repeat its last
-    // chunk (L2 hits), so every step of the loop issues the same loads and the wait count is fixed;
-    // the last one or two steps after the loop issue nothing and wait for everything.
+    // barrier (every wave's x pieces of chunk c are then in LDS, and every wave is done with chunk
+    // c - 1), requests chunk c + 2 into stage (c + 2) % 3 while it computes, and at its end writes
+    // its pieces of chunk c + 1 (loaded during step c - 1) to buffer (c + 1) % 3, last read in step
+    // c - 2.  Requests past the slice repeat its last chunk (L2 hits), so every step of the loop
+    // issues the same loads and the wait count is fixed; the last one or two steps after the loop
+    // issue nothing and wait for everything.
     constexpr int NL = WN * PARTS + 2 * NSEG * WN + A_INST;   // loads per chunk per wave
     static_assert(NL < 64, "vmcnt holds at most 63");
     Stage st0, st1, st2;
     const int n = kc_hi - kc_lo;
-    issue(kc_lo, &xs[0][0], st0, true);
-    issue(kc_lo + (n > 1 ? 1 : 0), xs_b, st1, true);
-    auto step = [&](int c, const Stage& st, const uint8_t* xb, Stage& stn, uint8_t* xbn) {
+    issue(kc_lo, nullptr, st0, true);
+    issue(kc_lo + (n > 1 ? 1 : 0), nullptr, st1, true);
+    write_x(st0, &xs[0][0]);                 // (the compiler waits for the pieces' own loads)
+    auto step = [&](int c, const Stage& st, const uint8_t* xb, Stage& stn, const Stage& stx, uint8_t* xbx) {
       __builtin_amdgcn_sched_barrier(0);     // no instruction crosses a step boundary
-      // this wave's loads of chunk c are in, and its reads of chunk c - 1 (lgkmcnt); no fence
-      // (a workgroup fence waits for every load in flight)
+      // this wave's loads of chunk c are in (register loads complete in issue order), and its
+      // writes of chunk c's pieces and reads of chunk c - 1 (lgkmcnt); the barrier publishes the
+      // pieces with every other wave's.  No fence: a workgroup fence would wait for every load in
+      // flight.
       wait_vmcnt<NL>();
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt left alone
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       const int kn = kc_lo + min(c + 2, n - 1);
       compute(xb, st, [&](int i) {
-        if (i < A_INST) issue_x(kn, xbn, i);
-        if (i == UNITS_AT) issue(kn, xbn, stn, false);
+        if (i < A_INST) load_xr(kn, stn, i);
+        if (i == UNITS_AT) issue(kn, nullptr, stn, false);
       });
-    };
-    auto last_step = [&](const Stage& st, const uint8_t* xb) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      compute(xb, st, [](int) {});
+      write_x(stx, xbx);
     };
     int c = 0;
     for (; c + 2 < n; c += 3) {
-      step(c, st0, &xs[0][0], st2, xs_c);
-      step(c + 1, st1, xs_b, st0, &xs[0][0]);
-      step(c + 2, st2, xs_c, st1, xs_b);
+      step(c, st0, &xs[0][0], st2, st1, xs_b);
+      step(c + 1, st1, xs_b, st0, st2, xs_c);
+      step(c + 2, st2, xs_c, st1, st0, &xs[0][0]);
     }
-    if (c < n) last_step(st0, &xs[0][0]);
-    if (c + 1 < n) last_step(st1, xs_b);
+    if (c < n) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      compute(&xs[0][0], st0, [](int) {});
+      if (c + 1 < n) write_x(st1, xs_b);
+    }
+    if (c + 1 < n) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      compute(xs_b, st1, [](int) {});
+    }
     __builtin_amdgcn_s_waitcnt(0);
     if (a.part) store_part<OB, WM, WN>(a, acc, ks, m0, ct0, col, q);
     else store_tiles<OB, WM, WN>(a, acc, m0, ct0, col, q);
@@ -582,9 +611,12 @@ static hipError_t run_tiled_m(const TiledArgs& a, int tile, int seg, hipStream_t
     case 2: return run_tiled<BITS, OB, 8, 2, 4, 4>(a, s);
     case 3: return run_tiled<BITS, OB, 4, 2, 4, 4>(a, s);
     case 4: return run_tiled<BITS, OB, 8, 2, 4, 8>(a, s);
-    case 5: return run_tiled<BITS, OB, 4, 2, 4, 4, 2>(a, s);
-    case 6: return run_tiled<BITS, OB, 2, 2, 4, 4, 2>(a, s);
+    case 5:   // (the four-wave form runs out of registers with 7- and 8-bit stages)
+      if constexpr (BITS <= 6) return run_tiled<BITS, OB, 4, 2, 4, 4, 2>(a, s);
+      else return run_tiled<BITS, OB, 4, 1, 4, 8, 2>(a, s);
+    case 6: return run_tiled<BITS, OB, 2, 1, 4, 8, 2>(a, s);
     case 7: return run_tiled<BITS, OB, 1, 2, 4, 4, 2>(a, s);
+    case 8: return run_tiled<BITS, OB, 4, 1, 4, 8, 2>(a, s);
     default: return run_tiled<BITS, OB, 8, 1, 4, 8>(a, s);
   }
 }
