@@ -52,3 +52,23 @@ def test_two_chunk_ring_every_call(K, N, M, bits, gs, desc, xdt):
         y = run_gemm(h, x, xdt, path=wq.PATH_TILED)
         check(y, xdt, y_ref, label=(K, N, M, bits, gs, desc, xdt, rep))
     h.close()
+
+
+@pytest.mark.parametrize("K", [128, 256, 512, 640, 1152])
+def test_two_chunk_tiles_every_tail(K):
+    """Slices of 1, 2, 4, 5 and 9 chunks (K unsplit): no full step of three, the two tail steps
+    alone, one step of three and one or two tail steps, three steps of three and no tail.  The
+    36864-column layer gives the 64-row tile more than 256 workgroups (its four-wave form), and 16
+    rows take the 16-row tile."""
+    import weight_only_quantized_amd as wq
+    print("tiled-tail", K, flush=True)
+    N = 36864
+    L = gi.make_layer(K, N, 4, 128, scales_dtype="f16", seed=K + 7)
+    h = repack_layer(L)
+    for xdt in ("f16", "bf16"):
+        x = gi.make_x(64, K, xdt, seed=K + 8)
+        y_ref = o.gemm(x, xdt, L.qweight, L.qzeros, L.scales, "f16", L.g_idx, 4)
+        for M in (16, 64):
+            y = run_gemm(h, x[:M], xdt, path=wq.PATH_TILED)
+            check(y, xdt, y_ref[:M], label=(K, xdt, M))
+    h.close()
